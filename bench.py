@@ -1,0 +1,214 @@
+"""Benchmark of the fused tiled attention hot path on one MI355X.
+
+One step = one pass over every stage of the path, each on its own synthetic
+batch (already resident in HBM when timing starts):
+  1. causal forward,            B=4, H=32, N=4096, d=128, bf16
+  2. sliding-window forward,    same tensors, window 1024 (causal band)
+  3. KV-cache decode,           64 sequences x 32 heads, d=128, lengths U[512, 8192]
+  4. causal backward,           B=2, H=16, N=4096, d=128, bf16 (from the forward's O and L)
+
+The headline value is the causal forward's TFLOP/s (4*B*H*N^2*d/2 algorithmic
+flops per launch over its measured time); every stage is timed with HIP events
+recorded on the stream the kernels run on.  The fp64 oracle is timed on the
+host on a bounded sample of the causal forward (a few heads) as the CPU baseline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def window_pairs(N, W):
+    i = np.arange(N, dtype=np.int64)
+    return int(np.minimum(i + 1, W + 1).sum())
+
+
+def cpu_baseline(q, k, v, budget_s=12.0):
+    """The oracle, as it stands, on whole heads of the causal forward."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    B, H, N, d = q.shape
+    s = 1 / math.sqrt(d)
+    flops_head = 4.0 * N * N * d / 2
+    heads, t0 = 0, time.perf_counter()
+    while True:
+        b, h = divmod(heads, H)
+        oracle.attention_ref(q[b, h][None], k[b, h][None], v[b, h][None], s, causal=True)
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s or heads >= B * H:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": round(heads * flops_head / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{heads} of {B * H} (batch, head) slices of the causal N={N}, d={d} forward, "
+                      f"fp64 NumPy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stages", default="fwd,window,decode,bwd")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); every stage of this "
+              "path is independent per (batch, head) and is not run across GPUs here.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import tiled_attention_04_amd as fa
+    from tiled_attention_04_amd.inputs import WORKLOADS, attention_inputs, decode_inputs, dense_cache
+
+    stages = args.stages.split(",")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    fa.lib()
+
+    # ---- inputs -----------------------------------------------------------
+    w3 = WORKLOADS["fwd_b4_h32_n4096_d128_bf16"]
+    B3, H3, N3, d3 = w3["B"], w3["H"], w3["N"], w3["d"]
+    log("generating forward inputs")
+    q3c, k3c, v3c = attention_inputs(B3, H3, N3, d3, "bf16", seed=0)
+    q3, k3, v3 = (t.to(dev) for t in (q3c, k3c, v3c))
+    o3 = torch.empty_like(q3)
+    l3 = torch.empty((B3, H3, N3), dtype=torch.float32, device=dev)
+    o3w = torch.empty_like(q3)
+    l3w = torch.empty_like(l3)
+
+    w4 = WORKLOADS["decode_s64_h32_d128_len512to8192_bf16"]
+    if "decode" in stages:
+        log("generating decode inputs (ragged KV cache)")
+        inp4 = decode_inputs(w4["S"], w4["H"], w4["d"], w4["len_lo"], w4["len_hi"], seed=0)
+        kc4, vc4 = dense_cache(inp4, w4["Lmax"], device=dev)
+        q4 = inp4.q.to(dev)
+        sl4 = torch.from_numpy(inp4.seqlens).to(dev)
+        o4 = torch.empty_like(q4)
+        l4 = torch.empty(q4.shape[:2], dtype=torch.float32, device=dev)
+        ws4 = torch.empty(fa.fa_decode_workspace_size(w4["S"], w4["H"], w4["Lmax"], w4["d"]),
+                          dtype=torch.uint8, device=dev)
+        dec_bytes = inp4.valid_bytes(2) + 2 * q4.numel() * 2
+        del inp4
+
+    w5 = WORKLOADS["bwd_b2_h16_n4096_d128_bf16"]
+    B5, H5, N5, d5 = w5["B"], w5["H"], w5["N"], w5["d"]
+    if "bwd" in stages:
+        log("generating backward inputs")
+        q5, k5, v5, g5 = (t.to(dev) for t in attention_inputs(B5, H5, N5, d5, "bf16", seed=0, with_grad=True))
+        o5, l5 = fa.fa_fwd(q5, k5, v5, causal=True)
+        dq5, dk5, dv5 = (torch.empty(q5.shape, dtype=torch.float32, device=dev) for _ in range(3))
+        ws5 = torch.empty(fa.fa_bwd_workspace_size(B5, H5, N5, d5), dtype=torch.uint8, device=dev)
+
+    # ---- one step -----------------------------------------------------------
+    flops3 = 4.0 * B3 * H3 * N3 * N3 * d3 / 2
+    flops3w = 4.0 * d3 * B3 * H3 * window_pairs(N3, w3["window"])
+    flops5 = 10.0 * B5 * H5 * N5 * N5 * d5 / 2
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        if "fwd" in stages:
+            fa.fa_fwd(q3, k3, v3, causal=True, o=o3, lse=l3)
+        mark(1)
+        if "window" in stages:
+            fa.fa_fwd(q3, k3, v3, causal=True, window=w3["window"], o=o3w, lse=l3w)
+        mark(2)
+        if "decode" in stages:
+            fa.fa_decode(q4, kc4, vc4, sl4, o=o4, lse=l4, workspace=ws4)
+        mark(3)
+        if "bwd" in stages:
+            fa.fa_bwd(q5, k5, v5, o5, g5, l5, causal=True, dq=dq5, dk=dk5, dv=dv5, workspace=ws5)
+        mark(4)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    comp = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(4)]
+                     for i in range(args.steps)])  # ms
+    ms = comp.mean(axis=0)
+    log("stage ms (mean): " + ", ".join(f"{n}={m:.4f}" for n, m in zip(("fwd", "window", "decode", "bwd"), ms)))
+
+    components = {}
+    if "fwd" in stages:
+        tf = flops3 / (ms[0] * 1e-3) / 1e12
+        components["fwd_causal_b4_h32_n4096_d128"] = {
+            "ms": round(ms[0], 5), "TFLOP/s": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "algorithmic_tflop": round(flops3 / 1e12, 5)}
+    if "window" in stages:
+        tf = flops3w / (ms[1] * 1e-3) / 1e12
+        components["fwd_window1024_b4_h32_n4096_d128"] = {
+            "ms": round(ms[1], 5), "TFLOP/s": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "algorithmic_tflop": round(flops3w / 1e12, 5)}
+    if "decode" in stages:
+        gbs = dec_bytes / (ms[2] * 1e-3) / 1e9
+        components["decode_s64_h32_d128_len512to8192"] = {
+            "ms": round(ms[2], 5), "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "algorithmic_gb": round(dec_bytes / 1e9, 4)}
+    if "bwd" in stages:
+        tf = flops5 / (ms[3] * 1e-3) / 1e12
+        components["bwd_causal_b2_h16_n4096_d128"] = {
+            "ms": round(ms[3], 5), "TFLOP/s": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "algorithmic_tflop": round(flops5 / 1e12, 5)}
+
+    value = flops3 / (ms[0] * 1e-3) / 1e12 if "fwd" in stages else None
+    result = {
+        "metric": "causal fwd TFLOP/s & % bf16 MFMA peak (N=4096,d=128); decode % HBM BW",
+        "value": round(value, 3) if value is not None else None,
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1), rounded to bf16)",
+        "config": {"workload": "causal forward B=4 H=32 N=4096 d=128 bf16 (step also runs: window-1024 "
+                               "forward, 64x32 ragged decode d=128 lengths U[512,8192], causal backward "
+                               "B=2 H=16 N=4096 d=128)",
+                   "global_batch": B3, "seq_len": N3, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(value, 3) if value is not None else None,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(value / PEAK_BF16_TFLOPS, 4) if value is not None else None,
+                     "traffic": None, "kernel": "fwd_bf16_kernel<128, 4>"},
+        "components": components,
+    }
+    if not args.no_cpu_baseline and "fwd" in stages:
+        log("timing the fp64 oracle on the host (bounded sample)")
+        result["cpu_baseline"] = cpu_baseline(q3c, k3c, v3c)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,170 @@
+/*
+ * fa355.h -- C ABI of libfa355: fused tiled scaled-dot-product attention for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (defined on the pages cited per entry point):
+ *   S = scale * Q K^T, masked, P = softmax(S) row by row, O = P V,
+ *   L = per-row natural-log logsumexp of the visible entries of S.
+ * The N x N matrices S and P are never stored.
+ *
+ * Mask: key j is visible to query i iff
+ *   (causal == 0 || j <= i) && (window < 0 || j >= i - window).
+ * A window of W therefore admits W + 1 keys including the query's own
+ * position; window = -1 disables it.  A query row with no visible key gets
+ * O = 0 and L = -inf.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers (memory of the current HIP
+ *    device); sizes are element counts.  Tensors are dense and row-major
+ *    ("contiguous") in the layouts stated per call.
+ *  - dtype FA_BF16: q/k/v/o/dO are bfloat16; FA_FP32: they are float32.
+ *    lse, dq, dk, dv and all statistics are float32 in both cases.
+ *  - Ownership: the caller owns every buffer, including workspaces.  The
+ *    library never allocates, frees or synchronises; every call is
+ *    asynchronous on `stream` (a hipStream_t, NULL = the default stream).
+ *    Inputs are read only; outputs are fully overwritten; outputs must not
+ *    alias inputs or each other.
+ *  - Errors: a status is returned, nothing is thrown across the ABI.  Every
+ *    argument check happens before any HIP call, so an error status other
+ *    than FA_ERR_HIP means nothing was launched.  fa_last_error() returns a
+ *    thread-local text describing the most recent failure on this thread.
+ *  - scale is used as given (0 is legal and gives uniform weights); it must
+ *    be finite.
+ */
+#ifndef FA355_H
+#define FA355_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1, /* null required pointer, dim <= 0, window < -1,
+                             non-finite scale, bad block size, ...        */
+  FA_ERR_UNSUPPORTED = 2, /* valid arguments with no kernel (dtype x d)    */
+  FA_ERR_WORKSPACE = 3,   /* workspace pointer null or too small           */
+  FA_ERR_HIP = 4          /* the HIP launch itself failed                  */
+} fa_status;
+
+typedef enum fa_dtype { FA_FP32 = 0, FA_BF16 = 1 } fa_dtype;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int fa_version(void);
+
+/* Short constant text for a status code. */
+const char* fa_status_str(fa_status status);
+
+/* Thread-local description of the last failure ("" after a success). */
+const char* fa_last_error(void);
+
+/*
+ * fa_fwd -- tiled forward pass with online softmax.
+ *
+ * Defined by "Building Flash Attention from Scratch in Pure NumPy",
+ * Architecture Overview and Steps 2-3 (for each query tile walk the K/V
+ * tiles keeping a running max m, a running sum l and an unnormalised O,
+ * rescaled by exp(m_old - m_new); divide once at the end), with the causal
+ * and sliding-window masks of "Build a FlashAttention-2 Inference Kernel
+ * from Scratch in Pure Python", Steps 2-3.  Tiles that the mask hides
+ * entirely are skipped, never loaded.
+ *
+ *   q, k, v : [B, H, N, d] inputs, dtype
+ *   o       : [B, H, N, d] output, dtype
+ *   lse     : [B, H, N] float32 output, L = m + ln(l) (natural log), or NULL
+ *   causal  : 0 or 1;  window : -1 (off) or >= 0
+ *
+ * Supported: FA_BF16 with d in {64, 128} (MFMA kernels); FA_FP32 with
+ * 1 <= d <= 128 (generic kernel).  Other d: FA_ERR_UNSUPPORTED.
+ * Sizes: B*H <= 2^31-1 and B*H*N*d < 2^63; N need not be a tile multiple.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int N, int d, float scale, int causal, int window,
+                 fa_dtype dtype, void* stream);
+
+/*
+ * fa_fwd_ex -- fa_fwd with an explicit tile shape (0, 0 = automatic).
+ *   FA_FP32: 1 <= block_q <= 64, 1 <= block_k <= 64 (any values, e.g. 4 x 4
+ *            for the worked example "FlashAttention Algorithm > Worked
+ *            Example", Setting Up the Example).
+ *   FA_BF16: block_q in {32, 64, 128}, block_k = 64.
+ * Any other pair: FA_ERR_INVALID_ARG.
+ */
+fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int N, int d, float scale, int causal, int window,
+                    fa_dtype dtype, void* stream, int block_q, int block_k);
+
+/*
+ * fa_decode_workspace_size -- bytes of workspace fa_decode needs for these
+ * sizes and this split length (chunk = 0 means the automatic choice).
+ * Returns 0 for invalid sizes.
+ */
+size_t fa_decode_workspace_size(int S, int H, int Lmax, int d, int chunk);
+
+/*
+ * fa_decode -- one new query token per sequence against its KV cache,
+ * split over the cache length ("split-K") and merged by logsumexp.
+ *
+ * Defined by "Build a FlashAttention Kernel with Online Softmax and KV Cache
+ * in Pure Python", Steps 4-5: the new token's query attends to every cached
+ * key including its own (the last valid row), so no causal mask is needed.
+ * Each split produces a partial (m, l, o) by the online-softmax update of
+ * "Building Flash Attention from Scratch in Pure NumPy", Step 2; a second
+ * kernel merges the partials: M = max m_c, l = sum exp(m_c - M) l_c,
+ * o = sum exp(m_c - M) o_c / l.
+ *
+ *   q        : [S, H, d] new queries, dtype
+ *   kcache   : [S, H, Lmax, d] keys, dtype;  vcache: same for values
+ *   seqlens  : [S] int32 device array, 1 <= seqlens[s] <= Lmax: rows
+ *              0..seqlens[s]-1 of sequence s are valid (the last one is the
+ *              new token's); other rows are never read.  Values outside
+ *              [1, Lmax] are clamped into it on the device.
+ *   o        : [S, H, d] output, dtype;  lse: [S, H] float32 output or NULL
+ *   window   : -1 (off) or >= 0: only rows >= seqlens[s]-1-window are used
+ *   chunk    : tokens per split, a positive multiple of 64, or 0 (auto)
+ *   workspace: >= fa_decode_workspace_size(S, H, Lmax, d, chunk) bytes
+ *
+ * Supported: FA_BF16 and FA_FP32 with d in {64, 128}.
+ */
+fa_status fa_decode(const void* q, const void* kcache, const void* vcache,
+                    const int32_t* seqlens, void* o, float* lse,
+                    int S, int H, int Lmax, int d, float scale, int window, int chunk,
+                    void* workspace, size_t workspace_bytes, fa_dtype dtype, void* stream);
+
+/*
+ * fa_bwd_workspace_size -- bytes of workspace fa_bwd needs (0 if invalid).
+ */
+size_t fa_bwd_workspace_size(int B, int H, int N, int d);
+
+/*
+ * fa_bwd -- backward pass that recomputes P from the stored L.
+ *
+ * Defined by "Building Flash Attention from Scratch in Pure NumPy", Step 4:
+ * D = rowsum(dO * O), then per K/V tile, over the query tiles it is visible
+ * to, P = exp(S - L) is recomputed and
+ *   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),
+ *   dQ = scale * dS K,  dK = scale * dS^T Q
+ * (the page's dK/dQ lines are declared simplified; these are the exact
+ * gradients through the softmax).
+ *
+ *   q, k, v, o, dO : [B, H, N, d] dtype (o and lse from fa_fwd)
+ *   lse            : [B, H, N] float32
+ *   dq, dk, dv     : [B, H, N, d] float32 outputs
+ *   workspace      : >= fa_bwd_workspace_size(B, H, N, d) bytes
+ *
+ * Supported: FA_BF16 with d in {64, 128}.  dq is accumulated with float32
+ * atomics, so its last bits may differ from run to run.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                 const float* lse, float* dq, float* dk, float* dv,
+                 int B, int H, int N, int d, float scale, int causal, int window,
+                 void* workspace, size_t workspace_bytes, fa_dtype dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA355_H */

@@ -1,0 +1,117 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol,
+and rejects bad arguments before touching the GPU (no compute calls here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from tiled_attention_04_amd import build as fa_build
+from tiled_attention_04_amd import fa355
+
+HEADER = os.path.join(fa_build.ROOT, "include", "fa355.h")
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails before any HIP call
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa355.LIB_PATH):
+        fa_build.build()
+    return fa355.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_calls():
+    names = declared_functions()
+    for must in ("fa_fwd", "fa_fwd_ex", "fa_decode", "fa_bwd", "fa_decode_workspace_size",
+                 "fa_bwd_workspace_size", "fa_status_str", "fa_last_error", "fa_version"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in fa355.SIGNATURES, f"binding lacks a signature for {name}"
+
+
+def test_header_has_no_torch_or_hip_types():
+    code = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    assert "hipStream_t" not in code and "hip/" not in code
+    assert "at::" not in code and "Tensor" not in code and "torch" not in code
+
+
+def test_status_strings(lib):
+    assert lib.fa_version() >= 100
+    assert fa355.status_str(0) == "FA_OK"
+    assert fa355.status_str(1) == "FA_ERR_INVALID_ARG"
+    assert fa355.status_str(2) == "FA_ERR_UNSUPPORTED"
+    assert fa355.status_str(3) == "FA_ERR_WORKSPACE"
+    assert fa355.status_str(4) == "FA_ERR_HIP"
+
+
+def fwd(lib, q=FAKE, B=1, H=1, N=8, d=64, scale=0.125, causal=0, window=-1, dtype=1, bq=0, bk=0):
+    return lib.fa_fwd_ex(q, FAKE, FAKE, FAKE, None, B, H, N, d, scale, causal, window, dtype, None, bq, bk)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(B=0), 1), (dict(N=-3), 1), (dict(d=0), 1),
+    (dict(causal=2), 1), (dict(window=-2), 1), (dict(scale=float("inf")), 1),
+    (dict(scale=float("nan")), 1), (dict(dtype=7), 1),
+    (dict(d=96), 2), (dict(d=256, dtype=0), 2),
+    (dict(bq=48), 1), (dict(bk=32), 1), (dict(dtype=0, bq=65, bk=4), 1), (dict(dtype=0, bq=0, bk=5), 1),
+    (dict(B=1 << 16, H=1 << 16), 1),
+])
+def test_fwd_rejects_bad_arguments(lib, kw, status):
+    assert fwd(lib, **kw) == status
+    assert fa355.last_error() != ""
+
+
+def test_decode_rejects_bad_arguments(lib):
+    def call(**kw):
+        a = dict(q=FAKE, kc=FAKE, vc=FAKE, sl=FAKE, o=FAKE, S=2, H=2, L=128, d=128, scale=0.1,
+                 window=-1, chunk=0, ws=FAKE, wsb=1 << 30, dtype=1)
+        a.update(kw)
+        return lib.fa_decode(a["q"], a["kc"], a["vc"], a["sl"], a["o"], None, a["S"], a["H"], a["L"],
+                             a["d"], a["scale"], a["window"], a["chunk"], a["ws"], a["wsb"], a["dtype"], None)
+    assert call(sl=None) == 1
+    assert call(S=0) == 1
+    assert call(chunk=100) == 1
+    assert call(chunk=-64) == 1
+    assert call(window=-5) == 1
+    assert call(d=96) == 2
+    assert call(ws=None) == 3
+    assert call(wsb=16) == 3
+    assert "workspace" in fa355.last_error()
+
+
+def test_bwd_rejects_bad_arguments(lib):
+    def call(**kw):
+        a = dict(ptr=FAKE, B=1, H=1, N=64, d=128, dtype=1, ws=FAKE, wsb=1 << 20, window=-1)
+        a.update(kw)
+        p = a["ptr"]
+        return lib.fa_bwd(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["B"], a["H"], a["N"],
+                          a["d"], 0.1, 1, a["window"], a["ws"], a["wsb"], a["dtype"], None)
+    assert call(ptr=None) == 1
+    assert call(N=0) == 1
+    assert call(dtype=0) == 2
+    assert call(d=32) == 2
+    assert call(wsb=8) == 3
+
+
+def test_workspace_sizes(lib):
+    # decode: S*H*ceil(Lmax/chunk) partials of (d + 2) floats
+    assert fa355.fa_decode_workspace_size(64, 32, 8192, 128, 512) == 64 * 32 * 16 * 130 * 4
+    assert fa355.fa_decode_workspace_size(2, 2, 100, 64, 64) == 2 * 2 * 2 * 66 * 4
+    assert fa355.fa_decode_workspace_size(2, 2, 100, 64, 65) == 0
+    assert fa355.fa_decode_workspace_size(0, 2, 100, 64, 64) == 0
+    # auto chunk for the ragged decode batch is 512 tokens
+    assert fa355.fa_decode_workspace_size(64, 32, 8192, 128, 0) == 64 * 32 * 16 * 130 * 4
+    # backward: D and L (log2 units) per row
+    assert fa355.fa_bwd_workspace_size(2, 16, 4096, 128) == 2 * 16 * 4096 * 2 * 4
+    assert fa355.fa_bwd_workspace_size(0, 16, 4096, 128) == 0

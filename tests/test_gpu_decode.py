@@ -1,0 +1,101 @@
+"""GPU parity of fa_decode (split-K + logsumexp merge) against the fp64 oracle."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tiled_attention_04_amd as fa
+from parity import check_bf16, check_fp32, check_lse, need_gpu
+from tiled_attention_04_amd.inputs import WORKLOADS, attention_inputs, decode_inputs, dense_cache
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def run(inp, Lmax, window=-1, chunk=0, scale=None):
+    kc, vc = dense_cache(inp, Lmax, device="cuda")  # rows past the length are NaN
+    sl = torch.from_numpy(inp.seqlens).cuda()
+    o, lse = fa.fa_decode(inp.q.cuda(), kc, vc, sl, window=window, chunk=chunk, scale=scale)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def oracle_decode(inp, window=-1, scale=None):
+    d = inp.q.shape[2]
+    s = 1 / math.sqrt(d) if scale is None else scale
+    S, H = inp.q.shape[:2]
+    o = np.empty((S, H, d))
+    lse = np.empty((S, H))
+    for i in range(S):
+        n = int(inp.seqlens[i])
+        # a cache holding exactly the valid rows; the oracle reads rows < n only
+        oi, li = oracle.decode_ref(inp.q[i:i + 1], inp.k_rows[i][None], inp.v_rows[i][None], [n], s, window)
+        o[i], lse[i] = oi[0], li[0]
+    return o, lse
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("chunk", [0, 64, 128, 320])
+@pytest.mark.parametrize("window", [-1, 0, 70])
+def test_small_ragged_batch(d, dtype, chunk, window):
+    lens = [1, 2, 63, 64, 65, 300, 129]
+    inp = decode_inputs(len(lens), 3, d, 1, 300, dtype=dtype, seed=d + chunk, seqlens=lens)
+    o, lse = run(inp, 300, window, chunk)
+    O, L = oracle_decode(inp, window)
+    if dtype == "fp32":
+        check_fp32(o, O, "o")
+        check_fp32(lse, L, "lse")
+    else:
+        check_bf16(o, O, "o")
+        check_lse(lse, L, "lse")
+
+
+def test_split_count_independence():
+    """The merge is associative: every split length gives the same result."""
+    lens = [700, 1, 1024, 513]
+    inp = decode_inputs(4, 4, 128, 1, 1024, seed=2, seqlens=lens)
+    outs = [run(inp, 1024, -1, c) for c in (64, 128, 192, 512, 1024)]
+    for o, l in outs[1:]:
+        check_bf16(o, outs[0][0], "o vs chunk 64")
+        check_lse(l, outs[0][1], "lse vs chunk 64")
+
+
+def test_decode_equals_last_row_of_causal_forward():
+    """Decode of the newest token = last row of the causal forward (both GPU)."""
+    B, H, N, d = 1, 4, 777, 128
+    q, k, v = attention_inputs(B, H, N, d, "bf16", seed=9)
+    o_f, l_f = fa.fa_fwd(q.cuda(), k.cuda(), v.cuda(), causal=True)
+    sl = torch.tensor([N], dtype=torch.int32, device="cuda")
+    o_d, l_d = fa.fa_decode(q[0, :, N - 1][None].cuda().contiguous(), k.cuda(), v.cuda(), sl)
+    torch.cuda.synchronize()
+    check_bf16(o_d[0].cpu(), o_f[0, :, N - 1].cpu(), "decode vs forward")
+    check_lse(l_d[0].cpu(), l_f[0, :, N - 1].cpu(), "lse decode vs forward")
+
+
+def test_seqlens_out_of_range_are_clamped():
+    lens = np.array([0, 5, 999], dtype=np.int32)  # 0 -> 1 row, 999 -> Lmax rows
+    inp = decode_inputs(3, 2, 64, 1, 100, seed=4, seqlens=[1, 5, 100])
+    kc, vc = dense_cache(inp, 100, device="cuda")
+    o, lse = fa.fa_decode(inp.q.cuda(), kc, vc, torch.from_numpy(lens).cuda())
+    O, L = oracle_decode(inp)
+    check_bf16(o.cpu(), O, "o")
+    check_lse(lse.cpu(), L, "lse")
+
+
+@pytest.mark.slow
+def test_full_size_ragged_decode():
+    """64 sequences x 32 heads, d=128, lengths U[512, 8192]: every (s, h)."""
+    w = WORKLOADS["decode_s64_h32_d128_len512to8192_bf16"]
+    inp = decode_inputs(w["S"], w["H"], w["d"], w["len_lo"], w["len_hi"], seed=0)
+    o, lse = run(inp, w["Lmax"])
+    O, L = oracle_decode(inp)
+    check_bf16(o, O, "o")
+    check_lse(lse, L, "lse")

@@ -1,0 +1,22 @@
+"""libfa355: fused tiled scaled-dot-product attention for MI355X (gfx950).
+
+The computation lives in hand-written HIP kernels behind a C ABI
+(include/fa355.h, built into ``libfa355.so`` next to this file); this package
+is the thin binding.  The library is loaded on first use, never silently
+replaced: if it is missing, calls raise.
+"""
+
+from .fa355 import (  # noqa: F401
+    FA_BF16,
+    FA_FP32,
+    FaError,
+    fa_bwd,
+    fa_bwd_workspace_size,
+    fa_decode,
+    fa_decode_workspace_size,
+    fa_fwd,
+    fa_fwd_ex,
+    last_error,
+    lib,
+    status_str,
+)

@@ -1,0 +1,180 @@
+// C ABI of libfa355 (declared in include/fa355.h): argument validation,
+// kernel selection and launch on the caller's stream.  Every check runs
+// before the first HIP call, so a non-HIP error means nothing was launched.
+#include "fa355.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "fa_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+fa_status fail(fa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+fa_status done(hipError_t err, const char* what) {
+  if (err != hipSuccess) return fail(FA_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+  g_err[0] = '\0';
+  return FA_OK;
+}
+
+size_t elem_bytes(fa_dtype t) { return t == FA_BF16 ? 2 : 4; }
+
+bool valid_dtype(int t) { return t == FA_FP32 || t == FA_BF16; }
+
+constexpr long long kMaxThreadsPerLaunch = 0xFFFFFFFFLL;  // grid * block must fit 32 bits
+constexpr long long kMaxBufferBytes = 0x7FFFFFFFLL;       // 32-bit buffer offsets per slice
+
+// Checks common to the dense (forward / backward) calls.
+fa_status check_dense(int B, int H, int N, int d, float scale, int causal, int window, int dtype) {
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0)
+    return fail(FA_ERR_INVALID_ARG, "sizes must be positive (B=%d H=%d N=%d d=%d)", B, H, N, d);
+  if ((long long)B * H > INT_MAX) return fail(FA_ERR_INVALID_ARG, "B*H exceeds 2^31-1");
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
+  if (window < -1) return fail(FA_ERR_INVALID_ARG, "window must be -1 (off) or >= 0 (got %d)", window);
+  if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite");
+  if (!valid_dtype(dtype)) return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if ((long long)N * d * (long long)elem_bytes((fa_dtype)dtype) > kMaxBufferBytes)
+    return fail(FA_ERR_UNSUPPORTED, "one (batch, head) slice of N*d exceeds 2 GiB");
+  return FA_OK;
+}
+
+int auto_block_q(int B, int H, int N) {
+  // Prefer 4-wave workgroups; fall back to smaller query tiles while the grid
+  // would leave compute units idle (256 CUs on MI355X).
+  const long long bh = (long long)B * H;
+  if (bh * ((N + 127) / 128) >= 512) return 128;
+  if (bh * ((N + 63) / 64) >= 256) return 64;
+  return 32;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_version(void) { return 100; }
+
+const char* fa_status_str(fa_status status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
+    case FA_ERR_HIP: return "FA_ERR_HIP";
+  }
+  return "FA_ERR_UNKNOWN";
+}
+
+const char* fa_last_error(void) { return g_err; }
+
+fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                    int N, int d, float scale, int causal, int window, fa_dtype dtype, void* stream,
+                    int block_q, int block_k) {
+  if (!q || !k || !v || !o) return fail(FA_ERR_INVALID_ARG, "q, k, v and o must be non-null");
+  fa_status st = check_dense(B, H, N, d, scale, causal, window, dtype);
+  if (st != FA_OK) return st;
+  const fa::Mask mask{causal, window};
+  if (dtype == FA_FP32) {
+    if (d > 128) return fail(FA_ERR_UNSUPPORTED, "float32 forward supports d <= 128 (got %d)", d);
+    if (block_q == 0 && block_k == 0) block_q = block_k = 64;
+    if (block_q < 1 || block_q > 64 || block_k < 1 || block_k > 64)
+      return fail(FA_ERR_INVALID_ARG, "float32 tiles must be 1..64 x 1..64 (got %d x %d)", block_q, block_k);
+    const long long wgs = (long long)B * H * ((N + block_q - 1) / block_q);
+    if (wgs * 256 > kMaxThreadsPerLaunch) return fail(FA_ERR_UNSUPPORTED, "grid too large");
+    return done(fa::launch_fwd_fp32((const float*)q, (const float*)k, (const float*)v, (float*)o, lse,
+                                    B, H, N, d, scale, mask, block_q, block_k, (hipStream_t)stream),
+                "fa_fwd (float32)");
+  }
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "bf16 forward supports d in {64, 128} (got %d)", d);
+  if (block_q == 0) block_q = auto_block_q(B, H, N);
+  if (block_k == 0) block_k = 64;
+  if ((block_q != 32 && block_q != 64 && block_q != 128) || block_k != 64)
+    return fail(FA_ERR_INVALID_ARG, "bf16 tiles must be {32,64,128} x 64 (got %d x %d)", block_q, block_k);
+  const long long wgs = (long long)B * H * ((N + block_q - 1) / block_q);
+  if (wgs * 2 * block_q > kMaxThreadsPerLaunch) return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  return done(fa::launch_fwd_bf16(q, k, v, o, lse, B, H, N, d, scale, mask, block_q,
+                                  (hipStream_t)stream),
+              "fa_fwd (bf16)");
+}
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int N, int d, float scale, int causal, int window, fa_dtype dtype, void* stream) {
+  return fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, window, dtype, stream, 0, 0);
+}
+
+size_t fa_decode_workspace_size(int S, int H, int Lmax, int d, int chunk) {
+  if (S <= 0 || H <= 0 || Lmax <= 0 || d <= 0 || chunk < 0 || chunk % 64 != 0) return 0;
+  if (chunk == 0) chunk = fa::decode_auto_chunk(S, H, Lmax);
+  return fa::decode_workspace_bytes(S, H, Lmax, d, chunk);
+}
+
+fa_status fa_decode(const void* q, const void* kcache, const void* vcache, const int32_t* seqlens,
+                    void* o, float* lse, int S, int H, int Lmax, int d, float scale, int window,
+                    int chunk, void* workspace, size_t workspace_bytes, fa_dtype dtype,
+                    void* stream) {
+  if (!q || !kcache || !vcache || !seqlens || !o)
+    return fail(FA_ERR_INVALID_ARG, "q, kcache, vcache, seqlens and o must be non-null");
+  if (S <= 0 || H <= 0 || Lmax <= 0 || d <= 0)
+    return fail(FA_ERR_INVALID_ARG, "sizes must be positive (S=%d H=%d Lmax=%d d=%d)", S, H, Lmax, d);
+  if ((long long)S * H > INT_MAX) return fail(FA_ERR_INVALID_ARG, "S*H exceeds 2^31-1");
+  if (window < -1) return fail(FA_ERR_INVALID_ARG, "window must be -1 (off) or >= 0 (got %d)", window);
+  if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite");
+  if (chunk < 0 || chunk % 64 != 0)
+    return fail(FA_ERR_INVALID_ARG, "chunk must be 0 (auto) or a positive multiple of 64 (got %d)", chunk);
+  if (!valid_dtype(dtype)) return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "decode supports d in {64, 128} (got %d)", d);
+  if ((long long)Lmax * d * (long long)elem_bytes(dtype) > kMaxBufferBytes)
+    return fail(FA_ERR_UNSUPPORTED, "one (sequence, head) cache slice exceeds 2 GiB");
+  if (chunk == 0) chunk = fa::decode_auto_chunk(S, H, Lmax);
+  const long long nchunk = (Lmax + chunk - 1) / chunk;
+  if (nchunk * S * H * 256 > kMaxThreadsPerLaunch) return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  const size_t need = fa::decode_workspace_bytes(S, H, Lmax, d, chunk);
+  if (!workspace || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "decode needs %zu workspace bytes (got %zu%s)", need, workspace_bytes,
+                workspace ? "" : ", null pointer");
+  return done(fa::launch_decode(q, kcache, vcache, seqlens, o, lse, S, H, Lmax, d, scale, window, chunk,
+                                workspace, dtype == FA_BF16, (hipStream_t)stream),
+              "fa_decode");
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 0;
+  return fa::bwd_workspace_bytes(B, H, N, d);
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                 const float* lse, float* dq, float* dk, float* dv, int B, int H, int N, int d,
+                 float scale, int causal, int window, void* workspace, size_t workspace_bytes,
+                 fa_dtype dtype, void* stream) {
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv)
+    return fail(FA_ERR_INVALID_ARG, "every tensor pointer of fa_bwd must be non-null");
+  fa_status st = check_dense(B, H, N, d, scale, causal, window, dtype);
+  if (st != FA_OK) return st;
+  if (dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "backward supports bf16 inputs only");
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "backward supports d in {64, 128} (got %d)", d);
+  if ((long long)N * d * 4 > kMaxBufferBytes)
+    return fail(FA_ERR_UNSUPPORTED, "one (batch, head) slice of the float32 gradients exceeds 2 GiB");
+  const long long rows = (long long)B * H * N;
+  if (rows * 256 / (d / 8) > kMaxThreadsPerLaunch) return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  const size_t need = fa::bwd_workspace_bytes(B, H, N, d);
+  if (!workspace || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "backward needs %zu workspace bytes (got %zu%s)", need, workspace_bytes,
+                workspace ? "" : ", null pointer");
+  return done(fa::launch_bwd_bf16(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale,
+                                  fa::Mask{causal, window}, workspace, (hipStream_t)stream),
+              "fa_bwd");
+}
+
+}  // extern "C"

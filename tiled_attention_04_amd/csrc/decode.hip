@@ -1,0 +1,253 @@
+// Single-token decode over a KV cache, split over the cache length and merged
+// by logsumexp.
+//
+// Method: "Build a FlashAttention Kernel with Online Softmax and KV Cache in
+// Pure Python", Steps 4-5 -- the new token's query attends to every valid
+// cache row, its own included, so no mask is needed.  Each split runs the
+// online-softmax update of "Building Flash Attention from Scratch in Pure
+// NumPy", Step 2, over its rows and leaves a partial (m, l, o); the merge
+// kernel combines the partials with the same rescaling identity.
+//
+// The work is a matrix-vector product per (sequence, head): about one flop
+// per byte of K/V, so it is bound by HBM bandwidth, and it runs on the vector
+// ALUs (a 1-row MFMA would waste 31 of 32 rows).  Design points:
+//  * Every lane loads 16 bytes of a cache row; a group of D*elem/16 lanes
+//    covers one row and a wave reads several rows per instruction, fully
+//    coalesced.  Each lane keeps 8 rows of K and 8 of V in flight, so a
+//    256-thread workgroup has 64 KB of loads outstanding.
+//  * Loads go through a buffer resource sized to the valid rows of the
+//    (sequence, head), so rows at or past seqlens[s] are never read (they
+//    return zero and are masked), and no 64-bit address arithmetic is needed
+//    per lane.
+//  * q is pre-multiplied by scale*log2(e) in float32; scores are reduced
+//    across the row's lanes with DPP; exponentials are exp2.
+//  * Workgroups past the end of a sequence (the grid is sized from Lmax on
+//    the host, since the lengths live on the device) exit at once.
+#include "fa_common.h"
+#include "fa_launch.h"
+
+namespace fa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kUnroll = 8;
+
+template <typename T>
+__device__ __forceinline__ void widen(const uint4& u, float (&x)[16 / sizeof(T)]);
+
+template <>
+__device__ __forceinline__ void widen<bf16>(const uint4& u, float (&x)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = word(u, i);
+    x[2 * i] = bf16_lo(w);
+    x[2 * i + 1] = bf16_hi(w);
+  }
+}
+
+template <>
+__device__ __forceinline__ void widen<float>(const uint4& u, float (&x)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = __builtin_bit_cast(float, word(u, i));
+}
+
+__device__ __forceinline__ void clamp_len(int& n, int Lmax) { n = n < 1 ? 1 : (n > Lmax ? Lmax : n); }
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(
+    const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
+    const int32_t* __restrict__ seqlens, float* __restrict__ ws_o, float* __restrict__ ws_ml,
+    int S, int H, int Lmax, int nchunk, int chunk, float scale_log2, int window) {
+  constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte load
+  constexpr int LPR = D / VEC;          // lanes per cache row
+  constexpr int RPW = 64 / LPR;         // rows per wave instruction
+  constexpr int GROUPS = kWaves * RPW;  // row groups in the workgroup
+  __shared__ float red_o[GROUPS][D];
+  __shared__ float red_m[GROUPS], red_l[GROUPS];
+
+  const int id = blockIdx.x;
+  const int h = id % H;
+  const int s = (id / H) % S;
+  const int c = id / (H * S);
+  int n = seqlens[s];
+  clamp_len(n, Lmax);
+  const int lo = window >= 0 ? max(0, n - 1 - window) : 0;
+  const int c_begin = c * chunk;
+  if (c_begin >= n || c_begin + chunk <= lo) return;  // the merge skips this split too
+
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int g = lane / LPR, e = lane % LPR;
+  const size_t sh = (size_t)s * H + h;
+  const size_t slice = sh * (size_t)Lmax * D;
+  const uint32_t valid_bytes = (uint32_t)n * D * (uint32_t)sizeof(T);
+  const rsrc_t k_src = make_rsrc(kc + slice, valid_bytes);
+  const rsrc_t v_src = make_rsrc(vc + slice, valid_bytes);
+
+  float qv[VEC];
+  widen<T>(*(const uint4*)(q + sh * D + e * VEC), qv);
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) qv[i] *= scale_log2;
+
+  // This wave's rows: a quarter of the split, clipped to [lo, n).
+  const int per_wave = chunk / kWaves;
+  const int r_begin = max(lo, c_begin + w * per_wave);
+  const int r_end = min(n, c_begin + (w + 1) * per_wave);
+
+  float m = kNegInf, l = 0.f;
+  float acc[VEC];
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+
+  for (int r0 = r_begin; r0 < r_end; r0 += kUnroll * RPW) {
+    uint4 kr[kUnroll], vr[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t off = (uint32_t)((r0 + u * RPW + g) * D + e * VEC) * (uint32_t)sizeof(T);
+      kr[u] = load16(k_src, off);
+      vr[u] = load16(v_src, off);
+    }
+    float sc[kUnroll];
+    float mx = kNegInf;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      float kx[VEC];
+      widen<T>(kr[u], kx);
+      float p = 0.f;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) p = __builtin_fmaf(qv[i], kx[i], p);
+      p = group_sum<LPR>(p);
+      const int row = r0 + u * RPW + g;
+      sc[u] = row < r_end ? p : kNegInf;
+      mx = fmaxf(mx, sc[u]);
+    }
+    const float m_new = fmaxf(m, mx);
+    const float ref = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m - ref);
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc[i] *= alpha;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const float p = __builtin_amdgcn_exp2f(sc[u] - ref);
+      l += p;
+      float vx[VEC];
+      widen<T>(vr[u], vx);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[i] = __builtin_fmaf(p, vx[i], acc[i]);
+    }
+  }
+
+  // Combine the row groups of the workgroup, then write this split's partial.
+  const int gi = w * RPW + g;
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) red_o[gi][e * VEC + i] = acc[i];
+  if (e == 0) {
+    red_m[gi] = m;
+    red_l[gi] = l;
+  }
+  __syncthreads();
+  if (t < D) {
+    float M = kNegInf;
+    for (int j = 0; j < GROUPS; ++j) M = fmaxf(M, red_m[j]);
+    const float ref = M == kNegInf ? 0.f : M;
+    float o = 0.f, L = 0.f;
+    for (int j = 0; j < GROUPS; ++j) {
+      const float a = __builtin_amdgcn_exp2f(red_m[j] - ref);
+      o = __builtin_fmaf(a, red_o[j][t], o);
+      L = __builtin_fmaf(a, red_l[j], L);
+    }
+    const size_t part = sh * nchunk + c;
+    ws_o[part * D + t] = o;
+    if (t == 0) {
+      ws_ml[2 * part] = M;
+      ws_ml[2 * part + 1] = L;
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ T from_float(float x);
+template <>
+__device__ __forceinline__ float from_float<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ bf16 from_float<bf16>(float x) { return (bf16)x; }
+
+// One workgroup of D threads per (sequence, head): M = max m_c,
+// l = sum exp(m_c - M) l_c, o = sum exp(m_c - M) o_c / l, L = M ln2 + ln l.
+template <typename T, int D>
+__global__ __launch_bounds__(D) void decode_merge_kernel(
+    const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
+    const int32_t* __restrict__ seqlens, T* __restrict__ o, float* __restrict__ lse, int H,
+    int Lmax, int nchunk, int chunk, int window) {
+  const int sh = blockIdx.x;
+  const int s = sh / H;
+  const int t = threadIdx.x;
+  int n = seqlens[s];
+  clamp_len(n, Lmax);
+  const int lo = window >= 0 ? max(0, n - 1 - window) : 0;
+  const int c0 = lo / chunk, c1 = (n - 1) / chunk;
+  const size_t part0 = (size_t)sh * nchunk;
+  float M = kNegInf;
+  for (int c = c0; c <= c1; ++c) M = fmaxf(M, ws_ml[2 * (part0 + c)]);
+  const float ref = M == kNegInf ? 0.f : M;
+  float acc = 0.f, L = 0.f;
+  for (int c = c0; c <= c1; ++c) {
+    const float a = __builtin_amdgcn_exp2f(ws_ml[2 * (part0 + c)] - ref);
+    L = __builtin_fmaf(a, ws_ml[2 * (part0 + c) + 1], L);
+    acc = __builtin_fmaf(a, ws_o[(part0 + c) * D + t], acc);
+  }
+  o[(size_t)sh * D + t] = from_float<T>(L > 0.f ? acc / L : 0.f);
+  if (t == 0 && lse != nullptr) lse[sh] = L > 0.f ? M * kLn2 + logf(L) : kNegInf;
+}
+
+template <typename T, int D>
+hipError_t launch_t(const void* q, const void* kc, const void* vc, const int32_t* seqlens, void* o,
+                    float* lse, int S, int H, int Lmax, float scale, int window, int chunk,
+                    void* ws, hipStream_t stream) {
+  const int nchunk = (Lmax + chunk - 1) / chunk;
+  float* ws_o = (float*)ws;
+  float* ws_ml = ws_o + (size_t)S * H * nchunk * D;
+  const long long grid = (long long)nchunk * S * H;
+  hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                     (const T*)q, (const T*)kc, (const T*)vc, seqlens, ws_o, ws_ml, S, H, Lmax,
+                     nchunk, chunk, scale * kLog2e, window);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)(S * H)), dim3(D), 0, stream,
+                     ws_o, ws_ml, seqlens, (T*)o, lse, H, Lmax, nchunk, chunk, window);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int decode_auto_chunk(int S, int H, int Lmax) {
+  // Large splits keep the merge cheap; shrink them only when the grid would
+  // otherwise hold fewer than ~4 workgroups per compute unit.
+  long long target = (long long)S * H * Lmax / 1024;
+  int chunk = (int)(target / 64) * 64;
+  if (chunk > 512) chunk = 512;
+  if (chunk < 64) chunk = 64;
+  return chunk;
+}
+
+size_t decode_workspace_bytes(int S, int H, int Lmax, int d, int chunk) {
+  const size_t nchunk = (size_t)((Lmax + chunk - 1) / chunk);
+  return (size_t)S * H * nchunk * (size_t)(d + 2) * sizeof(float);
+}
+
+hipError_t launch_decode(const void* q, const void* kc, const void* vc, const int32_t* seqlens,
+                         void* o, float* lse, int S, int H, int Lmax, int d, float scale,
+                         int window, int chunk, void* ws, bool is_bf16, hipStream_t stream) {
+  if (is_bf16) {
+    if (d == 128)
+      return launch_t<bf16, 128>(q, kc, vc, seqlens, o, lse, S, H, Lmax, scale, window, chunk, ws, stream);
+    return launch_t<bf16, 64>(q, kc, vc, seqlens, o, lse, S, H, Lmax, scale, window, chunk, ws, stream);
+  }
+  if (d == 128)
+    return launch_t<float, 128>(q, kc, vc, seqlens, o, lse, S, H, Lmax, scale, window, chunk, ws, stream);
+  return launch_t<float, 64>(q, kc, vc, seqlens, o, lse, S, H, Lmax, scale, window, chunk, ws, stream);
+}
+
+}  // namespace fa

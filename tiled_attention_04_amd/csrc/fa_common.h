@@ -1,0 +1,87 @@
+// Device-side building blocks shared by the libfa355 kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// ---------------------------------------------------------------- bf16 ----
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// Two floats -> packed bf16 pair (round to nearest even, v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+// 32-bit word i (compile-time after unrolling) of a 16-byte register value.
+__device__ __forceinline__ uint32_t word(const uint4& u, int i) {
+  return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
+}
+
+// ------------------------------------------------------- buffer loads ----
+// A buffer resource covering `bytes` bytes from `base`: 16-byte loads at or
+// past the end read as zero, so ragged tails need no branches.  Offsets are
+// 32-bit byte offsets from `base`.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 load16(rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+// ---------------------------------------------------------------- MFMA ----
+// v_mfma_f32_32x32x16_bf16.  Operand layout (wave64):
+//   A (32 x 16, row-major M x K): lane l holds A[l % 32][8 * (l / 32) + 0..7]
+//   B (16 x 32, K x N):           lane l holds B[8 * (l / 32) + 0..7][l % 32]
+//   C (32 x 32):                  lane l, element r holds
+//                                 C[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32]
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row index (within a 32 x 32 C block) of element r for a lane in half h.
+__device__ __forceinline__ constexpr int c_row(int r, int h) { return 8 * (r / 4) + 4 * h + (r % 4); }
+
+// --------------------------------------------------------- cross-lane ----
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of G lanes (G in {1,2,4,8,16,32,64}); every lane of
+// the group receives the total.
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (G >= 2) x += dpp<0xB1>(x);    // quad_perm [1,0,3,2]
+  if constexpr (G >= 4) x += dpp<0x4E>(x);    // quad_perm [2,3,0,1]
+  if constexpr (G >= 8) x += dpp<0x141>(x);   // row_half_mirror
+  if constexpr (G >= 16) x += dpp<0x140>(x);  // row_mirror
+  if constexpr (G >= 32) x += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
+  if constexpr (G >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
+
+}  // namespace fa

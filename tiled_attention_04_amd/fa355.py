@@ -1,0 +1,185 @@
+"""Thin Python binding of libfa355's C ABI (include/fa355.h).
+
+Argument marshalling only: the functions check that tensors live on the GPU
+with the expected dtype/layout, allocate outputs and workspaces with torch
+(device memory is all torch is used for), and call the library on the
+current torch stream.  Every step of the computation runs in the HIP kernels.
+There is no fallback: if the library cannot be loaded, calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa355.so")
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
+FA_FP32, FA_BF16 = 0, 1
+
+_DTYPE = {torch.float32: FA_FP32, torch.bfloat16: FA_BF16}
+
+_lib = None
+
+# (name, restype, argtypes) for every symbol declared in include/fa355.h.
+_P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "fa_version": (_I, []),
+    "fa_status_str": (ctypes.c_char_p, [_I]),
+    "fa_last_error": (ctypes.c_char_p, []),
+    "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
+    "fa_fwd_ex": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P, _I, _I]),
+    "fa_decode_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
+    "fa_decode": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _I, _P]),
+    "fa_bwd_workspace_size": (_Z, [_I, _I, _I, _I]),
+    "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _I, _P]),
+}
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        super().__init__(f"{status_str(status)}: {message}")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (torch's HIP runtime is loaded first, so both share it)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                               "or python -m tiled_attention_04_amd.build")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().fa_status_str(status).decode()
+
+
+def last_error() -> str:
+    return lib().fa_last_error().decode()
+
+
+def _check(status: int):
+    if status != FA_OK:
+        raise FaError(status, last_error())
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    return t.data_ptr()
+
+
+def _default_scale(scale, d):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def fa_fwd_ex(q, k, v, block_q: int = 0, block_k: int = 0, *, causal: bool = False,
+              window: int = -1, scale=None, o=None, lse=None, stream=None):
+    """Forward pass; q, k, v: [B, H, N, d] GPU tensors (bf16 or fp32).
+    Returns (o [B,H,N,d] in the input dtype, lse [B,H,N] float32)."""
+    B, H, N, d = q.shape
+    dt = q.dtype
+    if dt not in _DTYPE:
+        raise ValueError(f"unsupported dtype {dt}")
+    qp = _dev(q, "q", dt)
+    kp = _dev(k, "k", dt, q.shape)
+    vp = _dev(v, "v", dt, q.shape)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    op = _dev(o, "o", dt, q.shape)
+    lp = _dev(lse, "lse", torch.float32, (B, H, N))
+    _check(lib().fa_fwd_ex(qp, kp, vp, op, lp, B, H, N, d, _default_scale(scale, d), int(causal),
+                           int(window), _DTYPE[dt], _stream(stream), int(block_q), int(block_k)))
+    return o, lse
+
+
+def fa_fwd(q, k, v, *, causal: bool = False, window: int = -1, scale=None, o=None, lse=None,
+           stream=None):
+    """Forward pass with the library's automatic tile choice."""
+    return fa_fwd_ex(q, k, v, 0, 0, causal=causal, window=window, scale=scale, o=o, lse=lse,
+                     stream=stream)
+
+
+def fa_decode_workspace_size(S: int, H: int, Lmax: int, d: int, chunk: int = 0) -> int:
+    return int(lib().fa_decode_workspace_size(S, H, Lmax, d, chunk))
+
+
+def fa_decode(q, kcache, vcache, seqlens, *, scale=None, window: int = -1, chunk: int = 0,
+              o=None, lse=None, workspace=None, stream=None):
+    """Single-token decode; q: [S,H,d], caches: [S,H,Lmax,d], seqlens: int32 [S] on the GPU.
+    Returns (o [S,H,d], lse [S,H] float32)."""
+    S, H, d = q.shape
+    Lmax = kcache.shape[2]
+    dt = q.dtype
+    if dt not in _DTYPE:
+        raise ValueError(f"unsupported dtype {dt}")
+    qp = _dev(q, "q", dt)
+    kp = _dev(kcache, "kcache", dt, (S, H, Lmax, d))
+    vp = _dev(vcache, "vcache", dt, (S, H, Lmax, d))
+    sp = _dev(seqlens, "seqlens", torch.int32, (S,))
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((S, H), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        need = fa_decode_workspace_size(S, H, Lmax, d, chunk)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    op = _dev(o, "o", dt, q.shape)
+    lp = _dev(lse, "lse", torch.float32, (S, H))
+    wp = _dev(workspace, "workspace")
+    _check(lib().fa_decode(qp, kp, vp, sp, op, lp, S, H, Lmax, d, _default_scale(scale, d),
+                           int(window), int(chunk), wp, workspace.numel() * workspace.element_size(),
+                           _DTYPE[dt], _stream(stream)))
+    return o, lse
+
+
+def fa_bwd_workspace_size(B: int, H: int, N: int, d: int) -> int:
+    return int(lib().fa_bwd_workspace_size(B, H, N, d))
+
+
+def fa_bwd(q, k, v, o, dO, lse, *, causal: bool = False, window: int = -1, scale=None,
+           dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Backward pass from the forward's o and lse.  Returns float32 (dq, dk, dv)."""
+    B, H, N, d = q.shape
+    dt = q.dtype
+    if dt not in _DTYPE:
+        raise ValueError(f"unsupported dtype {dt}")
+    ptrs = [_dev(t, n, dt, q.shape) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dO, "dO"))]
+    lp = _dev(lse, "lse", torch.float32, (B, H, N))
+    outs = []
+    for t in (dq, dk, dv):
+        outs.append(torch.empty(q.shape, dtype=torch.float32, device=q.device) if t is None else t)
+    gp = [_dev(t, n, torch.float32, q.shape) for t, n in zip(outs, ("dq", "dk", "dv"))]
+    if workspace is None:
+        workspace = torch.empty(max(fa_bwd_workspace_size(B, H, N, d), 1), dtype=torch.uint8,
+                                device=q.device)
+    wp = _dev(workspace, "workspace")
+    _check(lib().fa_bwd(*ptrs, lp, *gp, B, H, N, d, _default_scale(scale, d), int(causal),
+                        int(window), wp, workspace.numel() * workspace.element_size(), _DTYPE[dt],
+                        _stream(stream)))
+    return tuple(outs)
