@@ -52,8 +52,8 @@ fa_status check_dense(int B, int H, int N, int d, float scale, int causal, int w
 }
 
 int auto_block_q(int B, int H, int N) {
-  // Prefer 4-wave workgroups; fall back to smaller query tiles while the grid
-  // would leave compute units idle (256 CUs on MI355X).
+  // Prefer 4-wave workgroups (two per CU); fall back to smaller query tiles
+  // while the grid would leave compute units idle (256 CUs on MI355X).
   const long long bh = (long long)B * H;
   if (bh * ((N + 127) / 128) >= 512) return 128;
   if (bh * ((N + 63) / 64) >= 256) return 64;

@@ -10,23 +10,32 @@
 //
 // Mapping onto CDNA4:
 //  * A workgroup of NW waves owns BQ = 32*NW query rows; each wave owns 32.
-//    Key/value tiles are BK = 64 rows, double-buffered in LDS and prefetched
-//    from HBM into registers one tile ahead.
+//    Key/value tiles are 64 rows.  They go from HBM straight into LDS
+//    (buffer_load ... lds, 16 bytes per lane): no register staging and no
+//    ALU work to place them.  K and V are double-buffered.
 //  * Scores are computed transposed, S^T = K Q^T: K (from LDS) is the A
 //    operand and the wave's Q rows, loaded once into registers, are the B
 //    operand.  In the 32x32 accumulator layout every lane then holds one
 //    query column (lane % 32) and 16 of its keys, so the row max needs a
 //    single swap between the two 32-lane halves, the row sum is kept per lane
 //    and combined once at the end, and the rescale of O is one scalar per lane.
-//  * P (rounded to bf16) is already in the B-operand layout of O^T = V^T P^T,
-//    so it goes from the softmax straight into the second MFMA.  To make the
-//    A operand (V^T) a single 16-byte LDS read per step, V is written to LDS
-//    transposed, with the keys of every 16-key group permuted (bits 2 and 3
-//    of the key index swapped) to match the accumulator's row order.
-//  * LDS rows are XOR-swizzled in 16-byte chunks so that the MFMA operand
-//    reads are free of bank conflicts.
-//  * The exponentials use exp2 with scale*log2(e) folded into one multiply;
-//    L is converted back to natural log on output.
+//  * P (rounded to bf16) is already in the B-operand layout of O^T = V^T P^T.
+//    The A operand V^T is read from the row-major V tile with the LDS
+//    transpose read ds_read_b64_tr_b16, whose 16-lane groups deliver 4
+//    consecutive keys of one column per lane; the two reads per MFMA step
+//    pick the keys in the accumulator's row order.
+//  * Software pipeline: while the VALU runs the softmax of tile j, the
+//    matrix cores already compute the scores of tile j+1 (K runs one tile
+//    ahead of V), and the loads of K_{j+2} and V_{j+1} are in flight.
+//  * LDS rows are padded (K by 16 bytes, V by 64) so that the MFMA operand
+//    reads hit distinct banks with affine (immediate-offset) addressing; the
+//    direct loads skip the padding by giving those lanes an out-of-range
+//    offset.
+//  * The exponentials use exp2 with scale*log2(e) folded into one FMA; the
+//    running max is taken on raw scores (a negative scale negates Q's bits
+//    instead); the row sum is accumulated in fp32 (a sum of the bf16-rounded
+//    P would cost L up to 2^-9 on rows with few keys).  L is converted back
+//    to natural log.
 //  * Workgroups are ordered so that all query tiles of one (batch, head) land
 //    on the same XCD (the dispatcher deals workgroup ids round-robin over the
 //    8 XCDs), heaviest causal tiles first, so K/V tiles are reused from that
@@ -34,102 +43,160 @@
 #include "fa_common.h"
 #include "fa_launch.h"
 
+#include <type_traits>
+
 namespace fa {
 namespace {
 
 constexpr int kBK = 64;
 
-// Row-major [rows][D] tile: 16-byte chunk c of row r is stored at chunk
-// c ^ (r & 7) (D >= 64 so every row has at least 8 chunks).
 template <int D>
-__device__ __forceinline__ int rm_off(int row, int chunk) {
-  return row * D + ((chunk ^ (row & 7)) << 3);
-}
-
-// Transposed [D][kBK] tile: key u of the tile sits at position vt_pos(u) of
-// row c; 16-byte chunks of a row are swizzled with (c + c/8) & 7.
-__device__ __forceinline__ int vt_pos(int u) { return (u & ~12) | ((u & 4) << 1) | ((u & 8) >> 1); }
-__device__ __forceinline__ int vt_off(int c, int pos) {
-  return c * kBK + ((((pos >> 3) ^ ((c + (c >> 3)) & 7))) << 3) + (pos & 7);
-}
-
-template <int D, int T>
-struct TileIO {
-  static constexpr int kChunksPerRow = D / 8;
-  static constexpr int kKChunks = kBK * kChunksPerRow;         // 16-byte chunks of K
-  static constexpr int kKPer = (kKChunks + T - 1) / T;
-  static constexpr int kVUnits = (kBK / 4) * kChunksPerRow;      // 4 rows x 16 bytes of V
-  static constexpr int kVPer = (kVUnits + T - 1) / T;
-
-  uint4 kr[kKPer];
-  uint4 vr[kVPer][4];
-
-  // Tile rows k0.. of K and V into registers; rows >= N read as zero.
-  __device__ __forceinline__ void load(rsrc_t kr_src, rsrc_t vr_src, int k0, int t) {
-#pragma unroll
-    for (int j = 0; j < kKPer; ++j) {
-      const int i = t + j * T;
-      if (kKChunks % T == 0 || i < kKChunks) {
-        const int row = k0 + i / kChunksPerRow;
-        kr[j] = load16(kr_src, (uint32_t)(row * D + (i % kChunksPerRow) * 8) * 2u);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < kVPer; ++j) {
-      const int i = t + j * T;
-      if (kVUnits % T == 0 || i < kVUnits) {
-        const int co = i % kChunksPerRow;
-        const int row0 = k0 + 4 * (i / kChunksPerRow);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          vr[j][e] = load16(vr_src, (uint32_t)((row0 + e) * D + co * 8) * 2u);
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(bf16* __restrict__ Ks, bf16* __restrict__ Vt, int t) const {
-#pragma unroll
-    for (int j = 0; j < kKPer; ++j) {
-      const int i = t + j * T;
-      if (kKChunks % T == 0 || i < kKChunks)
-        *(uint4*)(Ks + rm_off<D>(i / kChunksPerRow, i % kChunksPerRow)) = kr[j];
-    }
-#pragma unroll
-    for (int j = 0; j < kVPer; ++j) {
-      const int i = t + j * T;
-      if (kVUnits % T == 0 || i < kVUnits) {
-        const int co = i % kChunksPerRow;
-        const int pos = vt_pos(4 * (i / kChunksPerRow));
-#pragma unroll
-        for (int cc = 0; cc < 8; ++cc) {
-          const uint32_t a0 = word(vr[j][0], cc >> 1), a1 = word(vr[j][1], cc >> 1);
-          const uint32_t a2 = word(vr[j][2], cc >> 1), a3 = word(vr[j][3], cc >> 1);
-          uint2 out;
-          if (cc & 1) {
-            out.x = (a0 >> 16) | (a1 & 0xffff0000u);
-            out.y = (a2 >> 16) | (a3 & 0xffff0000u);
-          } else {
-            out.x = (a0 & 0xffffu) | (a1 << 16);
-            out.y = (a2 & 0xffffu) | (a3 << 16);
-          }
-          *(uint2*)(Vt + vt_off(co * 8 + cc, pos)) = out;
-        }
-      }
-    }
-  }
+struct Tile {
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kKPitch = kRowBytes + 16;  // bytes per K row in LDS
+  static constexpr int kVPitch = kRowBytes + 64;  // bytes per V row in LDS
+  static constexpr int kKBytes = kBK * kKPitch;
+  static constexpr int kVBytes = kBK * kVPitch;
+  static constexpr int kKBlocks = kKBytes / 1024;  // 1 KB per wave-wide direct load
+  static constexpr int kVBlocks = kVBytes / 1024;
+  static_assert(kKBytes % 1024 == 0 && kVBytes % 1024 == 0, "tiles must be whole 1 KB blocks");
+  static constexpr int kSmem = 2 * (kKBytes + kVBytes);
 };
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Global byte offset (within the tile) that lane `lane` of direct-load block
+// `blk` must fetch, for a tile stored with `pitch` bytes per row; lanes that
+// land on row padding get an offset past any buffer so they read zero.
+template <int D>
+__device__ __forceinline__ uint32_t block_src(int blk, int lane, int pitch) {
+  const int pos = blk * 1024 + lane * 16;
+  const int row = pos / pitch, col = pos - row * pitch;
+  return col < D * 2 ? (uint32_t)(row * D * 2 + col) : 0x80000000u;
+}
+
+// Issue this wave's share of the direct loads of one tile (rows k0.. of a
+// [N][D] bf16 matrix) into an LDS tile with `PITCH`-byte rows.
+template <int D, int NW, int NBLK, int PITCH, bool PRE, int NPRE>
+__device__ __forceinline__ void load_tile(const bf16* __restrict__ g, int k0, int N, char* lds_tile,
+                                          const uint32_t (&pre)[NPRE], int w, int lane) {
+  const rsrc_t src = make_rsrc(g + (size_t)k0 * D, (uint32_t)max(0, N - k0) * D * 2u);
+#pragma unroll
+  for (int i = 0; i < (NBLK + NW - 1) / NW; ++i) {
+    const int blk = w + i * NW;
+    if (NBLK % NW == 0 || blk < NBLK) {
+      uint32_t off;
+      if constexpr (PRE) off = pre[i];
+      else off = block_src<D>(blk, lane, PITCH);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)(lds_tile + blk * 1024), 16, off, 0, 0, 0);
+    }
+  }
+}
+
+// Reference shift of the exponentials, in log2 units (see softmax_tile).
+constexpr float kTau = 8.f;
+
+// Hide the scores of keys outside [lo, hi] (tile-relative) by setting them
+// to -inf ("Build a FlashAttention-2 Inference Kernel from Scratch in Pure
+// Python", Step 2).  Only tiles that straddle a mask boundary or the end of
+// the sequence need this.
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int lo, int hi, int h) {
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int rel = kb2 * 32 + c_row(r, h);
+      s[kb2][r] = ((rel >= lo) & (rel <= hi)) ? s[kb2][r] : kNegInf;
+    }
+  }
+}
+
+// One tile of the online softmax for this lane's query row ("Building Flash
+// Attention from Scratch in Pure NumPy", Step 2): raw scores s (16 keys per
+// 32-key block, in the accumulator's row order) -> bf16 P in pk, with the
+// running reference m_ref and sum l_run updated and O rescaled by
+// 2^(m_old - m_new).  The reference is only raised when a tile's max exceeds
+// it by more than kTau (P = 2^(x - m) <= 2^kTau stays well inside bf16/fp32
+// range); O / l and L = m + log2(l) do not depend on that choice.
+// c = |scale| * log2(e), at least 1e-30 so that a hidden score (-inf) always
+// gives exp2(-inf * c - ref) = 0 exactly.
+template <int CB>
+__device__ __forceinline__ void softmax_tile(const f32x16 (&s)[2], uint32_t (&pk)[2][8],
+                                             f32x16 (&oacc)[CB], float& m_ref, float& l_run,
+                                             float c) {
+  float mx = kNegInf;
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb2][r]);
+  }
+  mx = fmaxf(mx, swap_halves(mx));
+  const float m_tile = mx == kNegInf ? kNegInf : mx * c;
+  const bool up = m_tile > m_ref + kTau;
+  const float alpha = up ? __builtin_amdgcn_exp2f(m_ref - m_tile) : 1.f;
+  m_ref = up ? m_tile : m_ref;
+  l_run *= alpha;
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) oacc[cb] *= alpha;
+  const float ref = m_ref == kNegInf ? 0.f : m_ref;
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][r], c, -ref));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][r + 1], c, -ref));
+      pk[kb2][r >> 1] = pack_bf16(p0, p1);
+      l_run += p0 + p1;
+    }
+  }
+}
+
+// Scheduling groups (masks of __builtin_amdgcn_sched_group_barrier).
+constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedDSRead = 0x100;
+
+// Interleave NS score MFMAs (one 16-byte K read each) with the softmax VALU
+// work, then NP PV MFMAs (two transpose reads each), keeping the LDS reads a
+// few MFMAs ahead of their use.
+template <int NS, int NP>
+__device__ __forceinline__ void schedule_pipeline() {
+  constexpr int kAheadS = 4, kAheadP = 4, kValuPerMfma = 7;
+  __builtin_amdgcn_sched_group_barrier(kSchedDSRead, kAheadS, 0);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+    if (i + kAheadS < NS) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedVALU, kValuPerMfma, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2 * kAheadP, 0);
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+    if (i + kAheadP < NP) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
+  }
+}
 
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1)))
 void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                      const bf16* __restrict__ v, bf16* __restrict__ o, float* __restrict__ lse,
-                     int BH, int N, int nqt, float scale_log2, int causal, int window) {
+                     int BH, int N, int nqt, float c_log2, int negate_q, int causal, int window) {
+  using TL = Tile<D>;
   constexpr int T = 64 * NW;
   constexpr int BQ = 32 * NW;
   constexpr int KS = D / 16;  // MFMA steps over the head dimension
   constexpr int CB = D / 32;  // 32-column blocks of O
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][kBK * D];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[2][D * kBK];
+  constexpr bool PRE = NW == 4;  // keep the per-lane direct-load offsets in registers
+  constexpr int KPER = PRE ? (TL::kKBlocks + NW - 1) / NW : 1;
+  constexpr int VPER = PRE ? (TL::kVBlocks + NW - 1) / NW : 1;
+  // Separate LDS objects per buffer: the compiler can then tell that the
+  // buffers being read do not alias the ones the direct loads are filling,
+  // and does not wait for those loads before every LDS read.
+  __shared__ __attribute__((aligned(1024))) char Kb0[TL::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char Kb1[TL::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char Vb0[TL::kVBytes];
+  __shared__ __attribute__((aligned(1024))) char Vb1[TL::kVBytes];
 
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6, h = lane >> 5, l32 = lane & 31;
@@ -148,96 +215,124 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int qt = causal ? nqt - 1 - qr : qr;
   const int q0 = qt * BQ;
   const size_t base = (size_t)bh * (size_t)N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2u;
-  const rsrc_t k_src = make_rsrc(k + base, head_bytes);
-  const rsrc_t v_src = make_rsrc(v + base, head_bytes);
-  const rsrc_t q_src = make_rsrc(q + base, head_bytes);
+  const bf16* kg = k + base;
+  const bf16* vg = v + base;
   const int qi = q0 + 32 * w + l32;  // this lane's query row
+
+  // Rows the direct loads may leave unwritten (past N) must hold finite values.
+  for (int i = t; i < TL::kKBytes / 16; i += T) {
+    ((uint4*)Kb0)[i] = uint4{0u, 0u, 0u, 0u};
+    ((uint4*)Kb1)[i] = uint4{0u, 0u, 0u, 0u};
+  }
+  for (int i = t; i < TL::kVBytes / 16; i += T) {
+    ((uint4*)Vb0)[i] = uint4{0u, 0u, 0u, 0u};
+    ((uint4*)Vb1)[i] = uint4{0u, 0u, 0u, 0u};
+  }
+
+  uint32_t kpre[KPER], vpre[VPER];
+  if constexpr (PRE) {
+#pragma unroll
+    for (int i = 0; i < KPER; ++i) kpre[i] = block_src<D>(w + i * NW, lane, TL::kKPitch);
+#pragma unroll
+    for (int i = 0; i < VPER; ++i) vpre[i] = block_src<D>(w + i * NW, lane, TL::kVPitch);
+  }
 
   // Q rows of this wave as MFMA B fragments: Q[qi][16 s + 8 h + 0..7]
   // (rows >= N read as zero).
+  const rsrc_t q_src = make_rsrc(q + base, (uint32_t)N * D * 2u);
   bf16x8 qf[KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s)
-    qf[s] = as_bf16x8(load16(q_src, (uint32_t)(qi * D + 16 * s + 8 * h) * 2u));
+  for (int s = 0; s < KS; ++s) {
+    uint4 u = load16(q_src, (uint32_t)(qi * D + 16 * s + 8 * h) * 2u);
+    if (negate_q) {  // negative scale: S * scale = (-S) * |scale|, exact in bf16
+      u.x ^= 0x80008000u;
+      u.y ^= 0x80008000u;
+      u.z ^= 0x80008000u;
+      u.w ^= 0x80008000u;
+    }
+    qf[s] = as_bf16x8(u);
+  }
 
   // Key tiles holding at least one visible key for this query tile.
   const int q_hi = q0 + BQ - 1;
   const int kmin = window >= 0 ? max(0, q0 - window) : 0;
   const int kmax = causal ? min(N - 1, q_hi) : N - 1;
   const int kt0 = kmin / kBK, kt1 = kmax / kBK + 1;
+  // Keys this lane's query row may see (the tail of the sequence included).
+  const int key_lo = window >= 0 ? qi - window : 0;
+  const int key_hi = causal ? min(qi, N - 1) : N - 1;
+
+  // Per-lane LDS byte offsets of the MFMA operand reads.
+  //  K (A of S^T): row l32 (+32 per key block), bytes 32 s + 16 h.
+  const int k_rd = l32 * TL::kKPitch + 16 * h;
+  //  V^T (A of O^T) via ds_read_b64_tr_b16: in 16-lane group g, lane i points
+  //  at key row 4 (g/2) + i/4 and columns 16 (g%2) + 4 (i%4) of the step's
+  //  16 keys; the second read of a step adds 8 key rows.
+  const int g = lane >> 4, gi = lane & 15;
+  const int v_rd = (4 * (g >> 1) + (gi >> 2)) * TL::kVPitch + (16 * (g & 1) + 4 * (gi & 3)) * 2;
 
   f32x16 oacc[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) oacc[cb] = f32x16{};
-  float m_run = kNegInf, l_run = 0.f;
+  float m_ref = kNegInf, l_run = 0.f;  // log2 units
 
-  TileIO<D, T> io;
-  io.load(k_src, v_src, kt0 * kBK, t);
-  io.store(Ks[0], Vt[0], t);
+  __syncthreads();  // LDS zeroed before any direct load lands
+  load_tile<D, NW, TL::kKBlocks, TL::kKPitch, PRE>(kg, kt0 * kBK, N, Kb0, kpre, w, lane);
+  load_tile<D, NW, TL::kVBlocks, TL::kVPitch, PRE>(vg, kt0 * kBK, N, Vb0, vpre, w, lane);
+  if (kt0 + 1 < kt1)
+    load_tile<D, NW, TL::kKBlocks, TL::kKPitch, PRE>(kg, (kt0 + 1) * kBK, N, Kb1, kpre, w, lane);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const int buf = (kt - kt0) & 1;
-    const bool more = kt + 1 < kt1;
-    if (more) io.load(k_src, v_src, (kt + 1) * kBK, t);
-    const bf16* Kc = Ks[buf];
-    const bf16* Vc = Vt[buf];
-
-    // S^T = K Q^T for the tile's two 32-key blocks.
-    f32x16 sacc[2];
+  // S^T = K Q^T of the first tile for its two 32-key blocks.
+  f32x16 s_a[2];
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      sacc[kb2] = f32x16{};
+  for (int kb2 = 0; kb2 < 2; ++kb2) {
+    s_a[kb2] = f32x16{};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const bf16x8 a = *(const bf16x8*)(Kc + rm_off<D>(kb2 * 32 + l32, 2 * s + h));
-        sacc[kb2] = mfma32(a, qf[s], sacc[kb2]);
-      }
+    for (int s = 0; s < KS; ++s) {
+      const bf16x8 a = *(const bf16x8*)(Kb0 + k_rd + kb2 * 32 * TL::kKPitch + 32 * s);
+      s_a[kb2] = mfma32(a, qf[s], s_a[kb2]);
     }
+  }
+  __syncthreads();  // every wave is done with K buffer 0 before it is refilled
 
-    // Scale into log2 units and mask (only tiles that straddle a boundary).
+  // One pipeline step for tile kt, whose parity selects the buffers at
+  // compile time: K_{kt+1} is in the "next" K buffer, V_kt in the "current"
+  // V buffer; S_kt is in s_cur and S_{kt+1} is written to s_next.
+  auto step = [&](auto parity, f32x16 (&s_cur)[2], f32x16 (&s_next)[2], int kt) {
+    constexpr int P = decltype(parity)::value;
+    char* const k_next = P ? Kb0 : Kb1;
+    char* const k_refill = P ? Kb1 : Kb0;
+    char* const v_cur = P ? Vb1 : Vb0;
+    char* const v_next = P ? Vb0 : Vb1;
+    const bool has_next = kt + 1 < kt1;
+    if (has_next) load_tile<D, NW, TL::kVBlocks, TL::kVPitch, PRE>(vg, (kt + 1) * kBK, N, v_next, vpre, w, lane);
+    if (kt + 2 < kt1) load_tile<D, NW, TL::kKBlocks, TL::kKPitch, PRE>(kg, (kt + 2) * kBK, N, k_refill, kpre, w, lane);
+
     const int k0 = kt * kBK;
     const bool need_mask = (k0 + kBK > N) || (causal && k0 + kBK - 1 > q0) ||
                            (window >= 0 && k0 < q_hi - window);
-    float mx = kNegInf;
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = sacc[kb2][r] * scale_log2;
-        if (need_mask) {
-          const int key = k0 + kb2 * 32 + c_row(r, h);
-          const bool vis = key < N && (!causal || key <= qi) && (window < 0 || key >= qi - window);
-          x = vis ? x : kNegInf;
-        }
-        sacc[kb2][r] = x;
-        mx = fmaxf(mx, x);
-      }
-    }
-    mx = fmaxf(mx, swap_halves(mx));
-    const float m_new = fmaxf(m_run, mx);
-    const float ref = m_new == kNegInf ? 0.f : m_new;  // nothing visible yet: any finite reference
-    const float alpha = __builtin_amdgcn_exp2f(m_run - ref);
-    m_run = m_new;
+    if (need_mask) mask_tile(s_cur, key_lo - k0, key_hi - k0, h);
 
-    uint32_t pk[2][8];
-    float psum = 0.f;
+    // Scores of the next tile on the matrix cores (on the last tile they are
+    // computed from whatever the buffer holds and discarded) ...
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
+      s_next[kb2] = mfma32(*(const bf16x8*)(k_next + k_rd + kb2 * 32 * TL::kKPitch), qf[0], f32x16{});
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(sacc[kb2][r] - ref);
-        const float p1 = __builtin_amdgcn_exp2f(sacc[kb2][r + 1] - ref);
-        psum += p0 + p1;
-        pk[kb2][r >> 1] = pack_bf16(p0, p1);
+      for (int s = 1; s < KS; ++s) {
+        const bf16x8 a = *(const bf16x8*)(k_next + k_rd + kb2 * 32 * TL::kKPitch + 32 * s);
+        s_next[kb2] = mfma32(a, qf[s], s_next[kb2]);
       }
     }
-    l_run = alpha * l_run + psum;
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) oacc[cb] *= alpha;
+
+    // ... while the vector ALUs run the softmax of this one.
+    uint32_t pk[2][8];
+    softmax_tile<CB>(s_cur, pk, oacc, m_ref, l_run, c_log2);
 
     // O^T += V^T P^T, 16 keys per step.
+    const char* vt = v_cur + v_rd;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const uint4 pw = {pk[s >> 1][4 * (s & 1) + 0], pk[s >> 1][4 * (s & 1) + 1],
@@ -245,13 +340,28 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       const bf16x8 pb = as_bf16x8(pw);
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        const bf16x8 a = *(const bf16x8*)(Vc + vt_off(cb * 32 + l32, 16 * s + 8 * h));
+        const char* p = vt + 16 * s * TL::kVPitch + 64 * cb;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * TL::kVPitch));
+        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+        const bf16x8 a = as_bf16x8(uint4{l2.x, l2.y, h2.x, h2.y});
         oacc[cb] = mfma32(a, pb, oacc[cb]);
       }
     }
 
-    if (more) io.store(Ks[buf ^ 1], Vt[buf ^ 1], t);
+    // Instruction order for the region above: K operand reads run a few
+    // MFMAs ahead, and each score MFMA is followed by a slice of the softmax
+    // so that the matrix cores and the vector ALUs work at the same time; the
+    // V^T reads likewise run ahead of the PV MFMAs.
+    schedule_pipeline<2 * KS, 4 * CB>();
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
     __syncthreads();
+  };
+
+  f32x16 s_b[2];
+  for (int kt = kt0; kt < kt1; kt += 2) {  // two tiles per trip: s_a and s_b swap roles
+    step(std::integral_constant<int, 0>{}, s_a, s_b, kt);
+    if (kt + 1 < kt1) step(std::integral_constant<int, 1>{}, s_b, s_a, kt + 1);
   }
 
   // Epilogue: O = O / l, L = m ln2 + ln l.
@@ -262,15 +372,15 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int gq = 0; gq < 4; ++gq) {
         uint2 st;
-        st.x = pack_bf16(oacc[cb][4 * g + 0] * inv, oacc[cb][4 * g + 1] * inv);
-        st.y = pack_bf16(oacc[cb][4 * g + 2] * inv, oacc[cb][4 * g + 3] * inv);
-        *(uint2*)(orow + cb * 32 + 8 * g + 4 * h) = st;
+        st.x = pack_bf16(oacc[cb][4 * gq + 0] * inv, oacc[cb][4 * gq + 1] * inv);
+        st.y = pack_bf16(oacc[cb][4 * gq + 2] * inv, oacc[cb][4 * gq + 3] * inv);
+        *(uint2*)(orow + cb * 32 + 8 * gq + 4 * h) = st;
       }
     }
     if (h == 0 && lse != nullptr)
-      lse[(size_t)bh * N + qi] = l_tot > 0.f ? m_run * kLn2 + logf(l_tot) : kNegInf;
+      lse[(size_t)bh * N + qi] = l_tot > 0.f ? m_ref * kLn2 + logf(l_tot) : kNegInf;
   }
 }
 
@@ -282,7 +392,8 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
   const long long grid = (long long)nqt * B * H;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, stream,
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, B * H, N, nqt,
-                     scale * kLog2e, mask.causal, mask.window);
+                     fmaxf(fabsf(scale) * kLog2e, 1e-30f), scale < 0.f ? 1 : 0, mask.causal,
+                     mask.window);
   return hipGetLastError();
 }
 
