@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def log(msg):
@@ -40,6 +41,30 @@ def log(msg):
 def window_pairs(N, W):
     i = np.arange(N, dtype=np.int64)
     return int(np.minimum(i + 1, W + 1).sum())
+
+
+def source_digest(names):
+    """sha256 over the kernel sources a counter measurement was taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "tiled_attention_04_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed counter runs (FETCH_SIZE +
+    WRITE_SIZE, scaled by a plain copy kernel), or None if the kernel's
+    sources changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("sources_sha256") != source_digest(rec["sources"]):
+        return None
+    return rec["bytes_per_launch"]
 
 
 def cpu_baseline(q, k, v, budget_s=12.0):
@@ -72,6 +97,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stages", default="fwd,window,decode,bwd")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, copy 1 GiB device-to-device three times: the reference "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); every stage of this "
@@ -164,26 +192,36 @@ def main():
     log("stage ms (mean): " + ", ".join(f"{n}={m:.4f}" for n, m in zip(("fwd", "window", "decode", "bwd"), ms)))
 
     components = {}
+
+    def mfma_stage(name, flops, t_ms, kernel):
+        tf = flops / (t_ms * 1e-3) / 1e12
+        components[name] = {
+            "ms": round(t_ms, 5), "TFLOP/s": round(tf, 2), "algorithmic_tflop": round(flops / 1e12, 5),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": measured_traffic(kernel)}}
+
     if "fwd" in stages:
-        tf = flops3 / (ms[0] * 1e-3) / 1e12
-        components["fwd_causal_b4_h32_n4096_d128"] = {
-            "ms": round(ms[0], 5), "TFLOP/s": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-            "algorithmic_tflop": round(flops3 / 1e12, 5)}
+        mfma_stage("fwd_causal_b4_h32_n4096_d128", flops3, ms[0], "fwd_bf16_causal")
     if "window" in stages:
-        tf = flops3w / (ms[1] * 1e-3) / 1e12
-        components["fwd_window1024_b4_h32_n4096_d128"] = {
-            "ms": round(ms[1], 5), "TFLOP/s": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-            "algorithmic_tflop": round(flops3w / 1e12, 5)}
+        mfma_stage("fwd_window1024_b4_h32_n4096_d128", flops3w, ms[1], "fwd_bf16_window")
     if "decode" in stages:
         gbs = dec_bytes / (ms[2] * 1e-3) / 1e9
         components["decode_s64_h32_d128_len512to8192"] = {
-            "ms": round(ms[2], 5), "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
-            "algorithmic_gb": round(dec_bytes / 1e9, 4)}
+            "ms": round(ms[2], 5), "GB/s": round(gbs, 1), "algorithmic_gb": round(dec_bytes / 1e9, 4),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode")}}
     if "bwd" in stages:
-        tf = flops5 / (ms[3] * 1e-3) / 1e12
-        components["bwd_causal_b2_h16_n4096_d128"] = {
-            "ms": round(ms[3], 5), "TFLOP/s": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-            "algorithmic_tflop": round(flops5 / 1e12, 5)}
+        mfma_stage("bwd_causal_b2_h16_n4096_d128", flops5, ms[3], "bwd_bf16")
+
+    if args.copy_calibration:
+        log("copy calibration: 3 x 1 GiB device-to-device")
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     value = flops3 / (ms[0] * 1e-3) / 1e12 if "fwd" in stages else None
     result = {
@@ -201,7 +239,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(value, 3) if value is not None else None,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(value / PEAK_BF16_TFLOPS, 4) if value is not None else None,
-                     "traffic": None, "kernel": "fwd_bf16_kernel<128, 4>"},
+                     "traffic": measured_traffic("fwd_bf16_causal"),
+                     "kernel": "fwd_bf16_kernel<128, 4> (causal)"},
         "components": components,
     }
     if not args.no_cpu_baseline and "fwd" in stages:
