@@ -90,7 +90,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
  *   FA_FP32: 1 <= block_q <= 64, 1 <= block_k <= 64 (any values, e.g. 4 x 4
  *            for the worked example "FlashAttention Algorithm > Worked
  *            Example", Setting Up the Example).
- *   FA_BF16: block_q in {32, 64, 128}, block_k = 64.
+ *   FA_BF16: block_q in {32, 64, 128, 256}, block_k = 64.
  * Any other pair: FA_ERR_INVALID_ARG.
  */
 fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,

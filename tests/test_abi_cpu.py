@@ -64,7 +64,7 @@ def fwd(lib, q=FAKE, B=1, H=1, N=8, d=64, scale=0.125, causal=0, window=-1, dtyp
     (dict(causal=2), 1), (dict(window=-2), 1), (dict(scale=float("inf")), 1),
     (dict(scale=float("nan")), 1), (dict(dtype=7), 1),
     (dict(d=96), 2), (dict(d=256, dtype=0), 2),
-    (dict(bq=48), 1), (dict(bq=256), 1), (dict(bk=32), 1), (dict(dtype=0, bq=65, bk=4), 1), (dict(dtype=0, bq=0, bk=5), 1),
+    (dict(bq=48), 1), (dict(bq=512), 1), (dict(bk=32), 1), (dict(dtype=0, bq=65, bk=4), 1), (dict(dtype=0, bq=0, bk=5), 1),
     (dict(B=1 << 16, H=1 << 16), 1),
 ])
 def test_fwd_rejects_bad_arguments(lib, kw, status):

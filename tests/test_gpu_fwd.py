@@ -83,7 +83,7 @@ MASKS = [(False, -1), (True, -1), (True, 37), (False, 20), (True, 0)]
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", [1, 37, 64, 65, 200, 333])
 @pytest.mark.parametrize("causal,window", MASKS)
-@pytest.mark.parametrize("bq", [32, 64, 128])
+@pytest.mark.parametrize("bq", [32, 64, 128, 256])
 def test_bf16_ragged_masks_tiles(d, N, causal, window, bq):
     q, k, v = attention_inputs(2, 2, N, d, "bf16", seed=7 * N + d)
     o, lse = run(q, k, v, causal, window, bq=bq)

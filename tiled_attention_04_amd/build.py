@@ -65,6 +65,12 @@ def build(jobs: int | None = None) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+    # Every kernel launched from host code must have its host stub defined;
+    # an undefined one only shows when the library is loaded.
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [ln.split()[-1] for ln in nm.stdout.splitlines() if "__device_stub__" in ln]
+    if missing:
+        raise RuntimeError("link left kernel stubs undefined: " + ", ".join(missing))
     os.replace(tmp, LIB)
     return LIB
 

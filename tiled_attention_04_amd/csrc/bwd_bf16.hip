@@ -115,14 +115,7 @@ void bwd_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   int bh, kt;
   const int id = blockIdx.x;
-  if ((BH & 7) == 0) {  // all key tiles of one head on one XCD, heaviest (kt = 0) first
-    const int xcd = id & 7, slot = id >> 3;
-    bh = (slot / nkt) * 8 + xcd;
-    kt = slot % nkt;
-  } else {
-    bh = id / nkt;
-    kt = id % nkt;
-  }
+  tile_order(id, BH, nkt, bh, kt);  // heaviest key tile (kt = 0) first
   const int k0 = kt * kBKV;
   const size_t base = (size_t)bh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;

@@ -84,4 +84,23 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
 
+// Workgroup id -> (head slice bh, tile rank r) for a grid of BH * ntiles
+// workgroups.  Ranks are dispatched in order (every head's rank 0 first,
+// then every head's rank 1, ...), so when rank 0 is the most expensive tile
+// the last workgroups to start are the cheapest ones and the tail of the
+// launch stays short.  Consecutive ids go round-robin over the 8 XCDs of the
+// chip, so when BH is a multiple of 8 every head stays on one XCD (its K/V
+// are shared in that XCD's L2).
+__device__ __forceinline__ void tile_order(int id, int BH, int ntiles, int& bh, int& r) {
+  (void)ntiles;
+  if ((BH & 7) == 0) {
+    const int xcd = id & 7, slot = id >> 3, nbh8 = BH >> 3;
+    r = slot / nbh8;
+    bh = (slot - r * nbh8) * 8 + xcd;
+  } else {
+    r = id / BH;
+    bh = id - r * BH;
+  }
+}
+
 }  // namespace fa

@@ -67,6 +67,13 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+// One 16-byte direct load per lane from a buffer resource into LDS: lane l's
+// bytes land at dst + 16 l (dst is wave-uniform).  Kept out of lambdas: the
+// host pass rejects this builtin there and then silently drops the kernel.
+__device__ __forceinline__ void load_lds16(rsrc_t src, char* dst, uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)dst, 16, voffset, 0, 0, 0);
+}
+
 // Global byte offset (within the tile) that lane `lane` of direct-load block
 // `blk` must fetch, for a tile stored with `pitch` bytes per row; lanes that
 // land on row padding get an offset past any buffer so they read zero.
@@ -90,7 +97,7 @@ __device__ __forceinline__ void load_tile(const bf16* __restrict__ g, int k0, in
       uint32_t off;
       if constexpr (PRE) off = pre[i];
       else off = block_src<D>(blk, lane, PITCH);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)(lds_tile + blk * 1024), 16, off, 0, 0, 0);
+      load_lds16(src, lds_tile + blk * 1024, off);
     }
   }
 }
@@ -204,14 +211,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   // Workgroup -> (batch*head, query tile).
   int bh, qr;
   const int id = blockIdx.x;
-  if ((BH & 7) == 0) {
-    const int xcd = id & 7, slot = id >> 3;
-    bh = (slot / nqt) * 8 + xcd;
-    qr = slot % nqt;
-  } else {
-    bh = id / nqt;
-    qr = id % nqt;
-  }
+  tile_order(id, BH, nqt, bh, qr);
   const int qt = causal ? nqt - 1 - qr : qr;
   const int q0 = qt * BQ;
   const size_t base = (size_t)bh * (size_t)N * D;
@@ -384,6 +384,318 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   }
 }
 
+// s_waitcnt on the vector-memory counter only: wait until at most n of this
+// wave's vector loads (here: direct loads into LDS) are still in flight.
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {  // the count is an immediate operand
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+  }
+}
+
+// Workgroup barrier that does not drain outstanding vector loads (unlike
+// __syncthreads, whose release fence waits for every memory operation).  The
+// "memory" clobber keeps LDS accesses on their side of it and the scheduling
+// barriers keep all other instructions there too (the ping-pong phases rely
+// on it).
+__device__ __forceinline__ void barrier_keep_loads() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// ---------------------------------------------------------------------------
+// Ping-pong forward for long sequences: 8 waves, 256 query rows per workgroup.
+//
+// The waves form two groups of four that run the same tile loop half a step
+// apart, separated by workgroup barriers: while one group issues its matrix
+// work for tile j (P_j V_j and the scores of tile j+1), the other runs the
+// softmax of its own tile j on the vector ALUs, then they swap.  Each SIMD
+// hosts one wave of each group, so its matrix core and vector ALU are busy at
+// the same time.  A wave keeps a single score buffer: the scores of tile j+1
+// are written after the softmax of tile j has consumed them.  K/V tiles sit in
+// three LDS stages (one workgroup per CU); tile j+2 is loaded while tiles j and
+// j+1 are in use, and every wave loads its share of each tile.
+//
+// Barrier bookkeeping: group 0 runs  [softmax j] B [matrix j] B ...  and group
+// 1 runs one barrier behind, so between consecutive barriers one group is in
+// its matrix phase and the other in its softmax phase.  Every wave executes
+// the same number of barriers, whichever group it is in.
+
+// Scheduling of the matrix phase: NPV PV MFMAs with two transpose reads each,
+// then NS score MFMAs with one K read each; operand reads run AHEAD MFMAs
+// ahead.
+template <int NPV, int NS>
+__device__ __forceinline__ void schedule_matrix_phase() {
+  constexpr int AHEAD = 4;
+  __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2 * AHEAD, 1);
+#pragma unroll
+  for (int i = 0; i < NPV; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 1);
+    if (i + AHEAD < NPV) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 1);
+    else __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 1);
+  }
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 1);
+    if (i + AHEAD < NS) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 1);
+  }
+}
+
+// Force values to be computed at this point of the program: an empty asm
+// that reads and "writes" them keeps compiler passes from sinking their
+// arithmetic past the barrier that follows (they would otherwise move next
+// to their only users, the MFMAs of the other phase).
+// (The asm only exists in the device pass: the host pass also parses device
+// functions, and AMDGPU register constraints mean nothing there.)
+template <int CB>
+__device__ __forceinline__ void pin_softmax_results(uint32_t (&pk)[2][8], f32x16 (&oacc)[CB],
+                                                    float& l_run, float& m_ref) {
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(pk[i][j]));
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) asm volatile("" : "+v"(oacc[cb]));
+  asm volatile("" : "+v"(l_run), "+v"(m_ref));
+#endif
+}
+
+// Ping-pong group of the calling wave: the order in which waves arrive on
+// their SIMD (HW_ID bits 5:4), modulo 2, so that each SIMD hosts one wave of
+// each group when the workgroup's waves are spread evenly.  `slots` is a
+// zeroed per-SIMD counter in LDS.
+__device__ __forceinline__ int wave_group(int* slots, int lane) {
+  const int simd = __builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4) & 3;
+  int slot = 0;
+  if (lane == 0) slot = atomicAdd(&slots[simd], 1);
+  return __builtin_amdgcn_readfirstlane(slot) & 1;
+}
+
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void fwd_pingpong_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                         const bf16* __restrict__ v, bf16* __restrict__ o, float* __restrict__ lse,
+                         int BH, int N, int nqt, float c_log2, int negate_q, int causal, int window) {
+  using TL = Tile<D>;
+  constexpr int NW = 8;
+  constexpr int T = 64 * NW;
+  constexpr int BQ = 32 * NW;
+  constexpr int KS = D / 16;
+  constexpr int CB = D / 32;
+  constexpr int KPER = (TL::kKBlocks + NW - 1) / NW;
+  constexpr int VPER = (TL::kVBlocks + NW - 1) / NW;
+  // One LDS object per stage and matrix (see the alias note in fwd_bf16_kernel).
+  __shared__ __attribute__((aligned(1024))) char K0[TL::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char K1[TL::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char K2[TL::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char V0[TL::kVBytes];
+  __shared__ __attribute__((aligned(1024))) char V1[TL::kVBytes];
+  __shared__ __attribute__((aligned(1024))) char V2[TL::kVBytes];
+  __shared__ int simd_slots[4];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6, h = lane >> 5, l32 = lane & 31;
+
+  int bh, qr;
+  const int id = blockIdx.x;
+  tile_order(id, BH, nqt, bh, qr);
+  const int qt = causal ? nqt - 1 - qr : qr;
+  const int q0 = qt * BQ;
+  const size_t base = (size_t)bh * (size_t)N * D;
+  const bf16* kg = k + base;
+  const bf16* vg = v + base;
+  const int qi = q0 + 32 * w + l32;
+
+  for (int i = t; i < TL::kKBytes / 16; i += T) {
+    ((uint4*)K0)[i] = uint4{0u, 0u, 0u, 0u};
+    ((uint4*)K1)[i] = uint4{0u, 0u, 0u, 0u};
+    ((uint4*)K2)[i] = uint4{0u, 0u, 0u, 0u};
+  }
+  for (int i = t; i < TL::kVBytes / 16; i += T) {
+    ((uint4*)V0)[i] = uint4{0u, 0u, 0u, 0u};
+    ((uint4*)V1)[i] = uint4{0u, 0u, 0u, 0u};
+    ((uint4*)V2)[i] = uint4{0u, 0u, 0u, 0u};
+  }
+  if (t < 4) simd_slots[t] = 0;
+  __syncthreads();
+  // Group = order of arrival of this wave on its SIMD (HW_ID bits 5:4), so
+  // that each SIMD hosts one wave of each group when waves are spread evenly.
+  const int grp = wave_group(simd_slots, lane);
+
+  uint32_t kpre[KPER], vpre[VPER];
+#pragma unroll
+  for (int i = 0; i < KPER; ++i) kpre[i] = block_src<D>(w + i * NW, lane, TL::kKPitch);
+#pragma unroll
+  for (int i = 0; i < VPER; ++i) vpre[i] = block_src<D>(w + i * NW, lane, TL::kVPitch);
+  const int v_nblk = (TL::kVBlocks - w + NW - 1) / NW;  // V blocks this wave loads per tile
+
+  const rsrc_t q_src = make_rsrc(q + base, (uint32_t)N * D * 2u);
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    uint4 u = load16(q_src, (uint32_t)(qi * D + 16 * s + 8 * h) * 2u);
+    if (negate_q) {
+      u.x ^= 0x80008000u;
+      u.y ^= 0x80008000u;
+      u.z ^= 0x80008000u;
+      u.w ^= 0x80008000u;
+    }
+    qf[s] = as_bf16x8(u);
+  }
+
+  const int q_hi = q0 + BQ - 1;
+  const int kmin = window >= 0 ? max(0, q0 - window) : 0;
+  const int kmax = causal ? min(N - 1, q_hi) : N - 1;
+  const int kt0 = kmin / kBK, kt1 = kmax / kBK + 1;
+  const int key_lo = window >= 0 ? qi - window : 0;
+  const int key_hi = causal ? min(qi, N - 1) : N - 1;
+  const int wq0 = q0 + 32 * w, wq1 = wq0 + 31;
+
+  const int k_rd = l32 * TL::kKPitch + 16 * h;
+  const int g = lane >> 4, gi = lane & 15;
+  const int v_rd = (4 * (g >> 1) + (gi >> 2)) * TL::kVPitch + (16 * (g & 1) + 4 * (gi & 3)) * 2;
+
+  auto kstage = [&] __device__ (auto st) -> char* {
+    constexpr int S = decltype(st)::value;
+    return S == 0 ? K0 : S == 1 ? K1 : K2;
+  };
+  auto vstage = [&] __device__ (auto st) -> char* {
+    constexpr int S = decltype(st)::value;
+    return S == 0 ? V0 : S == 1 ? V1 : V2;
+  };
+  // This wave's share of the direct loads of tile `tile` into stage st (K
+  // blocks first, then V, so that a wait for K can leave V in flight).
+  auto load_share = [&] __device__ (int tile, auto st) {
+    const int k0 = tile * kBK;
+    const rsrc_t ks = make_rsrc(kg + (size_t)k0 * D, (uint32_t)max(0, N - k0) * D * 2u);
+    const rsrc_t vs = make_rsrc(vg + (size_t)k0 * D, (uint32_t)max(0, N - k0) * D * 2u);
+    char* kd = kstage(st);
+    char* vd = vstage(st);
+#pragma unroll
+    for (int i = 0; i < KPER; ++i) {
+      const int blk = w + i * NW;
+      if (blk < TL::kKBlocks)
+        load_lds16(ks, kd + blk * 1024, kpre[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < VPER; ++i) {
+      const int blk = w + i * NW;
+      if (blk < TL::kVBlocks)
+        load_lds16(vs, vd + blk * 1024, vpre[i]);
+    }
+  };
+
+  f32x16 oacc[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) oacc[cb] = f32x16{};
+  float m_ref = kNegInf, l_run = 0.f;
+  f32x16 sc[2];  // scores of the tile in flight
+
+  using std::integral_constant;
+  // Prologue: tiles 0 and 1 resident, scores of tile 0.
+  load_share(kt0, integral_constant<int, 0>{});
+  if (kt0 + 1 < kt1) load_share(kt0 + 1, integral_constant<int, 1>{});
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2) {
+    sc[kb2] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      sc[kb2] = mfma32(*(const bf16x8*)(K0 + k_rd + kb2 * 32 * TL::kKPitch + 32 * s), qf[s], sc[kb2]);
+  }
+  if (grp == 1) barrier_keep_loads();  // group 1 runs one phase behind
+
+  // One tile: softmax phase, barrier, matrix phase, barrier.  Stage of tile
+  // kt is ST (compile time); tile kt+1 is in stage (ST+1)%3 and tile kt+2 is
+  // loaded into stage (ST+2)%3.
+  auto tile_step = [&] __device__ (auto stage, int kt) {
+    constexpr int ST = decltype(stage)::value;
+    constexpr int STN = (ST + 1) % 3, STF = (ST + 2) % 3;
+    const bool has_next = kt + 1 < kt1;
+    const bool load_far = kt + 2 < kt1;
+    // ---- softmax phase (group 1 also issues its loads of tile kt+2 here)
+    if (grp == 1 && load_far) load_share(kt + 2, integral_constant<int, STF>{});
+    const int k0 = kt * kBK;
+    const bool need_mask = (k0 + kBK > N) || (causal && k0 + kBK - 1 > wq0) ||
+                           (window >= 0 && k0 < wq1 - window);
+    if (need_mask) mask_tile(sc, key_lo - k0, key_hi - k0, h);
+    uint32_t pk[2][8];
+    softmax_tile<CB>(sc, pk, oacc, m_ref, l_run, c_log2);
+    pin_softmax_results<CB>(pk, oacc, l_run, m_ref);
+    // Group 0: tile kt+1's K must be resident for its matrix phase; its V may
+    // stay in flight (group 0 loaded tile kt+1 in its previous matrix phase).
+    if (grp == 0) wait_vm(has_next ? v_nblk : 0);
+    barrier_keep_loads();
+    // ---- matrix phase (group 0 issues its loads of tile kt+2 here)
+    if (grp == 0 && load_far) load_share(kt + 2, integral_constant<int, STF>{});
+    {
+      const char* vt = vstage(integral_constant<int, ST>{}) + v_rd;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint4 pw = {pk[s >> 1][4 * (s & 1) + 0], pk[s >> 1][4 * (s & 1) + 1],
+                          pk[s >> 1][4 * (s & 1) + 2], pk[s >> 1][4 * (s & 1) + 3]};
+        const bf16x8 pb = as_bf16x8(pw);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          const char* p = vt + 16 * s * TL::kVPitch + 64 * cb;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * TL::kVPitch));
+          const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+          oacc[cb] = mfma32(as_bf16x8(uint4{l2.x, l2.y, h2.x, h2.y}), pb, oacc[cb]);
+        }
+      }
+      // Scores of tile kt+1 (computed from whatever the stage holds and
+      // discarded if there is no such tile).
+      const char* kn = kstage(integral_constant<int, STN>{}) + k_rd;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        sc[kb2] = mfma32(*(const bf16x8*)(kn + kb2 * 32 * TL::kKPitch), qf[0], f32x16{});
+#pragma unroll
+        for (int s = 1; s < KS; ++s)
+          sc[kb2] = mfma32(*(const bf16x8*)(kn + kb2 * 32 * TL::kKPitch + 32 * s), qf[s], sc[kb2]);
+      }
+      schedule_matrix_phase<4 * CB, 2 * KS>();
+    }
+    // Group 1: its loads of tile kt+2 (issued this step) must have landed
+    // before group 0 needs K_{kt+2}; V may stay in flight.
+    if (grp == 1) wait_vm(load_far ? v_nblk : 0);
+    barrier_keep_loads();
+  };
+
+  for (int kt = kt0; kt < kt1; kt += 3) {
+    tile_step(integral_constant<int, 0>{}, kt);
+    if (kt + 1 >= kt1) break;
+    tile_step(integral_constant<int, 1>{}, kt + 1);
+    if (kt + 2 >= kt1) break;
+    tile_step(integral_constant<int, 2>{}, kt + 2);
+  }
+  if (grp == 0) barrier_keep_loads();  // match group 1's extra barrier
+
+  const float l_tot = l_run + swap_halves(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qi < N) {
+    bf16* orow = o + base + (size_t)qi * D;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        uint2 st;
+        st.x = pack_bf16(oacc[cb][4 * gq + 0] * inv, oacc[cb][4 * gq + 1] * inv);
+        st.y = pack_bf16(oacc[cb][4 * gq + 2] * inv, oacc[cb][4 * gq + 3] * inv);
+        *(uint2*)(orow + cb * 32 + 8 * gq + 4 * h) = st;
+      }
+    }
+    if (h == 0 && lse != nullptr)
+      lse[(size_t)bh * N + qi] = l_tot > 0.f ? m_ref * kLn2 + logf(l_tot) : kNegInf;
+  }
+}
+
 template <int D, int NW>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                   int N, float scale, Mask mask, hipStream_t stream) {
@@ -397,16 +709,30 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_pingpong(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                           int H, int N, float scale, Mask mask, hipStream_t stream) {
+  const int nqt = (N + 255) / 256;
+  const long long grid = (long long)nqt * B * H;
+  hipLaunchKernelGGL((fwd_pingpong_kernel<D>), dim3((unsigned)grid), dim3(512), 0, stream,
+                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, B * H, N, nqt,
+                     fmaxf(fabsf(scale) * kLog2e, 1e-30f), scale < 0.f ? 1 : 0, mask.causal,
+                     mask.window);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int H, int N, int d, float scale, Mask mask, int block_q,
                            hipStream_t stream) {
   if (d == 128) {
+    if (block_q == 256) return launch_pingpong<128>(q, k, v, o, lse, B, H, N, scale, mask, stream);
     if (block_q == 128) return launch<128, 4>(q, k, v, o, lse, B, H, N, scale, mask, stream);
     if (block_q == 64) return launch<128, 2>(q, k, v, o, lse, B, H, N, scale, mask, stream);
     return launch<128, 1>(q, k, v, o, lse, B, H, N, scale, mask, stream);
   }
+  if (block_q == 256) return launch_pingpong<64>(q, k, v, o, lse, B, H, N, scale, mask, stream);
   if (block_q == 128) return launch<64, 4>(q, k, v, o, lse, B, H, N, scale, mask, stream);
   if (block_q == 64) return launch<64, 2>(q, k, v, o, lse, B, H, N, scale, mask, stream);
   return launch<64, 1>(q, k, v, o, lse, B, H, N, scale, mask, stream);
