@@ -84,6 +84,31 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
 
+// The two halves of the wave exchanged by one VALU lane swap
+// (v_permlane32_swap): returns {value of lanes 0-31, value of lanes 32-63}
+// as seen by lane l and lane l ^ 32 alike.  (The vector result is copied to
+// scalars before any bit cast: casting its subscripted elements directly is
+// miscompiled.)
+__device__ __forceinline__ void wave_halves(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                  __builtin_bit_cast(unsigned, x), false, false);
+  const unsigned a = r[0], b = r[1];
+  lo = __builtin_bit_cast(float, a);
+  hi = __builtin_bit_cast(float, b);
+}
+
+// max / sum of x over lanes l and l ^ 32; both lanes get the same bits.
+__device__ __forceinline__ float pair_max(float x) {
+  float a, b;
+  wave_halves(x, a, b);
+  return a > b ? a : b;
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  float a, b;
+  wave_halves(x, a, b);
+  return a + b;
+}
+
 // Workgroup id -> (head slice bh, tile rank r) for a grid of BH * ntiles
 // workgroups.  Ranks are dispatched in order (every head's rank 0 first,
 // then every head's rank 1, ...), so when rank 0 is the most expensive tile

@@ -139,14 +139,18 @@ __device__ __forceinline__ void softmax_tile(const f32x16 (&s)[2], uint32_t (&pk
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb2][r]);
   }
-  mx = fmaxf(mx, swap_halves(mx));
+  mx = pair_max(mx);
   const float m_tile = mx == kNegInf ? kNegInf : mx * c;
   const bool up = m_tile > m_ref + kTau;
-  const float alpha = up ? __builtin_amdgcn_exp2f(m_ref - m_tile) : 1.f;
-  m_ref = up ? m_tile : m_ref;
-  l_run *= alpha;
+  // Rescaling is rare once the running max has settled: skip it (a branch
+  // that is uniform over the wave) unless some row raises its reference.
+  if (__builtin_amdgcn_ballot_w64(up) != 0) {
+    const float alpha = up ? __builtin_amdgcn_exp2f(m_ref - m_tile) : 1.f;
+    m_ref = up ? m_tile : m_ref;
+    l_run *= alpha;
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) oacc[cb] *= alpha;
+    for (int cb = 0; cb < CB; ++cb) oacc[cb] *= alpha;
+  }
   const float ref = m_ref == kNegInf ? 0.f : m_ref;
 #pragma unroll
   for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -365,7 +369,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   }
 
   // Epilogue: O = O / l, L = m ln2 + ln l.
-  const float l_tot = l_run + swap_halves(l_run);
+  const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qi < N) {
     bf16* orow = o + base + (size_t)qi * D;
@@ -677,7 +681,7 @@ void fwd_pingpong_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   }
   if (grp == 0) barrier_keep_loads();  // match group 1's extra barrier
 
-  const float l_tot = l_run + swap_halves(l_run);
+  const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qi < N) {
     bf16* orow = o + base + (size_t)qi * D;
