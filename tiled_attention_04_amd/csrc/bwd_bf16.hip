@@ -111,7 +111,8 @@ void bwd_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   __shared__ __attribute__((aligned(16))) float Ds[kBQ];
 
   const int t = threadIdx.x;
-  const int lane = t & 63, w = t >> 6, h = lane >> 5, l32 = lane & 31;
+  const int lane = t & 63, h = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform: keeps per-wave branches scalar
 
   int bh, kt;
   const int id = blockIdx.x;

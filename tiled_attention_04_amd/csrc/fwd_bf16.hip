@@ -120,19 +120,55 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int lo, int hi, int h)
   }
 }
 
+// Bounds of a lane's partial sum (its 32 keys of the tile) for which the
+// exponentials taken against the current reference are kept: above the cap
+// some P could exceed 2^14; below the floor (with nothing accumulated yet)
+// everything may have underflowed.
+constexpr float kSumCap = 16384.f;
+constexpr float kSumFloor = 0x1p-60f;
+
 // One tile of the online softmax for this lane's query row ("Building Flash
 // Attention from Scratch in Pure NumPy", Step 2): raw scores s (16 keys per
 // 32-key block, in the accumulator's row order) -> bf16 P in pk, with the
-// running reference m_ref and sum l_run updated and O rescaled by
-// 2^(m_old - m_new).  The reference is only raised when a tile's max exceeds
-// it by more than kTau (P = 2^(x - m) <= 2^kTau stays well inside bf16/fp32
-// range); O / l and L = m + log2(l) do not depend on that choice.
+// running reference m_ref (log2 units) and sum l_run updated and O rescaled
+// by 2^(m_old - m_new) when the reference moves.
+//
+// The reference is lazy: P = 2^(x - ref) is first computed against the
+// current reference (0 for a row that has none yet), and kept when every
+// lane's partial sum lies in [kSumFloor, kSumCap] -- then no P exceeds 2^14
+// and none that matters has underflowed, and the tile costs no max and no
+// rescale.  Otherwise (a row's first scores, a jump of the running max, or
+// keys all hidden so far) the wave takes the exact path: tile max, raise the
+// reference when the max exceeds it by more than kTau, rescale l and O, and
+// recompute P.  Rows that passed the test keep their reference and P.  O / l
+// and L = ref + log2(l) do not depend on the reference.
 // c = |scale| * log2(e), at least 1e-30 so that a hidden score (-inf) always
 // gives exp2(-inf * c - ref) = 0 exactly.
 template <int CB>
 __device__ __forceinline__ void softmax_tile(const f32x16 (&s)[2], uint32_t (&pk)[2][8],
                                              f32x16 (&oacc)[CB], float& m_ref, float& l_run,
                                              float c) {
+  auto exps = [&](float ref) {
+    float sum = 0.f;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][r], c, -ref));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][r + 1], c, -ref));
+        pk[kb2][r >> 1] = pack_bf16(p0, p1);
+        sum += p0 + p1;
+      }
+    }
+    return sum;
+  };
+  if (m_ref == kNegInf) m_ref = 0.f;
+  const float fast = exps(m_ref);
+  const bool keep = fast <= kSumCap && l_run + fast >= kSumFloor;
+  if (__builtin_amdgcn_ballot_w64(!keep) == 0) {
+    l_run += fast;
+    return;
+  }
   float mx = kNegInf;
 #pragma unroll
   for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -141,9 +177,12 @@ __device__ __forceinline__ void softmax_tile(const f32x16 (&s)[2], uint32_t (&pk
   }
   mx = pair_max(mx);
   const float m_tile = mx == kNegInf ? kNegInf : mx * c;
-  const bool up = m_tile > m_ref + kTau;
-  // Rescaling is rare once the running max has settled: skip it (a branch
-  // that is uniform over the wave) unless some row raises its reference.
+  // Only rows that failed the test move (both lanes of a row agree), so a
+  // row's result never depends on the other rows of the wave.  With nothing
+  // accumulated in the row yet, any finite reference will do: take the max.
+  const bool row_failed = pair_sum(keep ? 0.f : 1.f) != 0.f;
+  const bool up = row_failed &&
+                  (m_tile > m_ref + kTau || (pair_sum(l_run) == 0.f && m_tile != kNegInf));
   if (__builtin_amdgcn_ballot_w64(up) != 0) {
     const float alpha = up ? __builtin_amdgcn_exp2f(m_ref - m_tile) : 1.f;
     m_ref = up ? m_tile : m_ref;
@@ -151,17 +190,7 @@ __device__ __forceinline__ void softmax_tile(const f32x16 (&s)[2], uint32_t (&pk
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) oacc[cb] *= alpha;
   }
-  const float ref = m_ref == kNegInf ? 0.f : m_ref;
-#pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][r], c, -ref));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][r + 1], c, -ref));
-      pk[kb2][r >> 1] = pack_bf16(p0, p1);
-      l_run += p0 + p1;
-    }
-  }
+  l_run += exps(m_ref);
 }
 
 // Scheduling groups (masks of __builtin_amdgcn_sched_group_barrier).
@@ -210,7 +239,8 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   __shared__ __attribute__((aligned(1024))) char Vb1[TL::kVBytes];
 
   const int t = threadIdx.x;
-  const int lane = t & 63, w = t >> 6, h = lane >> 5, l32 = lane & 31;
+  const int lane = t & 63, h = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform: keeps per-wave branches scalar
 
   // Workgroup -> (batch*head, query tile).
   int bh, qr;
@@ -396,7 +426,11 @@ __device__ __forceinline__ void wait_vm(int n) {
     case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
     case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
     case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F78); break;
   }
 }
 
@@ -503,7 +537,8 @@ void fwd_pingpong_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   __shared__ int simd_slots[4];
 
   const int t = threadIdx.x;
-  const int lane = t & 63, w = t >> 6, h = lane >> 5, l32 = lane & 31;
+  const int lane = t & 63, h = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform: keeps per-wave branches scalar
 
   int bh, qr;
   const int id = blockIdx.x;
@@ -699,6 +734,7 @@ void fwd_pingpong_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       lse[(size_t)bh * N + qi] = l_tot > 0.f ? m_ref * kLn2 + logf(l_tot) : kNegInf;
   }
 }
+
 
 template <int D, int NW>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
