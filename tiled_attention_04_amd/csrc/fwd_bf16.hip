@@ -419,7 +419,8 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 }
 
 // s_waitcnt on the vector-memory counter only: wait until at most n of this
-// wave's vector loads (here: direct loads into LDS) are still in flight.
+// wave's vector loads (here: direct loads into LDS) are still in flight
+// (n above 12 waits for 12).
 __device__ __forceinline__ void wait_vm(int n) {
   switch (n) {  // the count is an immediate operand
     case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
@@ -430,7 +431,11 @@ __device__ __forceinline__ void wait_vm(int n) {
     case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
     case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
     case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
+    case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
+    case 11: __builtin_amdgcn_s_waitcnt(0x0F7B); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
   }
 }
 
@@ -503,6 +508,14 @@ __device__ __forceinline__ void pin_softmax_results(uint32_t (&pk)[2][8], f32x16
 #endif
 }
 
+// LDS stages of the ping-pong kernel (K and V each; 3 or 4).  Three keep the
+// direct loads two tiles ahead, which hides their latency (111 KB of LDS for
+// d = 128); four measured no faster.
+#ifndef FA_PINGPONG_STAGES
+#define FA_PINGPONG_STAGES 3
+#endif
+constexpr int kPingPongStages = FA_PINGPONG_STAGES;
+
 // Ping-pong group of the calling wave: the order in which waves arrive on
 // their SIMD (HW_ID bits 5:4), modulo 2, so that each SIMD hosts one wave of
 // each group when the workgroup's waves are spread evenly.  `slots` is a
@@ -527,13 +540,17 @@ void fwd_pingpong_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   constexpr int CB = D / 32;
   constexpr int KPER = (TL::kKBlocks + NW - 1) / NW;
   constexpr int VPER = (TL::kVBlocks + NW - 1) / NW;
+  constexpr int NS = kPingPongStages;  // LDS stages; loads run NS-1 tiles ahead
+  static_assert(NS == 3 || NS == 4, "3 or 4 stages");
   // One LDS object per stage and matrix (see the alias note in fwd_bf16_kernel).
   __shared__ __attribute__((aligned(1024))) char K0[TL::kKBytes];
   __shared__ __attribute__((aligned(1024))) char K1[TL::kKBytes];
   __shared__ __attribute__((aligned(1024))) char K2[TL::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char K3[NS > 3 ? TL::kKBytes : 1];
   __shared__ __attribute__((aligned(1024))) char V0[TL::kVBytes];
   __shared__ __attribute__((aligned(1024))) char V1[TL::kVBytes];
   __shared__ __attribute__((aligned(1024))) char V2[TL::kVBytes];
+  __shared__ __attribute__((aligned(1024))) char V3[NS > 3 ? TL::kVBytes : 1];
   __shared__ int simd_slots[4];
 
   const int t = threadIdx.x;
@@ -550,16 +567,8 @@ void fwd_pingpong_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const bf16* vg = v + base;
   const int qi = q0 + 32 * w + l32;
 
-  for (int i = t; i < TL::kKBytes / 16; i += T) {
-    ((uint4*)K0)[i] = uint4{0u, 0u, 0u, 0u};
-    ((uint4*)K1)[i] = uint4{0u, 0u, 0u, 0u};
-    ((uint4*)K2)[i] = uint4{0u, 0u, 0u, 0u};
-  }
-  for (int i = t; i < TL::kVBytes / 16; i += T) {
-    ((uint4*)V0)[i] = uint4{0u, 0u, 0u, 0u};
-    ((uint4*)V1)[i] = uint4{0u, 0u, 0u, 0u};
-    ((uint4*)V2)[i] = uint4{0u, 0u, 0u, 0u};
-  }
+  // (The stages need no clearing: a stage is read only after its tile has
+  // landed, except for the scores of a tile past the end, which are dropped.)
   if (t < 4) simd_slots[t] = 0;
   __syncthreads();
   // Group = order of arrival of this wave on its SIMD (HW_ID bits 5:4), so
@@ -571,7 +580,8 @@ void fwd_pingpong_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   for (int i = 0; i < KPER; ++i) kpre[i] = block_src<D>(w + i * NW, lane, TL::kKPitch);
 #pragma unroll
   for (int i = 0; i < VPER; ++i) vpre[i] = block_src<D>(w + i * NW, lane, TL::kVPitch);
-  const int v_nblk = (TL::kVBlocks - w + NW - 1) / NW;  // V blocks this wave loads per tile
+  const int k_nblk = (TL::kKBlocks - w + NW - 1) / NW;  // K / V blocks this wave loads per tile
+  const int v_nblk = (TL::kVBlocks - w + NW - 1) / NW;
 
   const rsrc_t q_src = make_rsrc(q + base, (uint32_t)N * D * 2u);
   bf16x8 qf[KS];
@@ -601,11 +611,11 @@ void fwd_pingpong_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   auto kstage = [&] __device__ (auto st) -> char* {
     constexpr int S = decltype(st)::value;
-    return S == 0 ? K0 : S == 1 ? K1 : K2;
+    return S == 0 ? K0 : S == 1 ? K1 : S == 2 ? K2 : K3;
   };
   auto vstage = [&] __device__ (auto st) -> char* {
     constexpr int S = decltype(st)::value;
-    return S == 0 ? V0 : S == 1 ? V1 : V2;
+    return S == 0 ? V0 : S == 1 ? V1 : S == 2 ? V2 : V3;
   };
   // This wave's share of the direct loads of tile `tile` into stage st (K
   // blocks first, then V, so that a wait for K can leave V in flight).
@@ -636,11 +646,19 @@ void fwd_pingpong_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   f32x16 sc[2];  // scores of the tile in flight
 
   using std::integral_constant;
-  // Prologue: tiles 0 and 1 resident, scores of tile 0.
+  // Loads of tile t by this wave (0 past the end).
+  auto n_loads = [&] __device__ (int tile) { return tile < kt1 ? k_nblk + v_nblk : 0; };
+  // Prologue: tiles kt0 .. kt0+NS-2 in flight, the first two resident, then
+  // the scores of tile kt0.
   load_share(kt0, integral_constant<int, 0>{});
   if (kt0 + 1 < kt1) load_share(kt0 + 1, integral_constant<int, 1>{});
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  if constexpr (NS > 3) {
+    if (kt0 + 2 < kt1) load_share(kt0 + 2, integral_constant<int, 2>{});
+    wait_vm(n_loads(kt0 + 2));
+  } else {
+    wait_vm(0);
+  }
+  barrier_keep_loads();
 #pragma unroll
   for (int kb2 = 0; kb2 < 2; ++kb2) {
     sc[kb2] = f32x16{};
@@ -651,15 +669,15 @@ void fwd_pingpong_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   if (grp == 1) barrier_keep_loads();  // group 1 runs one phase behind
 
   // One tile: softmax phase, barrier, matrix phase, barrier.  Stage of tile
-  // kt is ST (compile time); tile kt+1 is in stage (ST+1)%3 and tile kt+2 is
-  // loaded into stage (ST+2)%3.
+  // kt is ST (compile time); tile kt+1 is in stage (ST+1)%NS and tile
+  // kt+NS-1 is loaded into stage (ST+NS-1)%NS, the one tile kt-1 used.
   auto tile_step = [&] __device__ (auto stage, int kt) {
     constexpr int ST = decltype(stage)::value;
-    constexpr int STN = (ST + 1) % 3, STF = (ST + 2) % 3;
-    const bool has_next = kt + 1 < kt1;
-    const bool load_far = kt + 2 < kt1;
-    // ---- softmax phase (group 1 also issues its loads of tile kt+2 here)
-    if (grp == 1 && load_far) load_share(kt + 2, integral_constant<int, STF>{});
+    constexpr int STN = (ST + 1) % NS, STF = (ST + NS - 1) % NS;
+    const int far = kt + NS - 1;
+    const bool load_far = far < kt1;
+    // ---- softmax phase (group 1 also issues its loads of tile kt+NS-1 here)
+    if (grp == 1 && load_far) load_share(far, integral_constant<int, STF>{});
     const int k0 = kt * kBK;
     const bool need_mask = (k0 + kBK > N) || (causal && k0 + kBK - 1 > wq0) ||
                            (window >= 0 && k0 < wq1 - window);
@@ -667,12 +685,12 @@ void fwd_pingpong_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     uint32_t pk[2][8];
     softmax_tile<CB>(sc, pk, oacc, m_ref, l_run, c_log2);
     pin_softmax_results<CB>(pk, oacc, l_run, m_ref);
-    // Group 0: tile kt+1's K must be resident for its matrix phase; its V may
-    // stay in flight (group 0 loaded tile kt+1 in its previous matrix phase).
-    if (grp == 0) wait_vm(has_next ? v_nblk : 0);
+    // Group 0: tile kt+1's K must be resident for its matrix phase; its V
+    // and the tiles after it may stay in flight.
+    if (grp == 0) wait_vm((NS > 3 ? n_loads(kt + 2) : 0) + (kt + 1 < kt1 ? v_nblk : 0));
     barrier_keep_loads();
-    // ---- matrix phase (group 0 issues its loads of tile kt+2 here)
-    if (grp == 0 && load_far) load_share(kt + 2, integral_constant<int, STF>{});
+    // ---- matrix phase (group 0 issues its loads of tile kt+NS-1 here)
+    if (grp == 0 && load_far) load_share(far, integral_constant<int, STF>{});
     {
       const char* vt = vstage(integral_constant<int, ST>{}) + v_rd;
 #pragma unroll
@@ -701,18 +719,22 @@ void fwd_pingpong_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       }
       schedule_matrix_phase<4 * CB, 2 * KS>();
     }
-    // Group 1: its loads of tile kt+2 (issued this step) must have landed
-    // before group 0 needs K_{kt+2}; V may stay in flight.
-    if (grp == 1) wait_vm(load_far ? v_nblk : 0);
+    // Group 1: its K of tile kt+2 must have landed before group 0 needs it in
+    // the next matrix phase; V_{kt+2} and later tiles may stay in flight.
+    if (grp == 1) wait_vm((NS > 3 ? n_loads(kt + 3) : 0) + (kt + 2 < kt1 ? v_nblk : 0));
     barrier_keep_loads();
   };
 
-  for (int kt = kt0; kt < kt1; kt += 3) {
+  for (int kt = kt0; kt < kt1; kt += NS) {
     tile_step(integral_constant<int, 0>{}, kt);
     if (kt + 1 >= kt1) break;
     tile_step(integral_constant<int, 1>{}, kt + 1);
     if (kt + 2 >= kt1) break;
     tile_step(integral_constant<int, 2>{}, kt + 2);
+    if constexpr (NS > 3) {
+      if (kt + 3 >= kt1) break;
+      tile_step(integral_constant<int, 3 % NS>{}, kt + 3);
+    }
   }
   if (grp == 0) barrier_keep_loads();  // match group 1's extra barrier
 
