@@ -92,6 +92,18 @@ def test_bf16_ragged_masks_tiles(d, N, causal, window, bq):
     check_lse(lse, L, "L")
 
 
+@pytest.mark.parametrize("B,H,N,d", [(1, 160, 700, 128), (2, 96, 1100, 64)])
+@pytest.mark.parametrize("causal,window", [(True, -1), (False, -1), (True, 200), (False, 300)])
+def test_bf16_many_query_tiles_per_workgroup(B, H, N, d, causal, window):
+    """More 256-row query tiles than compute units, so each workgroup of the
+    256-row kernel runs several of them back to back (ragged N, all masks)."""
+    q, k, v = attention_inputs(B, H, N, d, "bf16", seed=N + H)
+    o, lse = run(q, k, v, causal, window, bq=256)
+    O, L = oracle.attention_ref(q, k, v, 1 / math.sqrt(d), causal, window)
+    check_bf16(o, O, "O")
+    check_lse(lse, L, "L")
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.3, 0.9])
 def test_bf16_scale_values(scale):
     q, k, v = attention_inputs(1, 3, 150, 128, "bf16", seed=3)
