@@ -240,7 +240,7 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(value / PEAK_BF16_TFLOPS, 4) if value is not None else None,
                      "traffic": measured_traffic("fwd_bf16_causal"),
-                     "kernel": "fwd_bf16_kernel<128, 4> (causal)"},
+                     "kernel": "fwd_pingpong_kernel<128> (causal; the automatic tile for this shape is 256 query rows)"},
         "components": components,
     }
     if not args.no_cpu_baseline and "fwd" in stages:

@@ -116,7 +116,7 @@ void bwd_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   int bh, kt;
   const int id = blockIdx.x;
-  tile_order(id, BH, nkt, bh, kt);  // heaviest key tile (kt = 0) first
+  tile_order(id, BH, nkt, causal && window < 0, bh, kt);  // heaviest key tile (kt = 0) first
   const int k0 = kt * kBKV;
   const size_t base = (size_t)bh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;

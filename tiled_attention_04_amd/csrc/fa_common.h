@@ -110,18 +110,33 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 // Workgroup id -> (head slice bh, tile rank r) for a grid of BH * ntiles
-// workgroups.  Ranks are dispatched in order (every head's rank 0 first,
-// then every head's rank 1, ...), so when rank 0 is the most expensive tile
-// the last workgroups to start are the cheapest ones and the tail of the
-// launch stays short.  Consecutive ids go round-robin over the 8 XCDs of the
-// chip, so when BH is a multiple of 8 every head stays on one XCD (its K/V
-// are shared in that XCD's L2).
-__device__ __forceinline__ void tile_order(int id, int BH, int ntiles, int& bh, int& r) {
-  (void)ntiles;
+// workgroups; rank 0 is dispatched first.  Consecutive ids go round-robin
+// over the 8 XCDs of the chip and, when BH is a multiple of 8, every head
+// stays on one XCD (its K/V are shared in that XCD's L2).  Two orders:
+//  * spread (for plain causal attention, where rank 0 is the most expensive
+//    tile and the cost falls with the rank): all heads rank by rank, so the
+//    last workgroups to start are the cheapest ones and the tail stays short;
+//  * grouped (work about the same for every tile): each XCD walks its heads
+//    in groups of two, all ranks of a group before the next group, so only a
+//    few heads are live per XCD and their K/V stay in its L2.
+__device__ __forceinline__ void tile_order(int id, int BH, int ntiles, bool spread, int& bh, int& r) {
   if ((BH & 7) == 0) {
     const int xcd = id & 7, slot = id >> 3, nbh8 = BH >> 3;
-    r = slot / nbh8;
-    bh = (slot - r * nbh8) * 8 + xcd;
+    const int G = spread ? nbh8 : 2;  // heads per group and XCD
+    const int full = nbh8 / G;        // groups of G heads; a last group may hold fewer
+    int grp, hh;
+    if (slot < full * G * ntiles) {
+      grp = slot / (G * ntiles);
+      const int rem = slot - grp * G * ntiles;
+      r = rem / G;
+      hh = rem - r * G;
+    } else {
+      const int rem = slot - full * G * ntiles, last = nbh8 - full * G;
+      grp = full;
+      r = rem / last;
+      hh = rem - r * last;
+    }
+    bh = (grp * G + hh) * 8 + xcd;
   } else {
     r = id / BH;
     bh = id - r * BH;

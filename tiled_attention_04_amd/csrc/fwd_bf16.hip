@@ -245,7 +245,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   // Workgroup -> (batch*head, query tile).
   int bh, qr;
   const int id = blockIdx.x;
-  tile_order(id, BH, nqt, bh, qr);
+  tile_order(id, BH, nqt, causal && window < 0, bh, qr);
   const int qt = causal ? nqt - 1 - qr : qr;
   const int q0 = qt * BQ;
   const size_t base = (size_t)bh * (size_t)N * D;
@@ -559,7 +559,7 @@ void fwd_pingpong_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   int bh, qr;
   const int id = blockIdx.x;
-  tile_order(id, BH, nqt, bh, qr);
+  tile_order(id, BH, nqt, causal && window < 0, bh, qr);
   const int qt = causal ? nqt - 1 - qr : qr;
   const int q0 = qt * BQ;
   const size_t base = (size_t)bh * (size_t)N * D;
