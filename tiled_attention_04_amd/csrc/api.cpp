@@ -51,12 +51,13 @@ fa_status check_dense(int B, int H, int N, int d, float scale, int causal, int w
   return FA_OK;
 }
 
-int auto_block_q(int B, int H, int N) {
+int auto_block_q(int B, int H, int N, int window) {
   // Prefer the 8-wave ping-pong kernel (256 query rows, one workgroup per
-  // CU) while it still fills the 256 CUs of an MI355X; then 4-wave
+  // CU) while it still fills the 256 CUs of an MI355X -- except under a
+  // sliding window, where the 4-wave kernel measured faster; then 4-wave
   // workgroups (two per CU); then smaller query tiles.
   const long long bh = (long long)B * H;
-  if (bh * ((N + 255) / 256) >= 256) return 256;
+  if (window < 0 && bh * ((N + 255) / 256) >= 256) return 256;
   if (bh * ((N + 127) / 128) >= 512) return 128;
   if (bh * ((N + 63) / 64) >= 256) return 64;
   return 32;
@@ -100,7 +101,7 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float*
                 "fa_fwd (float32)");
   }
   if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "bf16 forward supports d in {64, 128} (got %d)", d);
-  if (block_q == 0) block_q = auto_block_q(B, H, N);
+  if (block_q == 0) block_q = auto_block_q(B, H, N, window);
   if (block_k == 0) block_k = 64;
   if ((block_q != 32 && block_q != 64 && block_q != 128 && block_q != 256) || block_k != 64)
     return fail(FA_ERR_INVALID_ARG, "bf16 tiles must be {32,64,128,256} x 64 (got %d x %d)", block_q, block_k);

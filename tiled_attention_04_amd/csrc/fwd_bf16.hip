@@ -604,6 +604,15 @@ void fwd_pingpong_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int key_lo = window >= 0 ? qi - window : 0;
   const int key_hi = causal ? min(qi, N - 1) : N - 1;
   const int wq0 = q0 + 32 * w, wq1 = wq0 + 31;
+  // Keys visible to at least one row of this wave: tiles outside this range
+  // (past a causal diagonal, before a window) are skipped by the wave, which
+  // still takes part in the loads and barriers.
+  const int wk_lo = window >= 0 ? max(0, wq0 - window) : 0;
+  const int wk_hi = wq0 < N ? (causal ? min(N - 1, wq1) : N - 1) : -1;
+  auto active = [&] __device__ (int tile) {
+    const int k0 = tile * kBK;
+    return k0 <= wk_hi && k0 + kBK - 1 >= wk_lo;
+  };
 
   const int k_rd = l32 * TL::kKPitch + 16 * h;
   const int g = lane >> 4, gi = lane & 15;
@@ -678,12 +687,20 @@ void fwd_pingpong_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const bool load_far = far < kt1;
     // ---- softmax phase (group 1 also issues its loads of tile kt+NS-1 here)
     if (grp == 1 && load_far) load_share(far, integral_constant<int, STF>{});
-    const int k0 = kt * kBK;
-    const bool need_mask = (k0 + kBK > N) || (causal && k0 + kBK - 1 > wq0) ||
-                           (window >= 0 && k0 < wq1 - window);
-    if (need_mask) mask_tile(sc, key_lo - k0, key_hi - k0, h);
+    const bool act = active(kt), act_next = kt + 1 < kt1 && active(kt + 1);
     uint32_t pk[2][8];
-    softmax_tile<CB>(sc, pk, oacc, m_ref, l_run, c_log2);
+    if (act) {
+      const int k0 = kt * kBK;
+      const bool need_mask = (k0 + kBK > N) || (causal && k0 + kBK - 1 > wq0) ||
+                             (window >= 0 && k0 < wq1 - window);
+      if (need_mask) mask_tile(sc, key_lo - k0, key_hi - k0, h);
+      softmax_tile<CB>(sc, pk, oacc, m_ref, l_run, c_log2);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pk[i][j] = 0u;  // (P V adds nothing)
+    }
     pin_softmax_results<CB>(pk, oacc, l_run, m_ref);
     // Group 0: tile kt+1's K must be resident for its matrix phase; its V
     // and the tiles after it may stay in flight.
@@ -693,31 +710,38 @@ void fwd_pingpong_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     if (grp == 0 && load_far) load_share(far, integral_constant<int, STF>{});
     {
       const char* vt = vstage(integral_constant<int, ST>{}) + v_rd;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint4 pw = {pk[s >> 1][4 * (s & 1) + 0], pk[s >> 1][4 * (s & 1) + 1],
-                          pk[s >> 1][4 * (s & 1) + 2], pk[s >> 1][4 * (s & 1) + 3]};
-        const bf16x8 pb = as_bf16x8(pw);
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          const char* p = vt + 16 * s * TL::kVPitch + 64 * cb;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * TL::kVPitch));
-          const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-          oacc[cb] = mfma32(as_bf16x8(uint4{l2.x, l2.y, h2.x, h2.y}), pb, oacc[cb]);
-        }
-      }
-      // Scores of tile kt+1 (computed from whatever the stage holds and
-      // discarded if there is no such tile).
       const char* kn = kstage(integral_constant<int, STN>{}) + k_rd;
+      // P V of this tile, then the scores of tile kt+1.
+      auto pv = [&] __device__ () {
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        sc[kb2] = mfma32(*(const bf16x8*)(kn + kb2 * 32 * TL::kKPitch), qf[0], f32x16{});
+        for (int s = 0; s < 4; ++s) {
+          const uint4 pw = {pk[s >> 1][4 * (s & 1) + 0], pk[s >> 1][4 * (s & 1) + 1],
+                            pk[s >> 1][4 * (s & 1) + 2], pk[s >> 1][4 * (s & 1) + 3]};
+          const bf16x8 pb = as_bf16x8(pw);
 #pragma unroll
-        for (int s = 1; s < KS; ++s)
-          sc[kb2] = mfma32(*(const bf16x8*)(kn + kb2 * 32 * TL::kKPitch + 32 * s), qf[s], sc[kb2]);
+          for (int cb = 0; cb < CB; ++cb) {
+            const char* p = vt + 16 * s * TL::kVPitch + 64 * cb;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * TL::kVPitch));
+            const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+            oacc[cb] = mfma32(as_bf16x8(uint4{l2.x, l2.y, h2.x, h2.y}), pb, oacc[cb]);
+          }
+        }
+      };
+      auto qk = [&] __device__ () {
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          sc[kb2] = mfma32(*(const bf16x8*)(kn + kb2 * 32 * TL::kKPitch), qf[0], f32x16{});
+#pragma unroll
+          for (int s = 1; s < KS; ++s)
+            sc[kb2] = mfma32(*(const bf16x8*)(kn + kb2 * 32 * TL::kKPitch + 32 * s), qf[s], sc[kb2]);
+        }
+      };
+      if (act || act_next) {  // (a wave past all its keys does no matrix work)
+        pv();
+        qk();
+        schedule_matrix_phase<4 * CB, 2 * KS>();
       }
-      schedule_matrix_phase<4 * CB, 2 * KS>();
     }
     // Group 1: its K of tile kt+2 must have landed before group 0 needs it in
     // the next matrix phase; V_{kt+2} and later tiles may stay in flight.
