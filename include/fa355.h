@@ -155,8 +155,8 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d);
  *   dq, dk, dv     : [B, H, N, d] float32 outputs
  *   workspace      : >= fa_bwd_workspace_size(B, H, N, d) bytes
  *
- * Supported: FA_BF16 with d in {64, 128}.  dq is accumulated with float32
- * atomics, so its last bits may differ from run to run.
+ * Supported: FA_BF16 with d in {64, 128}.  No atomics: dq, dk and dv are
+ * each written once, so repeated calls give identical bits.
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
                  const float* lse, float* dq, float* dk, float* dv,

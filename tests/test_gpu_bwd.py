@@ -76,3 +76,24 @@ def test_full_size_sampled_heads():
         check_bf16(dq[b, h], rq[0], f"dQ[{b},{h}]")
         check_bf16(dk[b, h], rk[0], f"dK[{b},{h}]")
         check_bf16(dv[b, h], rv[0], f"dV[{b},{h}]")
+
+
+@pytest.mark.parametrize("B,H,N,d", [(1, 3, 700, 128), (1, 2, 1100, 64)])
+@pytest.mark.parametrize("causal,window", [(False, -1), (True, -1), (True, 100), (False, 50)])
+def test_several_tiles_ragged(B, H, N, d, causal, window):
+    """Several 128-key and 128-query tiles of both kernels, a ragged tail."""
+    q, k, v, dO = attention_inputs(B, H, N, d, "bf16", seed=N + 7 * d, with_grad=True)
+    dq, dk, dv = run(q, k, v, dO, causal, window)
+    rq, rk, rv = oracle.attention_bwd_ref(q, k, v, dO, 1 / math.sqrt(d), causal, window)
+    check_bf16(dq, rq, "dQ")
+    check_bf16(dk, rk, "dK")
+    check_bf16(dv, rv, "dV")
+
+
+def test_backward_is_deterministic():
+    """No atomics: two calls on the same inputs give identical bits."""
+    q, k, v, dO = attention_inputs(2, 4, 515, 128, "bf16", seed=3, with_grad=True)
+    a = run(q, k, v, dO, True)
+    b = run(q, k, v, dO, True)
+    for x, y, name in zip(a, b, ("dQ", "dK", "dV")):
+        assert torch.equal(x, y), name

@@ -170,7 +170,11 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   if ((long long)N * d * 4 > kMaxBufferBytes)
     return fail(FA_ERR_UNSUPPORTED, "one (batch, head) slice of the float32 gradients exceeds 2 GiB");
   const long long rows = (long long)B * H * N;
-  if (rows * 256 / (d / 8) > kMaxThreadsPerLaunch) return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  const long long pre_rows_per_block = 2048 / d;  // 256 threads, d / 8 per row
+  const long long pre_threads = (rows + pre_rows_per_block - 1) / pre_rows_per_block * 256;
+  const long long main_threads = (long long)((N + 127) / 128) * B * H * 512;  // 128 keys per workgroup
+  if (pre_threads > kMaxThreadsPerLaunch || main_threads > kMaxThreadsPerLaunch)
+    return fail(FA_ERR_UNSUPPORTED, "grid too large");
   const size_t need = fa::bwd_workspace_bytes(B, H, N, d);
   if (!workspace || workspace_bytes < need)
     return fail(FA_ERR_WORKSPACE, "backward needs %zu workspace bytes (got %zu%s)", need, workspace_bytes,

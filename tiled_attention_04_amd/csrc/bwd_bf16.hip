@@ -8,62 +8,55 @@
 //   P = exp(S - L),  dV += P^T dO,  dP = dO V^T,  dS = P * (dP - D),
 //   dK += scale * dS^T Q,  dQ += scale * dS K.
 //
-// Mapping onto CDNA4 (v_mfma_f32_32x32x16_bf16, fp32 accumulation):
-//  * bwd_pre: one 16-byte slice per lane, D reduced with DPP; it also zeroes
-//    dq and stores L in log2 units so the main kernel needs one exp2 per score.
-//  * bwd_main: a workgroup of 4 waves owns 128 keys (32 per wave) for its
-//    whole life: the wave's K and V rows sit in registers as MFMA B operands
-//    and its dK, dV accumulators in registers.  It walks the 64-row query
-//    tiles that see those keys; each tile's Q and dO are staged in LDS both
-//    row-major (A operands of S = Q K^T and dP = dO V^T) and transposed (B
-//    operands of dK and dV), the transposed copies with the row order of the
-//    accumulator layout so that P and dS feed the next MFMAs straight from
-//    registers.  dS is also written to LDS so that dQ = dS K can be formed per
-//    query row; dQ is accumulated in float32 with atomics.  The next query
-//    tile is prefetched into registers while the current one is computed.
+// Mapping onto CDNA4 (v_mfma_f32_32x32x16_bf16, fp32 accumulation), three
+// kernels on one stream:
+//  * bwd_pre: one 16-byte slice per lane, D reduced with DPP; it also stores
+//    L in log2 units so the other kernels need one exp2 per score.
+//  * bwd_main: dK and dV, in the page's loop order (key/value tiles outer):
+//    a workgroup of 8 waves owns a 128-key tile and walks the query tiles.
+//  * bwd_dq: dQ, with the loops the other way round (a workgroup owns 128
+//    query rows and walks the key tiles, as the forward does), recomputing
+//    S, P, dP and dS; no atomics, so dQ is deterministic.
 #include "fa_common.h"
 #include "fa_launch.h"
 
 namespace fa {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;     // main kernel: 8 waves
+constexpr int kPreThreads = 256;  // preprocessing kernel
 constexpr int kBKV = 128;  // keys per workgroup
 constexpr int kBQ = 64;    // queries per step
 
-template <int W>
-__device__ __forceinline__ int rm_off(int row, int chunk) {  // row-major [rows][W], swizzled
-  return row * W + ((chunk ^ (row & 7)) << 3);
-}
+constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedDSRead = 0x100;
 
-// Transposed [D][64] tile with the accumulator's row order (bits 2 and 3 of
-// the row index swapped within each group of 16) and a chunk swizzle.
-__device__ __forceinline__ int tpos(int u) { return (u & ~12) | ((u & 4) << 1) | ((u & 8) >> 1); }
-__device__ __forceinline__ int t64_off(int c, int pos) {
-  return c * kBQ + ((((pos >> 3) ^ ((c + (c >> 3)) & 7))) << 3) + (pos & 7);
-}
-
-// Two packed bf16 columns of four rows -> the 4 values of column cc.
-__device__ __forceinline__ uint2 column4(const uint4 (&r)[4], int cc) {
-  const uint32_t a0 = word(r[0], cc >> 1), a1 = word(r[1], cc >> 1);
-  const uint32_t a2 = word(r[2], cc >> 1), a3 = word(r[3], cc >> 1);
-  uint2 out;
-  if (cc & 1) {
-    out.x = (a0 >> 16) | (a1 & 0xffff0000u);
-    out.y = (a2 >> 16) | (a3 & 0xffff0000u);
-  } else {
-    out.x = (a0 & 0xffffu) | (a1 << 16);
-    out.y = (a2 & 0xffffu) | (a3 << 16);
+// Scheduling pattern for a block of M MFMAs fed by R LDS reads, with V
+// vector-ALU instructions of independent work placed after each MFMA: the
+// first A reads go ahead, the rest are spread evenly over the MFMAs.  Keeps
+// the compiler from hoisting every operand read (which runs out of registers
+// at one wave per SIMD) while the reads still run ahead of their MFMAs.
+template <int I, int M, int R, int A, int V, int SYNC>
+__device__ __forceinline__ void interleave_step() {
+  if constexpr (I < M) {
+    constexpr int n = (I + 1) * (R - A) / M - I * (R - A) / M;
+    __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, SYNC);
+    if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, n, SYNC);
+    if constexpr (V > 0) __builtin_amdgcn_sched_group_barrier(kSchedVALU, V, SYNC);
+    interleave_step<I + 1, M, R, A, V, SYNC>();
   }
-  return out;
+}
+template <int M, int R, int A, int V, int SYNC>
+__device__ __forceinline__ void interleave() {
+  __builtin_amdgcn_sched_group_barrier(kSchedDSRead, A, SYNC);
+  interleave_step<0, M, R, A, V, SYNC>();
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_pre_kernel(
+__global__ __launch_bounds__(kPreThreads) void bwd_pre_kernel(
     const bf16* __restrict__ o, const bf16* __restrict__ dO, const float* __restrict__ lse,
-    float* __restrict__ Dv, float* __restrict__ L2, float* __restrict__ dq, long long rows) {
+    float* __restrict__ Dv, float* __restrict__ L2, long long rows) {
   constexpr int LPR = D / 8;
-  constexpr int RPB = kThreads / LPR;
+  constexpr int RPB = kPreThreads / LPR;
   const int t = threadIdx.x;
   const long long row = (long long)blockIdx.x * RPB + t / LPR;
   const int e = t % LPR;
@@ -77,9 +70,6 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(
       p = __builtin_fmaf(bf16_lo(word(a, i)), bf16_lo(word(b, i)), p);
       p = __builtin_fmaf(bf16_hi(word(a, i)), bf16_hi(word(b, i)), p);
     }
-    const float4 z = {0.f, 0.f, 0.f, 0.f};
-    *(float4*)(dq + off) = z;
-    *(float4*)(dq + off + 4) = z;
   }
   p = group_sum<LPR>(p);
   if (row < rows && e == 0) {
@@ -89,71 +79,81 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(
   }
 }
 
+// Main backward kernel: dK and dV.  A workgroup of 8 waves (two per SIMD)
+// owns 128 keys and walks the 64-row query tiles that see them.  Wave
+// w = (kb, qb), kb = w % 4 and qb = w / 4:
+//  * scores: S = Q K^T and dP = dO V^T for its 32 keys (block kb) and the
+//    tile's query rows 32 qb .. 32 qb + 31; Q, dO and K come from LDS as MFMA
+//    A / B operands, V from registers;
+//  * P = exp2(S c - L2) and dS = P (dP - D) on the vector ALUs, written to LDS
+//    (keys as rows) in the order of the MFMA A operand, so every wave reads
+//    P^T and dS^T of a key block for all 64 queries with 16-byte reads;
+//  * gradients: dV += P^T dO and dK += dS^T Q for the wave's key block and
+//    half of the columns, over all 64 queries (B operands by transpose reads
+//    of the row-major dO and Q tiles).
+// Q, dO, L2 and D of the next query tile stream into LDS by direct loads
+// while the current one is processed (two stages); the K tile is loaded once.
+// dQ is formed by its own kernel (below): accumulated here it would take one
+// float atomic per query row, column and key tile, and those atomics cost
+// about as much as all the rest of this kernel.
 template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+struct BwdTile {
+  static constexpr int kQPitch = D == 128 ? 304 : 144;  // bytes per Q / dO / K row in LDS
+  static constexpr int kSPitch = 144;                    // bytes per P^T / dS^T row (64 queries)
+  static constexpr int kQBytes = kBQ * kQPitch;
+  static constexpr int kKBytes = kBKV * kQPitch;
+  static constexpr int kSBytes = kBKV * kSPitch;
+  static constexpr int kQBlocks = kQBytes / 1024;  // 1 KB per wave-wide direct load
+  static constexpr int kKBlocks = kKBytes / 1024;
+  static_assert(kQBytes % 1024 == 0 && kKBytes % 1024 == 0, "tiles must be whole 1 KB blocks");
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                      const bf16* __restrict__ v, const bf16* __restrict__ dO,
                      const float* __restrict__ Dv, const float* __restrict__ L2,
-                     float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv,
+                     float* __restrict__ dk, float* __restrict__ dv,
                      int BH, int N, int nkt, float scale, float scale_log2, int causal, int window) {
-  constexpr int KS = D / 16;
-  constexpr int CB = D / 32;
-  constexpr int CPR = D / 8;                  // 16-byte chunks per row
-  constexpr int QUNITS = (kBQ / 4) * CPR;     // 4-row x 16-byte units of a Q tile
-  constexpr int KUNITS = (kBKV / 4) * CPR;
-  __shared__ __attribute__((aligned(16))) bf16 Qs[kBQ * D];
-  __shared__ __attribute__((aligned(16))) bf16 dOs[kBQ * D];
-  __shared__ __attribute__((aligned(16))) bf16 Qt[D * kBQ];
-  __shared__ __attribute__((aligned(16))) bf16 dOt[D * kBQ];
-  __shared__ __attribute__((aligned(16))) bf16 Kt[D * kBKV];
-  __shared__ __attribute__((aligned(16))) bf16 dSs[kBQ * kBKV];
-  __shared__ __attribute__((aligned(16))) float Ls[kBQ];
-  __shared__ __attribute__((aligned(16))) float Ds[kBQ];
+  using TL = BwdTile<D>;
+  constexpr int NW = kThreads / 64;  // 8
+  constexpr int KS = D / 16;         // 16-wide steps over the head dimension
+  constexpr int CB = D / 32;         // 32-column blocks of the head dimension
+  constexpr int NCB = CB / 2;        // column blocks of dK / dV per wave
+  constexpr int QPER = (TL::kQBlocks + NW - 1) / NW;
+  constexpr int KPER = (TL::kKBlocks + NW - 1) / NW;
+  constexpr int QP = TL::kQPitch, SP = TL::kSPitch;
+  // One LDS object per stage and matrix (the compiler then knows that direct
+  // loads into one stage do not alias reads of the other).
+  __shared__ __attribute__((aligned(1024))) char Q0[TL::kQBytes];
+  __shared__ __attribute__((aligned(1024))) char Q1[TL::kQBytes];
+  __shared__ __attribute__((aligned(1024))) char O0[TL::kQBytes];
+  __shared__ __attribute__((aligned(1024))) char O1[TL::kQBytes];
+  __shared__ __attribute__((aligned(1024))) char Kt[TL::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char Pt[TL::kSBytes];
+  __shared__ __attribute__((aligned(1024))) char dSt[TL::kSBytes];
+  __shared__ __attribute__((aligned(256))) float LD0[2 * kBQ];  // L2 then D of a query tile
+  __shared__ __attribute__((aligned(256))) float LD1[2 * kBQ];
 
   const int t = threadIdx.x;
   const int lane = t & 63, h = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform: keeps per-wave branches scalar
+  const int kb = w & 3, qb = w >> 2;
 
   int bh, kt;
-  const int id = blockIdx.x;
-  tile_order(id, BH, nkt, causal && window < 0, bh, kt);  // heaviest key tile (kt = 0) first
+  tile_order(blockIdx.x, BH, nkt, causal && window < 0, bh, kt);  // heaviest key tile (kt = 0) first
   const int k0 = kt * kBKV;
   const size_t base = (size_t)bh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
-  const rsrc_t q_src = make_rsrc(q + base, head_bytes);
-  const rsrc_t k_src = make_rsrc(k + base, head_bytes);
-  const rsrc_t v_src = make_rsrc(v + base, head_bytes);
-  const rsrc_t do_src = make_rsrc(dO + base, head_bytes);
-  const float* Lrow = L2 + (size_t)bh * N;
-  const float* Drow = Dv + (size_t)bh * N;
 
-  // This wave's 32 keys as B fragments: K[key][16 s + 8 h + 0..7], same for V.
-  const int my_key = k0 + 32 * w + l32;
-  bf16x8 kf[KS], vf[KS];
+  // This wave's 32 value rows as B operands of dP: V[key][16 s + 8 h + 0..7].
+  const int my_key = k0 + 32 * kb + l32;
+  bf16x8 vf[KS];
+  {
+    const rsrc_t v_src = make_rsrc(v + base, head_bytes);
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    const uint32_t off = (uint32_t)(my_key * D + 16 * s + 8 * h) * 2u;
-    kf[s] = as_bf16x8(load16(k_src, off));
-    vf[s] = as_bf16x8(load16(v_src, off));
-  }
-  // K^T of the whole key tile in LDS (natural key order) for dQ = dS K.
-  for (int i = t; i < KUNITS; i += kThreads) {
-    const int co = i % CPR, kq = i / CPR;
-    uint4 r[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) r[e] = load16(k_src, (uint32_t)((k0 + 4 * kq + e) * D + co * 8) * 2u);
-#pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
-      const int c = co * 8 + cc;
-      *(uint2*)(Kt + c * kBKV + ((((4 * kq) >> 3) ^ (c & 7)) << 3) + ((4 * kq) & 7)) = column4(r, cc);
-    }
-  }
-
-  f32x16 dk_acc[CB], dv_acc[CB];
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    dk_acc[cb] = f32x16{};
-    dv_acc[cb] = f32x16{};
+    for (int s = 0; s < KS; ++s)
+      vf[s] = as_bf16x8(load16(v_src, (uint32_t)(my_key * D + 16 * s + 8 * h) * 2u));
   }
 
   // Query tiles that see at least one of this workgroup's keys.
@@ -162,171 +162,355 @@ void bwd_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int qmax = window >= 0 ? min(N - 1, k_hi + window) : N - 1;
   const int qt0 = qmin / kBQ, qt1 = qmax / kBQ + 1;
 
-  // Prefetch registers for one query tile: 4 rows x 16 bytes of Q and dO.
-  uint4 qr[4], dr[4];
-  float lv = 0.f;
-  auto prefetch = [&](int qt) {
-    const int q0 = qt * kBQ;
-    if (QUNITS >= kThreads || t < QUNITS) {
-      const int co = t % CPR, qq = t / CPR;
+  // Direct-load source offsets of this lane (padding lanes read nothing).
+  uint32_t qpre[QPER];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t off = (uint32_t)((q0 + 4 * qq + e) * D + co * 8) * 2u;
-        qr[e] = load16(q_src, off);
-        dr[e] = load16(do_src, off);
+  for (int i = 0; i < QPER; ++i) qpre[i] = block_src<D>(w + i * NW, lane, QP);
+
+  auto stage_q = [&] __device__ (auto st) -> char* { return decltype(st)::value == 0 ? Q0 : Q1; };
+  auto stage_o = [&] __device__ (auto st) -> char* { return decltype(st)::value == 0 ? O0 : O1; };
+  auto stage_ld = [&] __device__ (auto st) -> float* { return decltype(st)::value == 0 ? LD0 : LD1; };
+  const float* Lrow = L2 + (size_t)bh * N;
+  const float* Drow = Dv + (size_t)bh * N;
+  // This wave's share of the direct loads of query tile qt into stage st:
+  // Q and dO blocks, and (waves 0 and 1) the tile's 64 values of L2 / D.
+  auto load_qtile = [&] __device__ (int qt, auto st) {
+    const int q0 = qt * kBQ;
+    const uint32_t bytes = (uint32_t)max(0, N - q0) * D * 2u;
+    const rsrc_t qs = make_rsrc(q + base + (size_t)q0 * D, bytes);
+    const rsrc_t os = make_rsrc(dO + base + (size_t)q0 * D, bytes);
+    char* qd = stage_q(st);
+    char* od = stage_o(st);
+#pragma unroll
+    for (int i = 0; i < QPER; ++i) {
+      const int blk = w + i * NW;
+      if (blk < TL::kQBlocks) {
+        load_lds16(qs, qd + blk * 1024, qpre[i]);
+        load_lds16(os, od + blk * 1024, qpre[i]);
       }
     }
-    if (t < kBQ) lv = q0 + t < N ? Lrow[q0 + t] : __builtin_inff();
-    else if (t < 2 * kBQ) lv = q0 + t - kBQ < N ? Drow[q0 + t - kBQ] : 0.f;
+    if (w < 2) {
+      const rsrc_t ls = make_rsrc((w == 0 ? Lrow : Drow) + q0, (uint32_t)max(0, N - q0) * 4u);
+      load_lds4(ls, stage_ld(st) + w * kBQ, (uint32_t)lane * 4u);
+    }
   };
 
-  if (qt0 < qt1) prefetch(qt0);
-  for (int qt = qt0; qt < qt1; ++qt) {
+  using std::integral_constant;
+  // Prologue: the K tile and the first query tile resident.
+  {
+    const rsrc_t ks = make_rsrc(k + base + (size_t)k0 * D, (uint32_t)max(0, N - k0) * D * 2u);
+#pragma unroll
+    for (int i = 0; i < KPER; ++i) {
+      const int blk = w + i * NW;
+      if (blk < TL::kKBlocks) load_lds16(ks, Kt + blk * 1024, block_src<D>(blk, lane, QP));
+    }
+  }
+  if (qt0 < qt1) load_qtile(qt0, integral_constant<int, 0>{});
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  f32x16 dk_acc[NCB], dv_acc[NCB];
+#pragma unroll
+  for (int c = 0; c < NCB; ++c) {
+    dk_acc[c] = f32x16{};
+    dv_acc[c] = f32x16{};
+  }
+  const int q_rd = (32 * qb + l32) * QP + 16 * h;       // A operands of S and dP
+  const int k_rd = (32 * kb + l32) * QP + 16 * h;       // B operands of S
+  const int s_wr = (32 * kb + l32) * SP + (32 * qb + 8 * h) * 2;  // this lane's P / dS pieces
+  const int s_rd = (32 * kb + l32) * SP + 16 * h;       // A operands of dV / dK
+  const int tr_q = tr_addr<QP>(lane);                   // B operands of dV / dK
+
+  // One query tile in stage ST.
+  auto tile = [&] __device__ (auto stage, int qt) {
+    constexpr int ST = decltype(stage)::value;
+    const char* Qs = stage_q(stage);
+    const char* Os = stage_o(stage);
+    const float* LD = stage_ld(stage);
     const int q0 = qt * kBQ;
-    __syncthreads();  // every read of the previous tile's LDS is done
-    if (QUNITS >= kThreads || t < QUNITS) {
-      const int co = t % CPR, qq = t / CPR;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        *(uint4*)(Qs + rm_off<D>(4 * qq + e, co)) = qr[e];
-        *(uint4*)(dOs + rm_off<D>(4 * qq + e, co)) = dr[e];
-      }
-      const int pos = tpos(4 * qq);
-#pragma unroll
-      for (int cc = 0; cc < 8; ++cc) {
-        *(uint2*)(Qt + t64_off(co * 8 + cc, pos)) = column4(qr, cc);
-        *(uint2*)(dOt + t64_off(co * 8 + cc, pos)) = column4(dr, cc);
-      }
-    }
-    if (t < kBQ) Ls[t] = lv;
-    else if (t < 2 * kBQ) Ds[t - kBQ] = lv;
-    __syncthreads();
-    if (qt + 1 < qt1) prefetch(qt + 1);
-
-    // S = Q K^T and dP = dO V^T for the tile's two 32-row blocks.
-    f32x16 sacc[2], dpacc[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      sacc[qb] = f32x16{};
-      dpacc[qb] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const bf16x8 a = *(const bf16x8*)(Qs + rm_off<D>(qb * 32 + l32, 2 * s + h));
-        sacc[qb] = mfma32(a, kf[s], sacc[qb]);
-      }
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const bf16x8 a = *(const bf16x8*)(dOs + rm_off<D>(qb * 32 + l32, 2 * s + h));
-        dpacc[qb] = mfma32(a, vf[s], dpacc[qb]);
-      }
-    }
-
-    // P = exp2(S * scale * log2e - L2) and dS = P (dP - D), masked.
+    if (qt + 1 < qt1) load_qtile(qt + 1, integral_constant<int, ST ^ 1>{});
     const bool need_mask = (causal && q0 < k_hi) || (window >= 0 && q0 + kBQ - 1 - k0 > window) ||
                            (k_hi >= N) || (q0 + kBQ > N);
-    uint32_t ppk[2][8], dspk[2][8];
+
+    // 1) S = Q K^T, then dP = dO V^T while P = exp2(S * scale * log2e - L2)
+    //    (masked) is formed on the vector ALUs.
+    f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int s = 0; s < KS; ++s)
+      sacc = mfma32(*(const bf16x8*)(Qs + q_rd + 32 * s), *(const bf16x8*)(Kt + k_rd + 32 * s), sacc);
+    interleave<KS, 2 * KS, 4, 0, 1>();
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 L4 = *(const float4*)(Ls + qb * 32 + 8 * g + 4 * h);
-        const float4 D4 = *(const float4*)(Ds + qb * 32 + 8 * g + 4 * h);
-        float pv[4], dsv[4];
+    for (int s = 0; s < KS; ++s)
+      dpacc = mfma32(*(const bf16x8*)(Os + q_rd + 32 * s), vf[s], dpacc);
+    float pv[16];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * g + i;
-          const float Li = i == 0 ? L4.x : i == 1 ? L4.y : i == 2 ? L4.z : L4.w;
-          const float Di = i == 0 ? D4.x : i == 1 ? D4.y : i == 2 ? D4.z : D4.w;
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][r], scale_log2, -Li));
-          if (need_mask) {
-            const int qrow = q0 + qb * 32 + 8 * g + 4 * h + i;
-            const bool vis = my_key < N && qrow < N && (!causal || my_key <= qrow) &&
-                             (window < 0 || my_key >= qrow - window);
-            p = vis ? p : 0.f;
-          }
-          pv[i] = p;
-          dsv[i] = p * (dpacc[qb][r] - Di);
+    for (int g = 0; g < 4; ++g) {
+      const float4 L4 = *(const float4*)(LD + 32 * qb + 8 * g + 4 * h);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float Li = i == 0 ? L4.x : i == 1 ? L4.y : i == 2 ? L4.z : L4.w;
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * g + i], scale_log2, -Li));
+        if (need_mask) {
+          const int qrow = q0 + 32 * qb + 8 * g + 4 * h + i;
+          // (bitwise: short-circuit tests would branch per element)
+          const bool vis = (my_key < N) & (qrow < N) & (!causal | (my_key <= qrow)) &
+                           ((window < 0) | (my_key >= qrow - window));
+          p = vis ? p : 0.f;
         }
-        ppk[qb][2 * g] = pack_bf16(pv[0], pv[1]);
-        ppk[qb][2 * g + 1] = pack_bf16(pv[2], pv[3]);
-        dspk[qb][2 * g] = pack_bf16(dsv[0], dsv[1]);
-        dspk[qb][2 * g + 1] = pack_bf16(dsv[2], dsv[3]);
+        pv[4 * g + i] = p;
       }
     }
+    uint32_t ppk[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ppk[j] = pack_bf16(pv[2 * j], pv[2 * j + 1]);
+    interleave<KS, KS, 4, 6, 2>();
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t dspk[8];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float4 D4 = *(const float4*)(LD + kBQ + 32 * qb + 8 * g + 4 * h);
+      dspk[2 * g] = pack_bf16(pv[4 * g] * (dpacc[4 * g] - D4.x), pv[4 * g + 1] * (dpacc[4 * g + 1] - D4.y));
+      dspk[2 * g + 1] = pack_bf16(pv[4 * g + 2] * (dpacc[4 * g + 2] - D4.z),
+                                  pv[4 * g + 3] * (dpacc[4 * g + 3] - D4.w));
+    }
+    // P^T and dS^T rows: this lane's key, its 16 queries in A-operand order.
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      *(uint4*)(Pt + s_wr + 32 * j) = uint4{ppk[4 * j], ppk[4 * j + 1], ppk[4 * j + 2], ppk[4 * j + 3]};
+      *(uint4*)(dSt + s_wr + 32 * j) = uint4{dspk[4 * j], dspk[4 * j + 1], dspk[4 * j + 2], dspk[4 * j + 3]};
+    }
+    // LDS writes done, then the barrier; direct loads stay in flight.
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 
-    // dV += P^T dO and dK += dS^T Q, 16 queries per step.
+    // 2) dV += P^T dO and dK += dS^T Q over the tile's 64 queries (16 per
+    //    step) for this wave's column blocks.
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const uint4 pw = {ppk[s >> 1][4 * (s & 1)], ppk[s >> 1][4 * (s & 1) + 1],
-                        ppk[s >> 1][4 * (s & 1) + 2], ppk[s >> 1][4 * (s & 1) + 3]};
+      const bf16x8 pa = *(const bf16x8*)(Pt + s_rd + 32 * s);
+      const bf16x8 da = *(const bf16x8*)(dSt + s_rd + 32 * s);
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) {
+        const int off = tr_q + 16 * s * QP + 64 * (NCB * qb + c);
+        dv_acc[c] = mfma32(pa, read_tr8<QP>(Os + off), dv_acc[c]);
+        dk_acc[c] = mfma32(da, read_tr8<QP>(Qs + off), dk_acc[c]);
+      }
+    }
+    interleave<8 * NCB, 8 + 16 * NCB, 4, 0, 3>();
+    __builtin_amdgcn_sched_barrier(0);
+
+    // The next tile's direct loads have landed; after the barrier no wave
+    // reads this stage, P^T or dS^T any more.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+
+  for (int qt = qt0; qt < qt1; qt += 2) {
+    tile(integral_constant<int, 0>{}, qt);
+    if (qt + 1 >= qt1) break;
+    tile(integral_constant<int, 1>{}, qt + 1);
+  }
+
+  // dK = scale * dS^T Q, dV = P^T dO for key block kb and this wave's column
+  // blocks; rows past N fall outside the buffers and are dropped.
+  const rsrc_t dk_dst = make_rsrc(dk + base, (uint32_t)N * D * 4u);
+  const rsrc_t dv_dst = make_rsrc(dv + base, (uint32_t)N * D * 4u);
+#pragma unroll
+  for (int c = 0; c < NCB; ++c) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const uint32_t off =
+          ((uint32_t)(k0 + 32 * kb + c_row(r, h)) * D + 32 * (NCB * qb + c) + l32) * 4u;
+      store_f32(dk_dst, off, scale * dk_acc[c][r]);
+      store_f32(dv_dst, off, dv_acc[c][r]);
+    }
+  }
+}
+
+// dQ kernel: dQ = scale * dS K without atomics.  A workgroup of 4 waves owns
+// 128 query rows (32 per wave, one per lane pair as in the forward kernels)
+// and walks the 64-key tiles they see, recomputing per tile
+//   S^T = K Q^T,  dP^T = V dO^T   (Q and dO rows in registers as B operands,
+//                                  K and V rows from LDS as A operands),
+//   P^T = exp2(S^T * scale * log2e - L2),  dS^T = P^T (dP^T - D)
+//                                 (L2 and D: one value per lane),
+//   dQ^T += K^T dS^T              (K^T by transpose reads of the K tile, dS^T
+//                                  packed to bf16 straight from the
+//                                  accumulators, as P in the forward).
+// K and V tiles are double-buffered in LDS and filled by direct loads.
+constexpr int kDqBK = 64;   // keys per tile
+constexpr int kDqThreads = 256;
+
+template <int D>
+struct DqTile {
+  static constexpr int kKPitch = D == 128 ? 304 : 144;  // K rows: 16-byte and transpose reads
+  static constexpr int kVPitch = 2 * D + 16;             // V rows: 16-byte reads
+  static constexpr int kKBytes = kDqBK * kKPitch;
+  static constexpr int kVBytes = kDqBK * kVPitch;
+  static constexpr int kKBlocks = kKBytes / 1024;
+  static constexpr int kVBlocks = kVBytes / 1024;
+  static_assert(kKBytes % 1024 == 0 && kVBytes % 1024 == 0, "tiles must be whole 1 KB blocks");
+};
+
+template <int D>
+__global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                   const bf16* __restrict__ v, const bf16* __restrict__ dO,
+                   const float* __restrict__ Dv, const float* __restrict__ L2,
+                   float* __restrict__ dq, int BH, int N, int nqt, float scale, float scale_log2,
+                   int causal, int window) {
+  using TL = DqTile<D>;
+  constexpr int NW = kDqThreads / 64;
+  constexpr int BQ = 32 * NW;
+  constexpr int KS = D / 16;
+  constexpr int CB = D / 32;
+  constexpr int KPER = (TL::kKBlocks + NW - 1) / NW;
+  constexpr int VPER = (TL::kVBlocks + NW - 1) / NW;
+  constexpr int KP = TL::kKPitch, VP = TL::kVPitch;
+  __shared__ __attribute__((aligned(1024))) char Kb0[TL::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char Kb1[TL::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char Vb0[TL::kVBytes];
+  __shared__ __attribute__((aligned(1024))) char Vb1[TL::kVBytes];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, h = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+
+  int bh, qr;
+  tile_order(blockIdx.x, BH, nqt, causal && window < 0, bh, qr);
+  const int qt = causal ? nqt - 1 - qr : qr;  // causal: the longest rows first
+  const int q0 = qt * BQ;
+  const size_t base = (size_t)bh * (size_t)N * D;
+  const int qi = q0 + 32 * w + l32;  // this lane's query row
+
+  // Q and dO rows of this lane as B fragments: [qi][16 s + 8 h + 0..7]
+  // (rows past N read as zero), and the row's L2 and D.
+  bf16x8 qf[KS], of[KS];
+  {
+    const rsrc_t q_src = make_rsrc(q + base, (uint32_t)N * D * 2u);
+    const rsrc_t o_src = make_rsrc(dO + base, (uint32_t)N * D * 2u);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const uint32_t off = (uint32_t)(qi * D + 16 * s + 8 * h) * 2u;
+      qf[s] = as_bf16x8(load16(q_src, off));
+      of[s] = as_bf16x8(load16(o_src, off));
+    }
+  }
+  const bool row_ok = qi < N;
+  const float Li = row_ok ? L2[(size_t)bh * N + qi] : 0.f;
+  const float Di = row_ok ? Dv[(size_t)bh * N + qi] : 0.f;
+
+  // Key tiles holding at least one key visible to this query tile, and the
+  // keys this lane's row sees.
+  const int q_hi = q0 + BQ - 1;
+  const int kmin = window >= 0 ? max(0, q0 - window) : 0;
+  const int kmax = causal ? min(N - 1, q_hi) : N - 1;
+  const int kt0 = kmin / kDqBK, kt1 = kmax / kDqBK + 1;
+  const int key_lo = window >= 0 ? qi - window : 0;
+  const int key_hi = causal ? min(qi, N - 1) : N - 1;
+
+  uint32_t kpre[KPER], vpre[VPER];
+#pragma unroll
+  for (int i = 0; i < KPER; ++i) kpre[i] = block_src<D>(w + i * NW, lane, KP);
+#pragma unroll
+  for (int i = 0; i < VPER; ++i) vpre[i] = block_src<D>(w + i * NW, lane, VP);
+  auto load_kv = [&] __device__ (int kt, char* kd, char* vd) {
+    const int k0 = kt * kDqBK;
+    const uint32_t bytes = (uint32_t)max(0, N - k0) * D * 2u;
+    const rsrc_t ks = make_rsrc(k + base + (size_t)k0 * D, bytes);
+    const rsrc_t vs = make_rsrc(v + base + (size_t)k0 * D, bytes);
+#pragma unroll
+    for (int i = 0; i < KPER; ++i)
+      if (w + i * NW < TL::kKBlocks) load_lds16(ks, kd + (w + i * NW) * 1024, kpre[i]);
+#pragma unroll
+    for (int i = 0; i < VPER; ++i)
+      if (w + i * NW < TL::kVBlocks) load_lds16(vs, vd + (w + i * NW) * 1024, vpre[i]);
+  };
+
+  const int k_rd = l32 * KP + 16 * h;  // A operands of S^T (K rows)
+  const int v_rd = l32 * VP + 16 * h;  // A operands of dP^T (V rows)
+  const int k_tr = tr_addr<KP>(lane);  // A operands of dQ^T (K^T)
+
+  f32x16 dqa[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) dqa[cb] = f32x16{};
+
+  if (kt0 < kt1) load_kv(kt0, Kb0, Vb0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  auto tile = [&] __device__ (auto parity, int kt) {
+    constexpr int P = decltype(parity)::value;
+    const char* Kc = P ? Kb1 : Kb0;
+    const char* Vc = P ? Vb1 : Vb0;
+    if (kt + 1 < kt1) load_kv(kt + 1, P ? Kb0 : Kb1, P ? Vb0 : Vb1);
+    const int k0 = kt * kDqBK;
+    const bool need_mask = (k0 + kDqBK > N) || (causal && k0 + kDqBK - 1 > q0) ||
+                           (window >= 0 && k0 < q_hi - window);
+
+    // S^T and dP^T for the tile's two 32-key blocks.
+    f32x16 sacc[2], dpacc[2];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      sacc[kb2] = f32x16{};
+      dpacc[kb2] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        sacc[kb2] = mfma32(*(const bf16x8*)(Kc + k_rd + kb2 * 32 * KP + 32 * s), qf[s], sacc[kb2]);
+        dpacc[kb2] = mfma32(*(const bf16x8*)(Vc + v_rd + kb2 * 32 * VP + 32 * s), of[s], dpacc[kb2]);
+      }
+    }
+    // dS^T = P^T (dP^T - D), P^T = exp2(S^T c - L2) with hidden keys at 0.
+    uint32_t dspk[2][8];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float ds[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb2][r + u], scale_log2, -Li));
+          if (need_mask) {
+            const int key = k0 + kb2 * 32 + c_row(r + u, h);
+            p = ((key >= key_lo) & (key <= key_hi)) ? p : 0.f;
+          }
+          ds[u] = p * (dpacc[kb2][r + u] - Di);
+        }
+        dspk[kb2][r >> 1] = pack_bf16(ds[0], ds[1]);
+      }
+    }
+    // dQ^T += K^T dS^T, 16 keys per step.
+#pragma unroll
+    for (int s = 0; s < kDqBK / 16; ++s) {
       const uint4 dw = {dspk[s >> 1][4 * (s & 1)], dspk[s >> 1][4 * (s & 1) + 1],
                         dspk[s >> 1][4 * (s & 1) + 2], dspk[s >> 1][4 * (s & 1) + 3]};
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const int off = t64_off(cb * 32 + l32, 16 * s + 8 * h);
-        dv_acc[cb] = mfma32(as_bf16x8(pw), *(const bf16x8*)(dOt + off), dv_acc[cb]);
-        dk_acc[cb] = mfma32(as_bf16x8(dw), *(const bf16x8*)(Qt + off), dk_acc[cb]);
-      }
+      for (int cb = 0; cb < CB; ++cb)
+        dqa[cb] = mfma32(read_tr8<KP>(Kc + k_tr + 16 * s * KP + 64 * cb), as_bf16x8(dw), dqa[cb]);
     }
-
-    // dS (bf16) to LDS in natural [query][key] order for dQ.
-    {
-      const int kl = 32 * w + l32;
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ql = qb * 32 + c_row(r, h);
-          const uint32_t pair = dspk[qb][r >> 1];
-          const uint16_t bits = (r & 1) ? (uint16_t)(pair >> 16) : (uint16_t)(pair & 0xffffu);
-          *(uint16_t*)(dSs + ql * kBKV + ((((kl >> 3) ^ (ql & 7))) << 3) + (kl & 7)) = bits;
-        }
-      }
-    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads of the next tile have landed
     __syncthreads();
+  };
 
-    // dQ[64 x D] += dS K: wave w forms rows 32*(w/2).. and column blocks
-    // 2*(w%2) + {0, 1} of D=128 (column block w%2 of D=64).
-    {
-      constexpr int NCB = CB / 2;
-      const int qb = w >> 1;
-      f32x16 dqacc[NCB];
-#pragma unroll
-      for (int j = 0; j < NCB; ++j) dqacc[j] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < kBKV / 16; ++s) {
-        const bf16x8 a = *(const bf16x8*)(dSs + rm_off<kBKV>(qb * 32 + l32, 2 * s + h));
-#pragma unroll
-        for (int j = 0; j < NCB; ++j) {
-          const int c = (NCB * (w & 1) + j) * 32 + l32;
-          const bf16x8 b = *(const bf16x8*)(Kt + c * kBKV + (((2 * s + h) ^ (c & 7)) << 3));
-          dqacc[j] = mfma32(a, b, dqacc[j]);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < NCB; ++j) {
-        const int c = (NCB * (w & 1) + j) * 32 + l32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qrow = q0 + qb * 32 + c_row(r, h);
-          if (qrow < N) unsafeAtomicAdd(dq + base + (size_t)qrow * D + c, scale * dqacc[j][r]);
-        }
-      }
-    }
+  for (int kt = kt0; kt < kt1; kt += 2) {
+    tile(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 >= kt1) break;
+    tile(std::integral_constant<int, 1>{}, kt + 1);
   }
 
-  // dK = scale * dS^T Q, dV = P^T dO for this wave's 32 keys.
+  // dQ row qi: element r of block cb is column 32 cb + c_row(r, h); four
+  // consecutive columns per 16-byte store.
+  if (row_ok) {
+    float* drow = dq + base + (size_t)qi * D;
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int krow = k0 + 32 * w + c_row(r, h);
-      if (krow < N) {
-        const size_t off = base + (size_t)krow * D + cb * 32 + l32;
-        dk[off] = scale * dk_acc[cb][r];
-        dv[off] = dv_acc[cb][r];
-      }
-    }
+      for (int g = 0; g < 4; ++g)
+        *(float4*)(drow + 32 * cb + 8 * g + 4 * h) =
+            float4{scale * dqa[cb][4 * g], scale * dqa[cb][4 * g + 1], scale * dqa[cb][4 * g + 2],
+                   scale * dqa[cb][4 * g + 3]};
   }
 }
 
@@ -337,16 +521,23 @@ hipError_t launch_t(const void* q, const void* k, const void* v, const void* o, 
   const long long rows = (long long)B * H * N;
   float* Dv = (float*)ws;
   float* L2 = Dv + rows;
-  constexpr int RPB = kThreads / (D / 8);
-  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(kThreads),
-                     0, stream, (const bf16*)o, (const bf16*)dO, lse, Dv, L2, dq, rows);
+  constexpr int RPB = kPreThreads / (D / 8);
+  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(kPreThreads),
+                     0, stream, (const bf16*)o, (const bf16*)dO, lse, Dv, L2, rows);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int nkt = (N + kBKV - 1) / kBKV;
   const long long grid = (long long)nkt * B * H;
   hipLaunchKernelGGL((bwd_main_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dO, Dv, L2, dq, dk,
-                     dv, B * H, N, nkt, scale, scale * kLog2e, mask.causal, mask.window);
+                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dO, Dv, L2, dk, dv,
+                     B * H, N, nkt, scale, scale * kLog2e, mask.causal, mask.window);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  constexpr int BQ = kDqThreads / 2;  // 32 query rows per wave
+  const int nqt = (N + BQ - 1) / BQ;
+  hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)((long long)nqt * B * H)), dim3(kDqThreads), 0,
+                     stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dO, Dv, L2,
+                     dq, B * H, N, nqt, scale, scale * kLog2e, mask.causal, mask.window);
   return hipGetLastError();
 }
 

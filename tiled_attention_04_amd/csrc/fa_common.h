@@ -49,6 +49,17 @@ __device__ __forceinline__ uint4 load16(rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
+// One float to a buffer at a byte offset (dropped past the buffer's end).
+// The value is first forced into a VGPR: a store whose data is an element
+// of an accumulator vector held in AGPRs has been compiled to store the
+// vector's first element for every index.
+__device__ __forceinline__ void store_f32(rsrc_t r, uint32_t byte_off, float x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm("" : "+v"(x));
+#endif
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, byte_off, 0, 0);
+}
+
 // ---------------------------------------------------------------- MFMA ----
 // v_mfma_f32_32x32x16_bf16.  Operand layout (wave64):
 //   A (32 x 16, row-major M x K): lane l holds A[l % 32][8 * (l / 32) + 0..7]
@@ -141,6 +152,54 @@ __device__ __forceinline__ void tile_order(int id, int BH, int ntiles, bool spre
     r = id / BH;
     bh = id - r * BH;
   }
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// One 16-byte (4-byte) direct load per lane from a buffer resource into LDS:
+// lane l's bytes land at dst + 16 l (dst + 4 l); dst is wave-uniform.  Kept
+// out of lambdas: the host pass rejects this builtin there and then silently
+// drops the kernel.
+__device__ __forceinline__ void load_lds16(rsrc_t src, char* dst, uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)dst, 16, voffset, 0, 0, 0);
+}
+__device__ __forceinline__ void load_lds4(rsrc_t src, void* dst, uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)dst, 4, voffset, 0, 0, 0);
+}
+
+// Global byte offset (within the tile) that lane `lane` of direct-load block
+// `blk` must fetch, for a tile stored with `pitch` bytes per row; lanes that
+// land on row padding get an offset past any buffer so they read zero.
+template <int D>
+__device__ __forceinline__ uint32_t block_src(int blk, int lane, int pitch) {
+  const int pos = blk * 1024 + lane * 16;
+  const int row = pos / pitch, col = pos - row * pitch;
+  return col < D * 2 ? (uint32_t)(row * D * 2 + col) : 0x80000000u;
+}
+
+// V^T-style operand of one 32x32x16 MFMA from a row-major bf16 tile in LDS:
+// two transpose reads, 8 rows apart, at this lane's address a.
+template <int PITCH>
+__device__ __forceinline__ bf16x8 read_tr8(const char* a) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 8 * PITCH));
+  const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+  return as_bf16x8(uint4{l2.x, l2.y, h2.x, h2.y});
+}
+
+// This lane's transpose-read address in a row-major bf16 tile with
+// PITCH-byte rows.  With +16 s rows (a 16-row step) and +64 c bytes (a
+// 32-column block) read_tr8 yields, in lane l, 8 rows of column 32 c + l % 32
+// -- rows 16 s + {0..3, 8..11} in the lower half of the wave and
+// 16 s + {4..7, 12..15} in the upper half, the row order of the 32x32 MFMA
+// accumulator -- i.e. the operand "row block of 32, 16 along K" of an MFMA
+// whose K dimension runs along the tile's rows.
+template <int PITCH>
+__device__ __forceinline__ int tr_addr(int lane) {
+  const int g = lane >> 4, gi = lane & 15;
+  return (4 * (g >> 1) + (gi >> 2)) * PITCH + (16 * (g & 1) + 4 * (gi & 3)) * 2;
 }
 
 }  // namespace fa

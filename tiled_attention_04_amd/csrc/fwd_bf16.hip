@@ -63,27 +63,6 @@ struct Tile {
   static constexpr int kSmem = 2 * (kKBytes + kVBytes);
 };
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// One 16-byte direct load per lane from a buffer resource into LDS: lane l's
-// bytes land at dst + 16 l (dst is wave-uniform).  Kept out of lambdas: the
-// host pass rejects this builtin there and then silently drops the kernel.
-__device__ __forceinline__ void load_lds16(rsrc_t src, char* dst, uint32_t voffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)dst, 16, voffset, 0, 0, 0);
-}
-
-// Global byte offset (within the tile) that lane `lane` of direct-load block
-// `blk` must fetch, for a tile stored with `pitch` bytes per row; lanes that
-// land on row padding get an offset past any buffer so they read zero.
-template <int D>
-__device__ __forceinline__ uint32_t block_src(int blk, int lane, int pitch) {
-  const int pos = blk * 1024 + lane * 16;
-  const int row = pos / pitch, col = pos - row * pitch;
-  return col < D * 2 ? (uint32_t)(row * D * 2 + col) : 0x80000000u;
-}
-
 // Issue this wave's share of the direct loads of one tile (rows k0.. of a
 // [N][D] bf16 matrix) into an LDS tile with `PITCH`-byte rows.
 template <int D, int NW, int NBLK, int PITCH, bool PRE, int NPRE>
@@ -534,7 +513,6 @@ void fwd_pingpong_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                          int BH, int N, int nqt, float c_log2, int negate_q, int causal, int window) {
   using TL = Tile<D>;
   constexpr int NW = 8;
-  constexpr int T = 64 * NW;
   constexpr int BQ = 32 * NW;
   constexpr int KS = D / 16;
   constexpr int CB = D / 32;
