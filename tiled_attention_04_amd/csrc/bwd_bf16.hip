@@ -138,6 +138,7 @@ void bwd_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int t = threadIdx.x;
   const int lane = t & 63, h = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform: keeps per-wave branches scalar
+  __builtin_assume(w >= 0 && w < NW);
   const int kb = w & 3, qb = w >> 2;
 
   int bh, kt;
@@ -247,18 +248,21 @@ void bwd_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const float4 L4 = *(const float4*)(LD + 32 * qb + 8 * g + 4 * h);
+      pv[4 * g + 0] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * g + 0], scale_log2, -L4.x));
+      pv[4 * g + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * g + 1], scale_log2, -L4.y));
+      pv[4 * g + 2] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * g + 2], scale_log2, -L4.z));
+      pv[4 * g + 3] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * g + 3], scale_log2, -L4.w));
+    }
+    // Hidden pairs get P = 0 (one branch around the whole tile: inside the
+    // element loop the test would be evaluated on every tile).
+    if (need_mask) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float Li = i == 0 ? L4.x : i == 1 ? L4.y : i == 2 ? L4.z : L4.w;
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * g + i], scale_log2, -Li));
-        if (need_mask) {
-          const int qrow = q0 + 32 * qb + 8 * g + 4 * h + i;
-          // (bitwise: short-circuit tests would branch per element)
-          const bool vis = (my_key < N) & (qrow < N) & (!causal | (my_key <= qrow)) &
-                           ((window < 0) | (my_key >= qrow - window));
-          p = vis ? p : 0.f;
-        }
-        pv[4 * g + i] = p;
+      for (int r = 0; r < 16; ++r) {
+        const int qrow = q0 + 32 * qb + c_row(r, h);
+        const int lo = window >= 0 ? qrow - window : 0;
+        const int hi = min(causal ? qrow : N - 1, N - 1);
+        const bool vis = (qrow < N) & ((uint32_t)(my_key - lo) <= (uint32_t)(hi - lo));
+        pv[r] = vis ? pv[r] : 0.f;
       }
     }
     uint32_t ppk[8];
@@ -377,6 +381,7 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int t = threadIdx.x;
   const int lane = t & 63, h = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  __builtin_assume(w >= 0 && w < NW);
 
   int bh, qr;
   tile_order(blockIdx.x, BH, nqt, causal && window < 0, bh, qr);
@@ -462,25 +467,31 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         dpacc[kb2] = mfma32(*(const bf16x8*)(Vc + v_rd + kb2 * 32 * VP + 32 * s), of[s], dpacc[kb2]);
       }
     }
-    // dS^T = P^T (dP^T - D), P^T = exp2(S^T c - L2) with hidden keys at 0.
+    // dS^T = P^T (dP^T - D), P^T = exp2(S^T c - L2) with hidden keys at 0
+    // (the mask is one branch around the whole tile: inside the element
+    // loop it would be evaluated on every tile).
+    // (P^T overwrites S^T in place.)
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        sacc[kb2][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb2][r], scale_log2, -Li));
+    if (need_mask) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + kb2 * 32 + c_row(r, h);
+          sacc[kb2][r] = (uint32_t)(key - key_lo) <= (uint32_t)(key_hi - key_lo) ? sacc[kb2][r] : 0.f;
+        }
+    }
     uint32_t dspk[2][8];
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
+    for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float ds[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb2][r + u], scale_log2, -Li));
-          if (need_mask) {
-            const int key = k0 + kb2 * 32 + c_row(r + u, h);
-            p = ((key >= key_lo) & (key <= key_hi)) ? p : 0.f;
-          }
-          ds[u] = p * (dpacc[kb2][r + u] - Di);
-        }
-        dspk[kb2][r >> 1] = pack_bf16(ds[0], ds[1]);
-      }
-    }
+      for (int r = 0; r < 16; r += 2)
+        dspk[kb2][r >> 1] = pack_bf16(sacc[kb2][r] * (dpacc[kb2][r] - Di),
+                                      sacc[kb2][r + 1] * (dpacc[kb2][r + 1] - Di));
     // dQ^T += K^T dS^T, 16 keys per step.
 #pragma unroll
     for (int s = 0; s < kDqBK / 16; ++s) {
