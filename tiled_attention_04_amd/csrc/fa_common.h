@@ -202,4 +202,44 @@ __device__ __forceinline__ int tr_addr(int lane) {
   return (4 * (g >> 1) + (gi >> 2)) * PITCH + (16 * (g & 1) + 4 * (gi & 3)) * 2;
 }
 
+// s_waitcnt on the vector-memory counter only: wait until at most n of this
+// wave's vector loads (here: direct loads into LDS) are still in flight
+// (n above 12 waits for 12).
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {  // the count is an immediate operand
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
+    case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
+    case 11: __builtin_amdgcn_s_waitcnt(0x0F7B); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
+  }
+}
+
+// Workgroup barrier that does not drain outstanding vector loads (unlike
+// __syncthreads, whose release fence waits for every memory operation).  The
+// "memory" clobber keeps LDS accesses on their side of it and the scheduling
+// barriers keep all other instructions there too (the ping-pong phases rely
+// on it).
+__device__ __forceinline__ void barrier_keep_loads() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// The same, after this wave's LDS writes have completed (for data other
+// waves read after the barrier).
+__device__ __forceinline__ void barrier_after_lds_writes() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 }  // namespace fa
