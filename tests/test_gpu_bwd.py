@@ -97,3 +97,19 @@ def test_backward_is_deterministic():
     b = run(q, k, v, dO, True)
     for x, y, name in zip(a, b, ("dQ", "dK", "dV")):
         assert torch.equal(x, y), name
+
+
+@pytest.mark.parametrize("B,H,N,d", [(1, 64, 1100, 128), (1, 128, 600, 64)])
+@pytest.mark.parametrize("causal,window", [(False, -1), (True, -1), (True, 300), (False, 200)])
+def test_many_heads_256_row_dq_tiles(B, H, N, d, causal, window):
+    """Enough (head, 256-row tile) pairs to fill the chip, which selects the
+    256-row dQ kernel; ragged tails; sampled heads against the oracle."""
+    q, k, v, dO = attention_inputs(B, H, N, d, "bf16", seed=N + d + H, with_grad=True)
+    dq, dk, dv = run(q, k, v, dO, causal, window)
+    s = 1 / math.sqrt(d)
+    for h in (0, H // 2 + 5, H - 1):
+        rq, rk, rv = oracle.attention_bwd_ref(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1],
+                                              dO[:, h:h + 1], s, causal, window)
+        check_bf16(dq[:, h:h + 1], rq, f"dQ[h={h}]")
+        check_bf16(dk[:, h:h + 1], rk, f"dK[h={h}]")
+        check_bf16(dv[:, h:h + 1], rv, f"dV[h={h}]")

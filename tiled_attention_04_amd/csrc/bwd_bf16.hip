@@ -525,6 +525,263 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   }
 }
 
+// Ping-pong dQ kernel for long sequences: 8 waves, 256 query rows per
+// workgroup, the same computation as bwd_dq_kernel.  The waves form two groups
+// (by their order of arrival on a SIMD, one wave of each group per SIMD) that
+// run the tile loop one phase apart with workgroup barriers between phases:
+// while one group's waves form P and dS of tile j on the vector ALUs, the
+// other group's waves issue their matrix work -- dQ of tile j, then S and dP
+// of tile j+1 -- so every SIMD's matrix core has work while its vector ALU is
+// busy.  K and V tiles sit in three LDS stages; every wave loads its share of
+// tile j+2 while tiles j and j+1 are in use, and waits for its own loads just
+// before the barrier that opens group 0's next matrix phase.
+constexpr int kDqPPThreads = 512;
+
+template <int D>
+struct DqPPTile {
+  static constexpr int kKPitch = D == 128 ? 304 : 144;  // K rows: 16-byte and transpose reads
+  static constexpr int kVPitch = 2 * D + 16;             // V rows: 16-byte reads
+  static constexpr int kKBytes = kDqBK * kKPitch;
+  static constexpr int kVBytes = kDqBK * kVPitch;
+  static constexpr int kKBlocks = kKBytes / 1024;
+  static constexpr int kVBlocks = kVBytes / 1024;
+  static_assert(kKBytes % 1024 == 0 && kVBytes % 1024 == 0, "tiles must be whole 1 KB blocks");
+};
+
+// Keeps the vector-ALU results of a phase on their side of the barrier that
+// follows (compiler passes would otherwise sink the arithmetic next to its
+// only users, the MFMAs of the next phase).
+template <int CB>
+__device__ __forceinline__ void pin_dq_phase(uint32_t (&ds)[2][8], f32x16 (&acc)[CB]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(ds[i][j]));
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) asm volatile("" : "+v"(acc[cb]));
+#endif
+}
+
+template <int D>
+__global__ __launch_bounds__(kDqPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_pp_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                      const bf16* __restrict__ v, const bf16* __restrict__ dO,
+                      const float* __restrict__ Dv, const float* __restrict__ L2,
+                      float* __restrict__ dq, int BH, int N, int nqt, float scale, float scale_log2,
+                      int causal, int window) {
+  using TL = DqPPTile<D>;
+  constexpr int NW = kDqPPThreads / 64;
+  constexpr int BQ = 32 * NW;
+  constexpr int KS = D / 16;
+  constexpr int CB = D / 32;
+  constexpr int KPER = (TL::kKBlocks + NW - 1) / NW;
+  constexpr int VPER = (TL::kVBlocks + NW - 1) / NW;
+  constexpr int KP = TL::kKPitch, VP = TL::kVPitch;
+  __shared__ __attribute__((aligned(1024))) char K0[TL::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char K1[TL::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char K2[TL::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char V0[TL::kVBytes];
+  __shared__ __attribute__((aligned(1024))) char V1[TL::kVBytes];
+  __shared__ __attribute__((aligned(1024))) char V2[TL::kVBytes];
+  __shared__ int simd_slots[4];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, h = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  __builtin_assume(w >= 0 && w < NW);
+
+  int bh, qr;
+  tile_order(blockIdx.x, BH, nqt, causal && window < 0, bh, qr);
+  const int qt = causal ? nqt - 1 - qr : qr;  // causal: the longest rows first
+  const int q0 = qt * BQ;
+  const size_t base = (size_t)bh * (size_t)N * D;
+  const int qi = q0 + 32 * w + l32;  // this lane's query row
+
+  if (t < 4) simd_slots[t] = 0;
+  __syncthreads();
+  const int grp = wave_group(simd_slots, lane);
+
+  // Q and dO rows of this lane as B fragments (rows past N read as zero), and
+  // the row's L2 and D.
+  bf16x8 qf[KS], of[KS];
+  {
+    const rsrc_t q_src = make_rsrc(q + base, (uint32_t)N * D * 2u);
+    const rsrc_t o_src = make_rsrc(dO + base, (uint32_t)N * D * 2u);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const uint32_t off = (uint32_t)(qi * D + 16 * s + 8 * h) * 2u;
+      qf[s] = as_bf16x8(load16(q_src, off));
+      of[s] = as_bf16x8(load16(o_src, off));
+    }
+  }
+  const bool row_ok = qi < N;
+  const float Li = row_ok ? L2[(size_t)bh * N + qi] : 0.f;
+  const float Di = row_ok ? Dv[(size_t)bh * N + qi] : 0.f;
+
+  // Key tiles holding at least one key visible to this query tile, the keys
+  // this lane's row sees, and the tiles that hold any key visible to this
+  // wave's 32 rows (the others it skips).
+  const int q_hi = q0 + BQ - 1;
+  const int kmin = window >= 0 ? max(0, q0 - window) : 0;
+  const int kmax = causal ? min(N - 1, q_hi) : N - 1;
+  const int kt0 = kmin / kDqBK, kt1 = kmax / kDqBK + 1;
+  const int key_lo = window >= 0 ? qi - window : 0;
+  const int key_hi = causal ? min(qi, N - 1) : N - 1;
+  const int wq0 = q0 + 32 * w, wq1 = wq0 + 31;
+  const int wk_lo = window >= 0 ? max(0, wq0 - window) : 0;
+  const int wk_hi = wq0 < N ? (causal ? min(N - 1, wq1) : N - 1) : -1;
+  auto active = [&] __device__ (int tile) {
+    const int k0 = tile * kDqBK;
+    return k0 <= wk_hi && k0 + kDqBK - 1 >= wk_lo;
+  };
+
+  uint32_t kpre[KPER], vpre[VPER];
+#pragma unroll
+  for (int i = 0; i < KPER; ++i) kpre[i] = block_src<D>(w + i * NW, lane, KP);
+#pragma unroll
+  for (int i = 0; i < VPER; ++i) vpre[i] = block_src<D>(w + i * NW, lane, VP);
+  auto kstage = [&] __device__ (auto st) -> char* {
+    constexpr int S = decltype(st)::value;
+    return S == 0 ? K0 : S == 1 ? K1 : K2;
+  };
+  auto vstage = [&] __device__ (auto st) -> char* {
+    constexpr int S = decltype(st)::value;
+    return S == 0 ? V0 : S == 1 ? V1 : V2;
+  };
+  auto load_share = [&] __device__ (int tile, auto st) {
+    const int k0 = tile * kDqBK;
+    const uint32_t bytes = (uint32_t)max(0, N - k0) * D * 2u;
+    const rsrc_t ks = make_rsrc(k + base + (size_t)k0 * D, bytes);
+    const rsrc_t vs = make_rsrc(v + base + (size_t)k0 * D, bytes);
+    char* kd = kstage(st);
+    char* vd = vstage(st);
+#pragma unroll
+    for (int i = 0; i < KPER; ++i)
+      if (w + i * NW < TL::kKBlocks) load_lds16(ks, kd + (w + i * NW) * 1024, kpre[i]);
+#pragma unroll
+    for (int i = 0; i < VPER; ++i)
+      if (w + i * NW < TL::kVBlocks) load_lds16(vs, vd + (w + i * NW) * 1024, vpre[i]);
+  };
+
+  const int k_rd = l32 * KP + 16 * h;  // A operands of S^T (K rows)
+  const int v_rd = l32 * VP + 16 * h;  // A operands of dP^T (V rows)
+  const int k_tr = tr_addr<KP>(lane);  // A operands of dQ^T (K^T)
+
+  f32x16 dqa[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) dqa[cb] = f32x16{};
+  f32x16 sc[2], dpc[2];  // S^T and dP^T of the tile in flight
+
+  // S^T and dP^T of a tile (stage `st`) for its two 32-key blocks.
+  auto scores = [&] __device__ (auto st) {
+    const char* kn = kstage(st) + k_rd;
+    const char* vn = vstage(st) + v_rd;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      sc[kb2] = f32x16{};
+      dpc[kb2] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        sc[kb2] = mfma32(*(const bf16x8*)(kn + kb2 * 32 * KP + 32 * s), qf[s], sc[kb2]);
+        dpc[kb2] = mfma32(*(const bf16x8*)(vn + kb2 * 32 * VP + 32 * s), of[s], dpc[kb2]);
+      }
+    }
+  };
+
+  using std::integral_constant;
+  load_share(kt0, integral_constant<int, 0>{});
+  if (kt0 + 1 < kt1) load_share(kt0 + 1, integral_constant<int, 1>{});
+  wait_vm(0);
+  barrier_keep_loads();
+  if (active(kt0)) scores(integral_constant<int, 0>{});
+  if (grp == 1) barrier_keep_loads();  // group 1 runs one phase behind
+
+  // Tile kt in stage ST: vector phase (P, dS of tile kt), barrier, matrix
+  // phase (dQ of tile kt, S and dP of tile kt+1), barrier.
+  auto tile_step = [&] __device__ (auto stage, int kt) {
+    constexpr int ST = decltype(stage)::value;
+    constexpr int STN = (ST + 1) % 3, STF = (ST + 2) % 3;
+    const bool load_far = kt + 2 < kt1;
+    // ---- vector phase (group 1 also issues its loads of tile kt+2 here)
+    if (grp == 1 && load_far) load_share(kt + 2, integral_constant<int, STF>{});
+    const bool act = active(kt), act_next = kt + 1 < kt1 && active(kt + 1);
+    uint32_t dspk[2][8];
+    if (act) {
+      const int k0 = kt * kDqBK;
+      // (P^T overwrites S^T in place.)
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          sc[kb2][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb2][r], scale_log2, -Li));
+      const bool need_mask = (k0 + kDqBK > N) || (causal && k0 + kDqBK - 1 > wq0) ||
+                             (window >= 0 && k0 < wq1 - window);
+      if (need_mask) {
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kb2 * 32 + c_row(r, h);
+            sc[kb2][r] = (uint32_t)(key - key_lo) <= (uint32_t)(key_hi - key_lo) ? sc[kb2][r] : 0.f;
+          }
+      }
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2)
+          dspk[kb2][r >> 1] = pack_bf16(sc[kb2][r] * (dpc[kb2][r] - Di),
+                                        sc[kb2][r + 1] * (dpc[kb2][r + 1] - Di));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dspk[i][j] = 0u;
+    }
+    pin_dq_phase<CB>(dspk, dqa);
+    // Group 0's matrix phase (after this barrier) needs tile kt+1 whole;
+    // group 1 waits for its loads at the end of its matrix phase instead.
+    if (grp == 0) wait_vm(0);
+    barrier_keep_loads();
+    // ---- matrix phase (group 0 issues its loads of tile kt+2 here)
+    if (grp == 0 && load_far) load_share(kt + 2, integral_constant<int, STF>{});
+    if (act) {
+      const char* kc = kstage(integral_constant<int, ST>{}) + k_tr;
+#pragma unroll
+      for (int s = 0; s < kDqBK / 16; ++s) {
+        const uint4 dw = {dspk[s >> 1][4 * (s & 1)], dspk[s >> 1][4 * (s & 1) + 1],
+                          dspk[s >> 1][4 * (s & 1) + 2], dspk[s >> 1][4 * (s & 1) + 3]};
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          dqa[cb] = mfma32(read_tr8<KP>(kc + 16 * s * KP + 64 * cb), as_bf16x8(dw), dqa[cb]);
+      }
+    }
+    if (act_next) scores(integral_constant<int, STN>{});
+    if (grp == 1) wait_vm(0);
+    barrier_keep_loads();
+  };
+
+  for (int kt = kt0; kt < kt1; kt += 3) {
+    tile_step(integral_constant<int, 0>{}, kt);
+    if (kt + 1 >= kt1) break;
+    tile_step(integral_constant<int, 1>{}, kt + 1);
+    if (kt + 2 >= kt1) break;
+    tile_step(integral_constant<int, 2>{}, kt + 2);
+  }
+  if (grp == 0) barrier_keep_loads();  // match group 1's extra barrier
+
+  if (row_ok) {
+    float* drow = dq + base + (size_t)qi * D;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *(float4*)(drow + 32 * cb + 8 * g + 4 * h) =
+            float4{scale * dqa[cb][4 * g], scale * dqa[cb][4 * g + 1], scale * dqa[cb][4 * g + 2],
+                   scale * dqa[cb][4 * g + 3]};
+  }
+}
+
 template <int D>
 hipError_t launch_t(const void* q, const void* k, const void* v, const void* o, const void* dO,
                     const float* lse, float* dq, float* dk, float* dv, int B, int H, int N,
@@ -544,11 +801,20 @@ hipError_t launch_t(const void* q, const void* k, const void* v, const void* o, 
                      B * H, N, nkt, scale, scale * kLog2e, mask.causal, mask.window);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  constexpr int BQ = kDqThreads / 2;  // 32 query rows per wave
-  const int nqt = (N + BQ - 1) / BQ;
-  hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)((long long)nqt * B * H)), dim3(kDqThreads), 0,
-                     stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dO, Dv, L2,
-                     dq, B * H, N, nqt, scale, scale * kLog2e, mask.causal, mask.window);
+  // dQ: the ping-pong kernel (256 query rows per workgroup) when its grid
+  // still fills the chip, else the 4-wave kernel (128 rows).
+  if ((long long)B * H * ((N + 255) / 256) >= 256) {
+    const int nqt = (N + 255) / 256;
+    hipLaunchKernelGGL((bwd_dq_pp_kernel<D>), dim3((unsigned)((long long)nqt * B * H)), dim3(kDqPPThreads),
+                       0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dO, Dv,
+                       L2, dq, B * H, N, nqt, scale, scale * kLog2e, mask.causal, mask.window);
+  } else {
+    constexpr int BQ = kDqThreads / 2;  // 32 query rows per wave
+    const int nqt = (N + BQ - 1) / BQ;
+    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)((long long)nqt * B * H)), dim3(kDqThreads), 0,
+                       stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dO, Dv, L2,
+                       dq, B * H, N, nqt, scale, scale * kLog2e, mask.causal, mask.window);
+  }
   return hipGetLastError();
 }
 

@@ -242,4 +242,15 @@ __device__ __forceinline__ void barrier_after_lds_writes() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Ping-pong group of the calling wave: the order in which waves arrive on
+// their SIMD (HW_ID bits 5:4), modulo 2, so that each SIMD hosts one wave of
+// each group when the workgroup's waves are spread evenly.  `slots` is a
+// zeroed per-SIMD counter in LDS.
+__device__ __forceinline__ int wave_group(int* slots, int lane) {
+  const int simd = __builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4) & 3;
+  int slot = 0;
+  if (lane == 0) slot = atomicAdd(&slots[simd], 1);
+  return __builtin_amdgcn_readfirstlane(slot) & 1;
+}
+
 }  // namespace fa

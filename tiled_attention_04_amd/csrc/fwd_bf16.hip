@@ -463,16 +463,6 @@ __device__ __forceinline__ void pin_softmax_results(uint32_t (&pk)[2][8], f32x16
 #endif
 constexpr int kPingPongStages = FA_PINGPONG_STAGES;
 
-// Ping-pong group of the calling wave: the order in which waves arrive on
-// their SIMD (HW_ID bits 5:4), modulo 2, so that each SIMD hosts one wave of
-// each group when the workgroup's waves are spread evenly.  `slots` is a
-// zeroed per-SIMD counter in LDS.
-__device__ __forceinline__ int wave_group(int* slots, int lane) {
-  const int simd = __builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4) & 3;
-  int slot = 0;
-  if (lane == 0) slot = atomicAdd(&slots[simd], 1);
-  return __builtin_amdgcn_readfirstlane(slot) & 1;
-}
 
 template <int D>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
