@@ -6,6 +6,7 @@ batch (already resident in HBM when timing starts):
   2. sliding-window forward,    same tensors, window 1024 (causal band)
   3. KV-cache decode,           64 sequences x 32 heads, d=128, lengths U[512, 8192]
   4. causal backward,           B=2, H=16, N=4096, d=128, bf16 (from the forward's O and L)
+  5. paged KV-cache decode,     the decode batch of 3 in 64-token pages scattered over a pool
 
 The headline value is the causal forward's TFLOP/s (4*B*H*N^2*d/2 algorithmic
 flops per launch over its measured time); every stage is timed with HIP events
@@ -96,7 +97,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--stages", default="fwd,window,decode,bwd")
+    ap.add_argument("--stages", default="fwd,window,decode,bwd,paged")
+    ap.add_argument("--page-size", type=int, default=64)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, copy 1 GiB device-to-device three times: the reference "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters")
@@ -109,7 +111,8 @@ def main():
     import torch
 
     import tiled_attention_04_amd as fa
-    from tiled_attention_04_amd.inputs import WORKLOADS, attention_inputs, decode_inputs, dense_cache
+    from tiled_attention_04_amd.inputs import (WORKLOADS, attention_inputs, decode_inputs, dense_cache,
+                                              paged_cache)
 
     stages = args.stages.split(",")
     dev = torch.device("cuda:0")
@@ -128,17 +131,26 @@ def main():
     l3w = torch.empty_like(l3)
 
     w4 = WORKLOADS["decode_s64_h32_d128_len512to8192_bf16"]
-    if "decode" in stages:
+    if "decode" in stages or "paged" in stages:
         log("generating decode inputs (ragged KV cache)")
         inp4 = decode_inputs(w4["S"], w4["H"], w4["d"], w4["len_lo"], w4["len_hi"], seed=0)
-        kc4, vc4 = dense_cache(inp4, w4["Lmax"], device=dev)
         q4 = inp4.q.to(dev)
         sl4 = torch.from_numpy(inp4.seqlens).to(dev)
         o4 = torch.empty_like(q4)
         l4 = torch.empty(q4.shape[:2], dtype=torch.float32, device=dev)
+        dec_bytes = inp4.valid_bytes(2) + 2 * q4.numel() * 2
+    if "decode" in stages:
+        kc4, vc4 = dense_cache(inp4, w4["Lmax"], device=dev)
         ws4 = torch.empty(fa.fa_decode_workspace_size(w4["S"], w4["H"], w4["Lmax"], w4["d"]),
                           dtype=torch.uint8, device=dev)
-        dec_bytes = inp4.valid_bytes(2) + 2 * q4.numel() * 2
+    if "paged" in stages:
+        log(f"paging the decode cache ({args.page_size}-token pages)")
+        kp6, vp6, tb6 = paged_cache(inp4, args.page_size, device=dev, seed=0)
+        o6 = torch.empty_like(q4)
+        l6 = torch.empty_like(l4)
+        ws6 = torch.empty(fa.fa_decode_workspace_size(w4["S"], w4["H"], tb6.shape[1] * args.page_size,
+                                                      w4["d"]), dtype=torch.uint8, device=dev)
+    if "decode" in stages or "paged" in stages:
         del inp4
 
     w5 = WORKLOADS["bwd_b2_h16_n4096_d128_bf16"]
@@ -172,6 +184,9 @@ def main():
         if "bwd" in stages:
             fa.fa_bwd(q5, k5, v5, o5, g5, l5, causal=True, dq=dq5, dk=dk5, dv=dv5, workspace=ws5)
         mark(4)
+        if "paged" in stages:
+            fa.fa_decode_paged(q4, kp6, vp6, tb6, sl4, o=o6, lse=l6, workspace=ws6)
+        mark(5)
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -179,17 +194,17 @@ def main():
     torch.cuda.synchronize()
 
     log(f"timing {args.steps} steps")
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    comp = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(4)]
+    comp = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(5)]
                      for i in range(args.steps)])  # ms
     ms = comp.mean(axis=0)
-    log("stage ms (mean): " + ", ".join(f"{n}={m:.4f}" for n, m in zip(("fwd", "window", "decode", "bwd"), ms)))
+    log("stage ms (mean): " + ", ".join(f"{n}={m:.4f}" for n, m in zip(("fwd", "window", "decode", "bwd", "paged"), ms)))
 
     components = {}
 
@@ -213,6 +228,13 @@ def main():
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode")}}
     if "bwd" in stages:
         mfma_stage("bwd_causal_b2_h16_n4096_d128", flops5, ms[3], "bwd_bf16")
+    if "paged" in stages:
+        gbs = dec_bytes / (ms[4] * 1e-3) / 1e9
+        components[f"decode_paged{args.page_size}_s64_h32_d128_len512to8192"] = {
+            "ms": round(ms[4], 5), "GB/s": round(gbs, 1), "algorithmic_gb": round(dec_bytes / 1e9, 4),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic(f"decode_paged{args.page_size}")}}
 
     if args.copy_calibration:
         log("copy calibration: 3 x 1 GiB device-to-device")
@@ -233,8 +255,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded N(0,1), rounded to bf16)",
         "config": {"workload": "causal forward B=4 H=32 N=4096 d=128 bf16 (step also runs: window-1024 "
-                               "forward, 64x32 ragged decode d=128 lengths U[512,8192], causal backward "
-                               "B=2 H=16 N=4096 d=128)",
+                               "forward, 64x32 ragged decode d=128 lengths U[512,8192] from a dense and "
+                               "from a 64-token paged cache, causal backward B=2 H=16 N=4096 d=128)",
                    "global_batch": B3, "seq_len": N3, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(value, 3) if value is not None else None,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

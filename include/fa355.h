@@ -135,6 +135,41 @@ fa_status fa_decode(const void* q, const void* kcache, const void* vcache,
                     void* workspace, size_t workspace_bytes, fa_dtype dtype, void* stream);
 
 /*
+ * fa_decode_paged -- fa_decode over a paged KV cache.
+ *
+ * The cache of "Build a FlashAttention Kernel with Online Softmax and KV
+ * Cache in Pure Python", Step 2, grows token by token; here its rows live in
+ * fixed-size pages drawn from a shared pool and found through a per-sequence
+ * page table -- the paged KV cache listed as the first upgrade in "Build a
+ * FlashAttention-2 Inference Kernel from Scratch in Pure Python", Extending
+ * It -- so no sequence reserves Lmax rows.  The result is exactly fa_decode's
+ * on the logical cache the table describes.
+ *
+ *   q, o, lse, seqlens, window, chunk : as in fa_decode
+ *   k_pages     : [num_pages, H, page_size, d] key pool, dtype
+ *   v_pages     : [num_pages, H, page_size, d] value pool, dtype
+ *   block_table : [S, max_pages] int32 device array: logical token t of
+ *                 sequence s is row t % page_size of page
+ *                 block_table[s * max_pages + t / page_size].  Only the
+ *                 entries covering tokens 0..seqlens[s]-1 are read.  An entry
+ *                 outside [0, num_pages) hides the tokens it would hold
+ *                 (used for pages evicted from a sliding window); nothing
+ *                 outside the pool is ever read.
+ *   page_size   : a positive multiple of 64 tokens
+ *   max_pages   : table columns; seqlens[s] is clamped to
+ *                 [1, max_pages * page_size]
+ *   workspace   : >= fa_decode_workspace_size(S, H, max_pages * page_size,
+ *                 d, chunk) bytes
+ *
+ * Supported: FA_BF16 and FA_FP32 with d in {64, 128}.
+ */
+fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                          const int32_t* block_table, const int32_t* seqlens, void* o, float* lse,
+                          int S, int H, int d, int num_pages, int page_size, int max_pages,
+                          float scale, int window, int chunk,
+                          void* workspace, size_t workspace_bytes, fa_dtype dtype, void* stream);
+
+/*
  * fa_bwd_workspace_size -- bytes of workspace fa_bwd needs (0 if invalid).
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);

@@ -17,6 +17,8 @@ Sources (web pages; cited by title and section):
 * "Build a FlashAttention Kernel with Online Softmax and KV Cache in Pure
   Python" (martinuke0.github.io, 2026-11-01) -- Steps 4-5 (single-token
   decode over a cache, naive reference).
+* "Build a FlashAttention-2 Inference Kernel from Scratch in Pure Python",
+  Extending It -- the paged KV cache (``decode_paged_ref``).
 * "FlashAttention Algorithm > Worked Example" (mbrenndoerfer.com) -- Setup and
   Steps 1-3 (n=8, d=4, block 4 trace).
 
@@ -32,5 +34,6 @@ from .attention import (  # noqa: F401
     attention_probs_ref,
     attention_tiled_ref,
     decode_ref,
+    decode_paged_ref,
     attention_bwd_ref,
 )

@@ -203,6 +203,61 @@ def decode_ref(q, kcache, vcache, seqlens, scale: float, window: int = -1):
     return o, lse
 
 
+def _gather(pool, pages, h: int, rows) -> np.ndarray:
+    """Rows pool[pages[i], h, rows[i]] as float64 (numpy array or torch tensor)."""
+    if hasattr(pool, "detach"):
+        import torch
+        pages, rows = torch.as_tensor(pages), torch.as_tensor(rows)
+    return _f64(pool[pages, h, rows])
+
+
+def _page_rows(table_row, n: int, P: int, num_pages: int):
+    """Where tokens 0..n-1 of one sequence live: (page, row in page, present)."""
+    t = np.arange(n)
+    page = np.asarray(table_row, dtype=np.int64)[t // P]
+    return page, t % P, (page >= 0) & (page < num_pages)
+
+
+def decode_paged_ref(q, k_pages, v_pages, block_table, seqlens, scale: float, window: int = -1):
+    """Single-token decode whose cache rows are held in pages.
+
+    The logical cache is the one of the KV-cache page, Step 2 (one key and one
+    value row per token, in token order); the rows are stored in fixed-size
+    pages of a shared pool, as in the paged KV cache named among the upgrades
+    of the FlashAttention-2 inference page (Extending It).  Token t of
+    sequence s is row t % P of page block_table[s, t // P], P the page size.
+    A table entry outside [0, num_pages) marks its tokens as absent: they take
+    no part in the softmax (a page dropped from a sliding window).  The
+    result is then decode_ref's on that logical cache: the query sits at
+    position seqlens[s]-1 and, with a window W, sees positions >= seqlens[s]-1-W.
+
+    q: [S, H, d]; k_pages, v_pages: [num_pages, H, P, d]; block_table:
+    [S, max_pages] ints; seqlens: [S] ints >= 1.  Returns (o [S, H, d],
+    lse [S, H]).
+    """
+    Sq, H, d = q.shape
+    num_pages, _, P, _ = k_pages.shape
+    table = np.asarray(block_table, dtype=np.int64)
+    seqlens = np.asarray(seqlens, dtype=np.int64)
+    o = np.empty((Sq, H, v_pages.shape[-1]))
+    lse = np.empty((Sq, H))
+    for s in range(Sq):
+        n = int(seqlens[s])
+        page, row, present = _page_rows(table[s], n, P, num_pages)
+        at = np.nonzero(present)[0]
+        for h in range(H):
+            K = np.zeros((n, k_pages.shape[-1]))
+            V = np.zeros((n, v_pages.shape[-1]))
+            K[at] = _gather(k_pages, page[at], h, row[at])
+            V[at] = _gather(v_pages, page[at], h, row[at])
+            S_row = (K @ _f64(q[s, h])) * scale
+            ok = allowed_mask([n - 1], n, False, window) & present[None, :]
+            P_row, L_row = _softmax_rows(S_row[None, :], ok)
+            o[s, h] = (P_row @ V)[0]
+            lse[s, h] = L_row[0]
+    return o, lse
+
+
 def attention_bwd_ref(q, k, v, dO, scale: float, causal: bool = False, window: int = -1):
     """Exact gradients of O = attention(Q, K, V) with respect to Q, K and V.
 

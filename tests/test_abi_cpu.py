@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_header_declares_the_expected_calls():
     names = declared_functions()
-    for must in ("fa_fwd", "fa_fwd_ex", "fa_decode", "fa_bwd", "fa_decode_workspace_size",
+    for must in ("fa_fwd", "fa_fwd_ex", "fa_decode", "fa_decode_paged", "fa_bwd", "fa_decode_workspace_size",
                  "fa_bwd_workspace_size", "fa_status_str", "fa_last_error", "fa_version"):
         assert must in names
 
@@ -87,6 +87,34 @@ def test_decode_rejects_bad_arguments(lib):
     assert call(d=96) == 2
     assert call(ws=None) == 3
     assert call(wsb=16) == 3
+    assert "workspace" in fa355.last_error()
+
+
+def test_decode_paged_rejects_bad_arguments(lib):
+    def call(**kw):
+        a = dict(q=FAKE, kp=FAKE, vp=FAKE, tb=FAKE, sl=FAKE, o=FAKE, S=2, H=2, d=128, num_pages=8,
+                 page=64, max_pages=4, scale=0.1, window=-1, chunk=0, ws=FAKE, wsb=1 << 30, dtype=1)
+        a.update(kw)
+        return lib.fa_decode_paged(a["q"], a["kp"], a["vp"], a["tb"], a["sl"], a["o"], None, a["S"],
+                                   a["H"], a["d"], a["num_pages"], a["page"], a["max_pages"],
+                                   a["scale"], a["window"], a["chunk"], a["ws"], a["wsb"], a["dtype"],
+                                   None)
+    assert call(tb=None) == 1
+    assert call(kp=None) == 1
+    assert call(num_pages=0) == 1
+    assert call(max_pages=0) == 1
+    assert call(page=0) == 1
+    assert call(page=32) == 1
+    assert call(page=100) == 1
+    assert call(page=1 << 20, max_pages=1 << 12) == 1
+    assert call(chunk=96) == 1
+    assert call(window=-2) == 1
+    assert call(scale=float("nan")) == 1
+    assert call(dtype=5) == 1
+    assert call(d=80) == 2
+    assert call(ws=None) == 3
+    need = fa355.fa_decode_workspace_size(2, 2, 4 * 64, 128, 0)
+    assert call(wsb=need - 1) == 3
     assert "workspace" in fa355.last_error()
 
 

@@ -9,7 +9,8 @@ import torch
 import oracle
 import tiled_attention_04_amd as fa
 from parity import check_bf16, check_fp32, check_lse, need_gpu
-from tiled_attention_04_amd.inputs import WORKLOADS, attention_inputs, decode_inputs, dense_cache
+from tiled_attention_04_amd.inputs import (WORKLOADS, attention_inputs, decode_inputs, dense_cache,
+                                          paged_cache)
 
 pytestmark = pytest.mark.gpu
 
@@ -99,3 +100,86 @@ def test_full_size_ragged_decode():
     O, L = oracle_decode(inp)
     check_bf16(o, O, "o")
     check_lse(lse, L, "lse")
+
+
+# ------------------------------------------------------------ paged cache --
+
+def run_paged(inp, page_size, window=-1, chunk=0, scale=None, spare=2, seed=0, hide=()):
+    kp, vp, table = paged_cache(inp, page_size, device="cuda", seed=seed, spare_pages=spare)
+    for s, j, val in hide:  # table entries outside the pool hide their tokens
+        table[s, j] = val
+    sl = torch.from_numpy(inp.seqlens).cuda()
+    o, lse = fa.fa_decode_paged(inp.q.cuda(), kp, vp, table, sl, window=window, chunk=chunk,
+                                scale=scale)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu(), (kp.cpu(), vp.cpu(), table.cpu().numpy())
+
+
+def oracle_paged(inp, pool, window=-1, scale=None):
+    kp, vp, table = pool
+    d = inp.q.shape[2]
+    s = 1 / math.sqrt(d) if scale is None else scale
+    return oracle.decode_paged_ref(inp.q, kp, vp, table, inp.seqlens, s, window)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("page_size,chunk", [(64, 0), (64, 192), (128, 64), (192, 320)])
+@pytest.mark.parametrize("window", [-1, 0, 70])
+def test_paged_small_ragged_batch(d, dtype, page_size, chunk, window):
+    lens = [1, 2, 63, 64, 65, 300, 129, 500]
+    inp = decode_inputs(len(lens), 3, d, 1, 500, dtype=dtype, seed=d + page_size, seqlens=lens)
+    o, lse, pool = run_paged(inp, page_size, window, chunk, seed=chunk)
+    O, L = oracle_paged(inp, pool, window)
+    if dtype == "fp32":
+        check_fp32(o, O, "o")
+        check_fp32(lse, L, "lse")
+    else:
+        check_bf16(o, O, "o")
+        check_lse(lse, L, "lse")
+
+
+def test_paged_equals_dense_decode():
+    lens = [700, 1, 1024, 513, 64, 65]
+    inp = decode_inputs(len(lens), 4, 128, 1, 1024, seed=5, seqlens=lens)
+    o_p, l_p, _ = run_paged(inp, 64, chunk=256)
+    o_d, l_d = run(inp, 1024, -1, 256)
+    check_bf16(o_p, o_d, "paged vs dense o")
+    check_lse(l_p, l_d, "paged vs dense lse")
+
+
+def test_paged_hidden_table_entries_drop_their_tokens():
+    """Entries -1 and >= num_pages hide whole pages (never read)."""
+    lens = [300, 260, 129]
+    inp = decode_inputs(len(lens), 2, 128, 1, 300, seed=6, seqlens=lens)
+    hide = [(0, 0, -1), (0, 2, 1 << 30), (1, 1, -5)]
+    o, lse, pool = run_paged(inp, 64, hide=hide)
+    O, L = oracle_paged(inp, pool)
+    check_bf16(o, O, "o")
+    check_lse(lse, L, "lse")
+
+
+def test_paged_sequence_with_every_page_hidden():
+    lens = [100, 150]
+    inp = decode_inputs(len(lens), 2, 64, 1, 150, seed=7, seqlens=lens)
+    o, lse, pool = run_paged(inp, 64, hide=[(0, 0, -1), (0, 1, -1)])
+    O, L = oracle_paged(inp, pool)
+    assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    check_bf16(o[1], O[1], "o")
+    check_lse(lse[1], L[1], "lse")
+
+
+@pytest.mark.slow
+def test_full_size_ragged_paged_decode():
+    """The ragged decode batch (64 x 32, d=128, lengths U[512, 8192]) in
+    64-token pages: sampled (sequence, head) pairs against the oracle."""
+    w = WORKLOADS["decode_s64_h32_d128_len512to8192_bf16"]
+    inp = decode_inputs(w["S"], w["H"], w["d"], w["len_lo"], w["len_hi"], seed=0)
+    o, lse, pool = run_paged(inp, 64)
+    kp, vp, table = pool
+    rng = np.random.default_rng(1)
+    for s in rng.choice(w["S"], 8, replace=False):
+        O, L = oracle.decode_paged_ref(inp.q[s:s + 1], kp, vp, table[s:s + 1], inp.seqlens[s:s + 1],
+                                       1 / math.sqrt(w["d"]))
+        check_bf16(o[s], O[0], f"o[{s}]")
+        check_lse(lse[s], L[0], f"lse[{s}]")

@@ -458,3 +458,107 @@ def test_planted_missing_rescale_fails_trace_pin(monkeypatch):
 
     with pytest.raises(AssertionError):
         _close(run(), exp["l_block1"][0], exp["l_block1"][1], "final running sum")
+
+
+# --------------------------------------------------------------------------
+# Paged KV cache (FlashAttention-2 inference page, Extending It): the pages
+# hold the KV-cache page's logical cache, token t at row t % P of page
+# table[t // P]
+# --------------------------------------------------------------------------
+
+def _paged_pool(lens, H, d, P, rng, hide=()):
+    """A pool whose row for token t of sequence s, head h holds
+    V = [t, t^2 / 100, s, h, 0, ...] (and random K); stale rows are NaN; the table
+    maps each sequence's page slots to a random permutation of the pool.
+    Slots listed in ``hide`` as (s, slot) get table entries outside the pool."""
+    slots = [-(-n // P) for n in lens]
+    num_pages = sum(slots) + 3  # 3 pages belong to nobody
+    perm = rng.permutation(num_pages)
+    max_pages = max(slots) + 1
+    table = np.full((len(lens), max_pages), -7, dtype=np.int64)
+    kp = np.full((num_pages, H, P, d), np.nan)
+    vp = np.full((num_pages, H, P, d), np.nan)
+    nxt = 0
+    for s, n in enumerate(lens):
+        for j in range(slots[s]):
+            p = perm[nxt]
+            nxt += 1
+            table[s, j] = p if (s, j) not in hide else (num_pages if j % 2 else -1)
+            for r in range(P):
+                t = j * P + r
+                if t < n:
+                    kp[p, :, r] = rng.standard_normal((H, d))
+                    for h in range(H):
+                        vp[p, h, r] = 0.0
+                        vp[p, h, r, :4] = [t, t * t / 100.0, s, h]
+    return kp, vp, table
+
+
+def _visible_mean(positions, s, h):
+    t = np.asarray(positions, dtype=np.float64)
+    return np.array([t.mean(), (t * t / 100.0).mean(), s, h])
+
+
+@pytest.mark.parametrize("window", [-1, 0, 5])
+def test_paged_decode_scale_zero_closed_form(window):
+    """scale = 0: the output is the mean of V over the visible positions, which
+    identifies those positions; L = ln(count)."""
+    rng = np.random.default_rng(21)
+    lens, H, d, P = [1, 4, 5, 11, 16], 2, 4, 4
+    kp, vp, table = _paged_pool(lens, H, d, P, rng)
+    q = rng.standard_normal((len(lens), H, d))
+    o, lse = oracle.decode_paged_ref(q, kp, vp, table, lens, 0.0, window)
+    for s, n in enumerate(lens):
+        lo = 0 if window < 0 else max(0, n - 1 - window)
+        for h in range(H):
+            _close(o[s, h], _visible_mean(range(lo, n), s, h), 1e-12, f"o[{s},{h}]")
+            _close(lse[s, h], math.log(n - lo), 1e-14, f"lse[{s},{h}]")
+
+
+def test_paged_decode_hidden_pages_drop_their_tokens():
+    rng = np.random.default_rng(22)
+    lens, H, d, P = [9, 12], 1, 4, 4
+    kp, vp, table = _paged_pool(lens, H, d, P, rng, hide={(0, 0), (1, 1)})
+    q = rng.standard_normal((2, H, d))
+    o, lse = oracle.decode_paged_ref(q, kp, vp, table, lens, 0.0)
+    _close(o[0, 0], _visible_mean(range(4, 9), 0, 0), 1e-12, "seq 0 without its first page")
+    _close(o[1, 0], _visible_mean(list(range(0, 4)) + list(range(8, 12)), 1, 0), 1e-12,
+           "seq 1 without its second page")
+    _close(lse[:, 0], np.log([5, 8]), 1e-14, "lse")
+
+
+@pytest.mark.parametrize("window", [-1, 3])
+def test_paged_decode_equals_dense_decode_on_the_logical_cache(window):
+    rng = np.random.default_rng(23)
+    lens, H, d, P = [1, 7, 8, 13], 3, 8, 4
+    kp, vp, table = _paged_pool(lens, H, d, P, rng)
+    vp = np.where(np.isnan(vp), np.nan, rng.standard_normal(vp.shape))  # V random as well
+    q = rng.standard_normal((len(lens), H, d))
+    Lmax = max(lens)
+    kc = np.full((len(lens), H, Lmax, d), np.nan)
+    vc = np.full((len(lens), H, Lmax, d), np.nan)
+    for s, n in enumerate(lens):  # unpage token by token, slot by slot
+        for j in range(-(-n // P)):
+            rows = min(P, n - j * P)
+            kc[s, :, j * P:j * P + rows] = kp[table[s, j], :, :rows]
+            vc[s, :, j * P:j * P + rows] = vp[table[s, j], :, :rows]
+    o1, l1 = oracle.decode_paged_ref(q, kp, vp, table, lens, 0.4, window)
+    o2, l2 = oracle.decode_ref(q, kc, vc, lens, 0.4, window)
+    _close(o1, o2, 1e-14, "o")
+    _close(l1, l2, 1e-14, "lse")
+
+
+@pytest.mark.parametrize("mistake", ["row_from_slot", "page_from_row"])
+def test_planted_page_mapping_mistakes_are_caught(monkeypatch, mistake):
+    def wrong(table_row, n, P, num_pages):
+        t = np.arange(n)
+        tr = np.asarray(table_row, dtype=np.int64)
+        if mistake == "row_from_slot":
+            page, row = tr[t // P], (t // P) % P
+        else:
+            page, row = tr[np.minimum(t % P, len(tr) - 1)], t % P
+        return page, row, (page >= 0) & (page < num_pages)
+
+    monkeypatch.setattr(oa, "_page_rows", wrong)
+    with pytest.raises(AssertionError):
+        test_paged_decode_scale_zero_closed_form(-1)

@@ -13,6 +13,7 @@ from .fa355 import (  # noqa: F401
     fa_bwd,
     fa_bwd_workspace_size,
     fa_decode,
+    fa_decode_paged,
     fa_decode_workspace_size,
     fa_fwd,
     fa_fwd_ex,

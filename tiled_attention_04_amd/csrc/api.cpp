@@ -152,6 +152,41 @@ fa_status fa_decode(const void* q, const void* kcache, const void* vcache, const
               "fa_decode");
 }
 
+fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                          const int32_t* block_table, const int32_t* seqlens, void* o, float* lse,
+                          int S, int H, int d, int num_pages, int page_size, int max_pages,
+                          float scale, int window, int chunk, void* workspace,
+                          size_t workspace_bytes, fa_dtype dtype, void* stream) {
+  if (!q || !k_pages || !v_pages || !block_table || !seqlens || !o)
+    return fail(FA_ERR_INVALID_ARG, "q, k_pages, v_pages, block_table, seqlens and o must be non-null");
+  if (S <= 0 || H <= 0 || d <= 0 || num_pages <= 0 || max_pages <= 0)
+    return fail(FA_ERR_INVALID_ARG, "sizes must be positive (S=%d H=%d d=%d num_pages=%d max_pages=%d)",
+                S, H, d, num_pages, max_pages);
+  if (page_size <= 0 || page_size % 64 != 0)
+    return fail(FA_ERR_INVALID_ARG, "page_size must be a positive multiple of 64 (got %d)", page_size);
+  if ((long long)S * H > INT_MAX) return fail(FA_ERR_INVALID_ARG, "S*H exceeds 2^31-1");
+  if ((long long)max_pages * page_size > INT_MAX)
+    return fail(FA_ERR_INVALID_ARG, "max_pages * page_size exceeds 2^31-1");
+  if (window < -1) return fail(FA_ERR_INVALID_ARG, "window must be -1 (off) or >= 0 (got %d)", window);
+  if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite");
+  if (chunk < 0 || chunk % 64 != 0)
+    return fail(FA_ERR_INVALID_ARG, "chunk must be 0 (auto) or a positive multiple of 64 (got %d)", chunk);
+  if (!valid_dtype(dtype)) return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "decode supports d in {64, 128} (got %d)", d);
+  const int Lmax = max_pages * page_size;
+  if (chunk == 0) chunk = fa::decode_auto_chunk(S, H, Lmax);
+  const long long nchunk = (Lmax + chunk - 1) / chunk;
+  if (nchunk * S * H * 256 > kMaxThreadsPerLaunch) return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  const size_t need = fa::decode_workspace_bytes(S, H, Lmax, d, chunk);
+  if (!workspace || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "paged decode needs %zu workspace bytes (got %zu%s)", need,
+                workspace_bytes, workspace ? "" : ", null pointer");
+  return done(fa::launch_decode_paged(q, k_pages, v_pages, block_table, seqlens, o, lse, S, H, d,
+                                      num_pages, page_size, max_pages, scale, window, chunk, workspace,
+                                      dtype == FA_BF16, (hipStream_t)stream),
+              "fa_decode_paged");
+}
+
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
   if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 0;
   return fa::bwd_workspace_bytes(B, H, N, d);

@@ -54,15 +54,25 @@ __device__ __forceinline__ void widen<float>(const uint4& u, float (&x)[4]) {
 
 __device__ __forceinline__ void clamp_len(int& n, int Lmax) { n = n < 1 ? 1 : (n > Lmax ? Lmax : n); }
 
-template <typename T, int D>
+// Where the cache rows live.  Dense: [S][H][Lmax][D].  Paged: a pool of pages
+// [num_pages][H][page_size][D]; token t of sequence s is row t % page_size of
+// page table[s * max_pages + t / page_size].  A table entry outside
+// [0, num_pages) hides the tokens it would hold (they are never read).
+struct PagedCache {
+  const int32_t* table;  // null: dense cache
+  int page_size, max_pages, num_pages;
+};
+
+template <typename T, int D, bool PAGED>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
     const int32_t* __restrict__ seqlens, float* __restrict__ ws_o, float* __restrict__ ws_ml,
-    int S, int H, int Lmax, int nchunk, int chunk, float scale_log2, int window) {
+    int S, int H, int Lmax, int nchunk, int chunk, float scale_log2, int window, PagedCache pc) {
   constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte load
   constexpr int LPR = D / VEC;          // lanes per cache row
   constexpr int RPW = 64 / LPR;         // rows per wave instruction
   constexpr int GROUPS = kWaves * RPW;  // row groups in the workgroup
+  constexpr int ROWS = kUnroll * RPW;   // rows per loop trip (at most 64)
   __shared__ float red_o[GROUPS][D];
   __shared__ float red_m[GROUPS], red_l[GROUPS];
 
@@ -79,19 +89,25 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int g = lane / LPR, e = lane % LPR;
   const size_t sh = (size_t)s * H + h;
-  const size_t slice = sh * (size_t)Lmax * D;
-  const uint32_t valid_bytes = (uint32_t)n * D * (uint32_t)sizeof(T);
-  const rsrc_t k_src = make_rsrc(kc + slice, valid_bytes);
-  const rsrc_t v_src = make_rsrc(vc + slice, valid_bytes);
+  rsrc_t k_src, v_src;
+  if constexpr (!PAGED) {  // one buffer over the valid rows of the (sequence, head) slice
+    const size_t slice = sh * (size_t)Lmax * D;
+    const uint32_t valid_bytes = (uint32_t)n * D * (uint32_t)sizeof(T);
+    k_src = make_rsrc(kc + slice, valid_bytes);
+    v_src = make_rsrc(vc + slice, valid_bytes);
+  }
 
   float qv[VEC];
   widen<T>(*(const uint4*)(q + sh * D + e * VEC), qv);
 #pragma unroll
   for (int i = 0; i < VEC; ++i) qv[i] *= scale_log2;
 
-  // This wave's rows: a quarter of the split, clipped to [lo, n).
+  // This wave's rows: a quarter of the split, clipped to [lo, n).  With pages
+  // the loop trips start at multiples of ROWS (page sizes are multiples of
+  // 64), so every trip reads a single page; rows before r_lo are masked.
   const int per_wave = chunk / kWaves;
-  const int r_begin = max(lo, c_begin + w * per_wave);
+  const int r_lo = max(lo, c_begin + w * per_wave);
+  const int r_begin = PAGED ? (r_lo & ~(ROWS - 1)) : r_lo;
   const int r_end = min(n, c_begin + (w + 1) * per_wave);
 
   float m = kNegInf, l = 0.f;
@@ -99,11 +115,26 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
 #pragma unroll
   for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
 
-  for (int r0 = r_begin; r0 < r_end; r0 += kUnroll * RPW) {
+  for (int r0 = r_begin; r0 < r_end; r0 += ROWS) {
+    int row0 = r0;  // row of the trip's first row within its buffer
+    bool page_ok = true;
+    if constexpr (PAGED) {
+      // The buffer covers the page's valid rows only: rows at or past n read
+      // as zero (a stale row could hold NaN, and 0 * NaN is NaN).
+      const int slot = r0 / pc.page_size;
+      const int page = pc.table[(size_t)s * pc.max_pages + slot];
+      page_ok = (uint32_t)page < (uint32_t)pc.num_pages;
+      const int rows_here = min(pc.page_size, n - slot * pc.page_size);
+      const size_t pbase = ((size_t)(page_ok ? page : 0) * H + h) * (size_t)pc.page_size * D;
+      const uint32_t pbytes = page_ok ? (uint32_t)rows_here * D * (uint32_t)sizeof(T) : 0u;
+      k_src = make_rsrc(kc + pbase, pbytes);
+      v_src = make_rsrc(vc + pbase, pbytes);
+      row0 = r0 - slot * pc.page_size;
+    }
     uint4 kr[kUnroll], vr[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const uint32_t off = (uint32_t)((r0 + u * RPW + g) * D + e * VEC) * (uint32_t)sizeof(T);
+      const uint32_t off = (uint32_t)((row0 + u * RPW + g) * D + e * VEC) * (uint32_t)sizeof(T);
       kr[u] = load16(k_src, off);
       vr[u] = load16(v_src, off);
     }
@@ -118,7 +149,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
       for (int i = 0; i < VEC; ++i) p = __builtin_fmaf(qv[i], kx[i], p);
       p = group_sum<LPR>(p);
       const int row = r0 + u * RPW + g;
-      sc[u] = row < r_end ? p : kNegInf;
+      const bool in = PAGED ? (row >= r_lo) & (row < r_end) & page_ok : row < r_end;
+      sc[u] = in ? p : kNegInf;
       mx = fmaxf(mx, sc[u]);
     }
     const float m_new = fmaxf(m, mx);
@@ -205,14 +237,19 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(
 template <typename T, int D>
 hipError_t launch_t(const void* q, const void* kc, const void* vc, const int32_t* seqlens, void* o,
                     float* lse, int S, int H, int Lmax, float scale, int window, int chunk,
-                    void* ws, hipStream_t stream) {
+                    void* ws, PagedCache pc, hipStream_t stream) {
   const int nchunk = (Lmax + chunk - 1) / chunk;
   float* ws_o = (float*)ws;
   float* ws_ml = ws_o + (size_t)S * H * nchunk * D;
   const long long grid = (long long)nchunk * S * H;
-  hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                     (const T*)q, (const T*)kc, (const T*)vc, seqlens, ws_o, ws_ml, S, H, Lmax,
-                     nchunk, chunk, scale * kLog2e, window);
+  if (pc.table)
+    hipLaunchKernelGGL((decode_split_kernel<T, D, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                       (const T*)q, (const T*)kc, (const T*)vc, seqlens, ws_o, ws_ml, S, H, Lmax,
+                       nchunk, chunk, scale * kLog2e, window, pc);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<T, D, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                       (const T*)q, (const T*)kc, (const T*)vc, seqlens, ws_o, ws_ml, S, H, Lmax,
+                       nchunk, chunk, scale * kLog2e, window, pc);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)(S * H)), dim3(D), 0, stream,
@@ -237,17 +274,35 @@ size_t decode_workspace_bytes(int S, int H, int Lmax, int d, int chunk) {
   return (size_t)S * H * nchunk * (size_t)(d + 2) * sizeof(float);
 }
 
+namespace {
+hipError_t dispatch(const void* q, const void* kc, const void* vc, const int32_t* seqlens, void* o,
+                    float* lse, int S, int H, int Lmax, int d, float scale, int window, int chunk,
+                    void* ws, bool is_bf16, PagedCache pc, hipStream_t stream) {
+  if (is_bf16) {
+    if (d == 128)
+      return launch_t<bf16, 128>(q, kc, vc, seqlens, o, lse, S, H, Lmax, scale, window, chunk, ws, pc, stream);
+    return launch_t<bf16, 64>(q, kc, vc, seqlens, o, lse, S, H, Lmax, scale, window, chunk, ws, pc, stream);
+  }
+  if (d == 128)
+    return launch_t<float, 128>(q, kc, vc, seqlens, o, lse, S, H, Lmax, scale, window, chunk, ws, pc, stream);
+  return launch_t<float, 64>(q, kc, vc, seqlens, o, lse, S, H, Lmax, scale, window, chunk, ws, pc, stream);
+}
+}  // namespace
+
 hipError_t launch_decode(const void* q, const void* kc, const void* vc, const int32_t* seqlens,
                          void* o, float* lse, int S, int H, int Lmax, int d, float scale,
                          int window, int chunk, void* ws, bool is_bf16, hipStream_t stream) {
-  if (is_bf16) {
-    if (d == 128)
-      return launch_t<bf16, 128>(q, kc, vc, seqlens, o, lse, S, H, Lmax, scale, window, chunk, ws, stream);
-    return launch_t<bf16, 64>(q, kc, vc, seqlens, o, lse, S, H, Lmax, scale, window, chunk, ws, stream);
-  }
-  if (d == 128)
-    return launch_t<float, 128>(q, kc, vc, seqlens, o, lse, S, H, Lmax, scale, window, chunk, ws, stream);
-  return launch_t<float, 64>(q, kc, vc, seqlens, o, lse, S, H, Lmax, scale, window, chunk, ws, stream);
+  return dispatch(q, kc, vc, seqlens, o, lse, S, H, Lmax, d, scale, window, chunk, ws, is_bf16,
+                  PagedCache{nullptr, 0, 0, 0}, stream);
+}
+
+hipError_t launch_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                               const int32_t* block_table, const int32_t* seqlens, void* o, float* lse,
+                               int S, int H, int d, int num_pages, int page_size, int max_pages,
+                               float scale, int window, int chunk, void* ws, bool is_bf16,
+                               hipStream_t stream) {
+  return dispatch(q, k_pages, v_pages, seqlens, o, lse, S, H, max_pages * page_size, d, scale, window,
+                  chunk, ws, is_bf16, PagedCache{block_table, page_size, max_pages, num_pages}, stream);
 }
 
 }  // namespace fa

@@ -32,6 +32,11 @@ int decode_auto_chunk(int S, int H, int Lmax);
 hipError_t launch_decode(const void* q, const void* kc, const void* vc, const int32_t* seqlens,
                          void* o, float* lse, int S, int H, int Lmax, int d, float scale,
                          int window, int chunk, void* ws, bool is_bf16, hipStream_t stream);
+hipError_t launch_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                               const int32_t* block_table, const int32_t* seqlens, void* o, float* lse,
+                               int S, int H, int d, int num_pages, int page_size, int max_pages,
+                               float scale, int window, int chunk, void* ws, bool is_bf16,
+                               hipStream_t stream);
 
 // bf16 backward (preprocess + K/V-stationary main kernel), d in {64, 128}.
 size_t bwd_workspace_bytes(int B, int H, int N, int d);

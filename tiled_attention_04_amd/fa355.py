@@ -34,6 +34,8 @@ SIGNATURES = {
     "fa_fwd_ex": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P, _I, _I]),
     "fa_decode_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
     "fa_decode": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _I, _P]),
+    "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _Z,
+                             _I, _P]),
     "fa_bwd_workspace_size": (_Z, [_I, _I, _I, _I]),
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _I, _P]),
 }
@@ -155,6 +157,39 @@ def fa_decode(q, kcache, vcache, seqlens, *, scale=None, window: int = -1, chunk
     _check(lib().fa_decode(qp, kp, vp, sp, op, lp, S, H, Lmax, d, _default_scale(scale, d),
                            int(window), int(chunk), wp, workspace.numel() * workspace.element_size(),
                            _DTYPE[dt], _stream(stream)))
+    return o, lse
+
+
+def fa_decode_paged(q, k_pages, v_pages, block_table, seqlens, *, scale=None, window: int = -1,
+                    chunk: int = 0, o=None, lse=None, workspace=None, stream=None):
+    """Single-token decode over a paged cache.  q: [S,H,d]; k_pages, v_pages:
+    [num_pages,H,page_size,d]; block_table: int32 [S,max_pages] and seqlens: int32
+    [S], both on the GPU.  Returns (o [S,H,d], lse [S,H] float32)."""
+    S, H, d = q.shape
+    num_pages, _, page_size, _ = k_pages.shape
+    max_pages = block_table.shape[1]
+    dt = q.dtype
+    if dt not in _DTYPE:
+        raise ValueError(f"unsupported dtype {dt}")
+    qp = _dev(q, "q", dt)
+    kp = _dev(k_pages, "k_pages", dt, (num_pages, H, page_size, d))
+    vp = _dev(v_pages, "v_pages", dt, (num_pages, H, page_size, d))
+    tp = _dev(block_table, "block_table", torch.int32, (S, max_pages))
+    sp = _dev(seqlens, "seqlens", torch.int32, (S,))
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((S, H), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        need = fa_decode_workspace_size(S, H, max_pages * page_size, d, chunk)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    op = _dev(o, "o", dt, q.shape)
+    lp = _dev(lse, "lse", torch.float32, (S, H))
+    wp = _dev(workspace, "workspace")
+    _check(lib().fa_decode_paged(qp, kp, vp, tp, sp, op, lp, S, H, d, num_pages, page_size, max_pages,
+                                 _default_scale(scale, d), int(window), int(chunk), wp,
+                                 workspace.numel() * workspace.element_size(), _DTYPE[dt],
+                                 _stream(stream)))
     return o, lse
 
 

@@ -102,3 +102,37 @@ def dense_cache(inp: DecodeInputs, Lmax: int, device="cpu", fill=float("nan")):
         kc[s, :, :n].copy_(inp.k_rows[s])
         vc[s, :, :n].copy_(inp.v_rows[s])
     return kc, vc
+
+
+def paged_cache(inp: DecodeInputs, page_size: int, device="cpu", seed: int = 0,
+                spare_pages: int = 0, fill=float("nan")):
+    """The same rows in a page pool: ([P_total, H, page_size, d] K and V pools,
+    [S, max_pages] int32 page table).
+
+    Sequence s takes ceil(n_s / page_size) pages; the pages of all sequences
+    (plus ``spare_pages`` that belong to nobody) are a random permutation of
+    the pool drawn from ``default_rng(seed)``, so neighbouring tokens of one
+    sequence are scattered over the pool.  Rows of a page past the sequence's
+    end, spare pages and unused table entries (-1) hold ``fill``.
+    """
+    S, H, d = inp.q.shape
+    slots = [-(-int(n) // page_size) for n in inp.seqlens]
+    num_pages = sum(slots) + spare_pages
+    perm = np.random.default_rng(seed).permutation(num_pages)
+    max_pages = max(slots)
+    table = np.full((S, max_pages), -1, dtype=np.int32)
+    kp = torch.full((num_pages, H, page_size, d), fill, dtype=inp.q.dtype, device=device)
+    vp = torch.full((num_pages, H, page_size, d), fill, dtype=inp.q.dtype, device=device)
+    nxt = 0
+    for s in range(S):
+        n, m = int(inp.seqlens[s]), slots[s]
+        ids = perm[nxt:nxt + m]
+        nxt += m
+        table[s, :m] = ids
+        idx = torch.from_numpy(ids.astype(np.int64)).to(device)
+        for pool, rows in ((kp, inp.k_rows[s]), (vp, inp.v_rows[s])):
+            pad = torch.full((H, m * page_size, d), fill, dtype=rows.dtype)
+            pad[:, :n] = rows
+            pages = pad.view(H, m, page_size, d).transpose(0, 1).contiguous().to(device)
+            pool.index_copy_(0, idx, pages)
+    return kp, vp, torch.from_numpy(table).to(device)
