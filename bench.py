@@ -7,6 +7,7 @@ batch (already resident in HBM when timing starts):
   3. KV-cache decode,           64 sequences x 32 heads, d=128, lengths U[512, 8192]
   4. causal backward,           B=2, H=16, N=4096, d=128, bf16 (from the forward's O and L)
   5. paged KV-cache decode,     the decode batch of 3 in 64-token pages scattered over a pool
+  6. causal forward in fp16,    the shape of 1 with fp16 inputs (same seeds)
 
 The headline value is the causal forward's TFLOP/s (4*B*H*N^2*d/2 algorithmic
 flops per launch over its measured time); every stage is timed with HIP events
@@ -97,7 +98,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--stages", default="fwd,window,decode,bwd,paged")
+    ap.add_argument("--stages", default="fwd,window,decode,bwd,paged,fwd16")
     ap.add_argument("--page-size", type=int, default=64)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, copy 1 GiB device-to-device three times: the reference "
@@ -129,6 +130,10 @@ def main():
     l3 = torch.empty((B3, H3, N3), dtype=torch.float32, device=dev)
     o3w = torch.empty_like(q3)
     l3w = torch.empty_like(l3)
+    if "fwd16" in stages:
+        q7, k7, v7 = (t.to(dev) for t in attention_inputs(B3, H3, N3, d3, "fp16", seed=0))
+        o7 = torch.empty_like(q7)
+        l7 = torch.empty_like(l3)
 
     w4 = WORKLOADS["decode_s64_h32_d128_len512to8192_bf16"]
     if "decode" in stages or "paged" in stages:
@@ -187,6 +192,9 @@ def main():
         if "paged" in stages:
             fa.fa_decode_paged(q4, kp6, vp6, tb6, sl4, o=o6, lse=l6, workspace=ws6)
         mark(5)
+        if "fwd16" in stages:
+            fa.fa_fwd(q7, k7, v7, causal=True, o=o7, lse=l7)
+        mark(6)
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -194,17 +202,17 @@ def main():
     torch.cuda.synchronize()
 
     log(f"timing {args.steps} steps")
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    comp = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(5)]
+    comp = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(6)]
                      for i in range(args.steps)])  # ms
     ms = comp.mean(axis=0)
-    log("stage ms (mean): " + ", ".join(f"{n}={m:.4f}" for n, m in zip(("fwd", "window", "decode", "bwd", "paged"), ms)))
+    log("stage ms (mean): " + ", ".join(f"{n}={m:.4f}" for n, m in zip(("fwd", "window", "decode", "bwd", "paged", "fwd16"), ms)))
 
     components = {}
 
@@ -236,6 +244,9 @@ def main():
                          "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "traffic": measured_traffic(f"decode_paged{args.page_size}")}}
 
+    if "fwd16" in stages:
+        mfma_stage("fwd_causal_fp16_b4_h32_n4096_d128", flops3, ms[5], "fwd_fp16_causal")
+
     if args.copy_calibration:
         log("copy calibration: 3 x 1 GiB device-to-device")
         src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)
@@ -256,7 +267,8 @@ def main():
         "dtype": "bf16", "data": "synthetic (seeded N(0,1), rounded to bf16)",
         "config": {"workload": "causal forward B=4 H=32 N=4096 d=128 bf16 (step also runs: window-1024 "
                                "forward, 64x32 ragged decode d=128 lengths U[512,8192] from a dense and "
-                               "from a 64-token paged cache, causal backward B=2 H=16 N=4096 d=128)",
+                               "from a 64-token paged cache, causal backward B=2 H=16 N=4096 d=128, the causal "
+                               "forward in fp16)",
                    "global_batch": B3, "seq_len": N3, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(value, 3) if value is not None else None,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

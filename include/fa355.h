@@ -17,8 +17,12 @@
  *  - All tensor pointers are DEVICE pointers (memory of the current HIP
  *    device); sizes are element counts.  Tensors are dense and row-major
  *    ("contiguous") in the layouts stated per call.
- *  - dtype FA_BF16: q/k/v/o/dO are bfloat16; FA_FP32: they are float32.
- *    lse, dq, dk, dv and all statistics are float32 in both cases.
+ *  - dtype FA_BF16: q/k/v/o/dO (and the caches) are bfloat16; FA_FP16:
+ *    IEEE half precision; FA_FP32: float32.  lse, dq, dk, dv and all
+ *    statistics are float32 in every case.  The 16-bit types run the same
+ *    matrix-core kernels (fp16 inputs with an fp32 accumulator are the
+ *    mixed-precision upgrade listed in "Build a FlashAttention Tiled
+ *    Self-Attention Block from Scratch in Pure NumPy", Extending It).
  *  - Ownership: the caller owns every buffer, including workspaces.  The
  *    library never allocates, frees or synchronises; every call is
  *    asynchronous on `stream` (a hipStream_t, NULL = the default stream).
@@ -50,7 +54,7 @@ typedef enum fa_status {
   FA_ERR_HIP = 4          /* the HIP launch itself failed                  */
 } fa_status;
 
-typedef enum fa_dtype { FA_FP32 = 0, FA_BF16 = 1 } fa_dtype;
+typedef enum fa_dtype { FA_FP32 = 0, FA_BF16 = 1, FA_FP16 = 2 } fa_dtype;
 
 /* Library version (major * 10000 + minor * 100 + patch). */
 int fa_version(void);
@@ -77,8 +81,8 @@ const char* fa_last_error(void);
  *   lse     : [B, H, N] float32 output, L = m + ln(l) (natural log), or NULL
  *   causal  : 0 or 1;  window : -1 (off) or >= 0
  *
- * Supported: FA_BF16 with d in {64, 128} (MFMA kernels); FA_FP32 with
- * 1 <= d <= 128 (generic kernel).  Other d: FA_ERR_UNSUPPORTED.
+ * Supported: FA_BF16 and FA_FP16 with d in {64, 128} (MFMA kernels);
+ * FA_FP32 with 1 <= d <= 128 (generic kernel).  Other d: FA_ERR_UNSUPPORTED.
  * Sizes: B*H <= 2^31-1 and B*H*N*d < 2^63; N need not be a tile multiple.
  */
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -90,7 +94,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
  *   FA_FP32: 1 <= block_q <= 64, 1 <= block_k <= 64 (any values, e.g. 4 x 4
  *            for the worked example "FlashAttention Algorithm > Worked
  *            Example", Setting Up the Example).
- *   FA_BF16: block_q in {32, 64, 128, 256}, block_k = 64.
+ *   FA_BF16, FA_FP16: block_q in {32, 64, 128, 256}, block_k = 64.
  * Any other pair: FA_ERR_INVALID_ARG.
  */
 fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -127,7 +131,7 @@ size_t fa_decode_workspace_size(int S, int H, int Lmax, int d, int chunk);
  *   chunk    : tokens per split, a positive multiple of 64, or 0 (auto)
  *   workspace: >= fa_decode_workspace_size(S, H, Lmax, d, chunk) bytes
  *
- * Supported: FA_BF16 and FA_FP32 with d in {64, 128}.
+ * Supported: FA_BF16, FA_FP16 and FA_FP32 with d in {64, 128}.
  */
 fa_status fa_decode(const void* q, const void* kcache, const void* vcache,
                     const int32_t* seqlens, void* o, float* lse,
@@ -161,7 +165,7 @@ fa_status fa_decode(const void* q, const void* kcache, const void* vcache,
  *   workspace   : >= fa_decode_workspace_size(S, H, max_pages * page_size,
  *                 d, chunk) bytes
  *
- * Supported: FA_BF16 and FA_FP32 with d in {64, 128}.
+ * Supported: FA_BF16, FA_FP16 and FA_FP32 with d in {64, 128}.
  */
 fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
                           const int32_t* block_table, const int32_t* seqlens, void* o, float* lse,
@@ -190,7 +194,7 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d);
  *   dq, dk, dv     : [B, H, N, d] float32 outputs
  *   workspace      : >= fa_bwd_workspace_size(B, H, N, d) bytes
  *
- * Supported: FA_BF16 with d in {64, 128}.  No atomics: dq, dk and dv are
+ * Supported: FA_BF16 and FA_FP16 with d in {64, 128}.  No atomics: dq, dk and dv are
  * each written once, so repeated calls give identical bits.
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,

@@ -8,6 +8,7 @@ replaced: if it is missing, calls raise.
 
 from .fa355 import (  # noqa: F401
     FA_BF16,
+    FA_FP16,
     FA_FP32,
     FaError,
     fa_bwd,

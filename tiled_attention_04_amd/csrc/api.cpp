@@ -30,9 +30,15 @@ fa_status done(hipError_t err, const char* what) {
   return FA_OK;
 }
 
-size_t elem_bytes(fa_dtype t) { return t == FA_BF16 ? 2 : 4; }
+size_t elem_bytes(fa_dtype t) { return t == FA_FP32 ? 4 : 2; }
 
-bool valid_dtype(int t) { return t == FA_FP32 || t == FA_BF16; }
+bool valid_dtype(int t) { return t == FA_FP32 || t == FA_BF16 || t == FA_FP16; }
+
+fa::Elem elem_of(fa_dtype t) {
+  return t == FA_BF16 ? fa::Elem::kBF16 : t == FA_FP16 ? fa::Elem::kF16 : fa::Elem::kF32;
+}
+
+const char* dtype_name(fa_dtype t) { return t == FA_BF16 ? "bf16" : t == FA_FP16 ? "fp16" : "float32"; }
 
 constexpr long long kMaxThreadsPerLaunch = 0xFFFFFFFFLL;  // grid * block must fit 32 bits
 constexpr long long kMaxBufferBytes = 0x7FFFFFFFLL;       // 32-bit buffer offsets per slice
@@ -100,16 +106,17 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float*
                                     B, H, N, d, scale, mask, block_q, block_k, (hipStream_t)stream),
                 "fa_fwd (float32)");
   }
-  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "bf16 forward supports d in {64, 128} (got %d)", d);
+  if (d != 64 && d != 128)
+    return fail(FA_ERR_UNSUPPORTED, "%s forward supports d in {64, 128} (got %d)", dtype_name(dtype), d);
   if (block_q == 0) block_q = auto_block_q(B, H, N, window);
   if (block_k == 0) block_k = 64;
   if ((block_q != 32 && block_q != 64 && block_q != 128 && block_q != 256) || block_k != 64)
-    return fail(FA_ERR_INVALID_ARG, "bf16 tiles must be {32,64,128,256} x 64 (got %d x %d)", block_q, block_k);
+    return fail(FA_ERR_INVALID_ARG, "16-bit tiles must be {32,64,128,256} x 64 (got %d x %d)", block_q, block_k);
   const long long wgs = (long long)B * H * ((N + block_q - 1) / block_q);
   if (wgs * 2 * block_q > kMaxThreadsPerLaunch) return fail(FA_ERR_UNSUPPORTED, "grid too large");
-  return done(fa::launch_fwd_bf16(q, k, v, o, lse, B, H, N, d, scale, mask, block_q,
-                                  (hipStream_t)stream),
-              "fa_fwd (bf16)");
+  return done(fa::launch_fwd_mfma(q, k, v, o, lse, B, H, N, d, scale, mask, block_q,
+                                  dtype == FA_FP16, (hipStream_t)stream),
+              dtype == FA_FP16 ? "fa_fwd (fp16)" : "fa_fwd (bf16)");
 }
 
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -148,7 +155,7 @@ fa_status fa_decode(const void* q, const void* kcache, const void* vcache, const
     return fail(FA_ERR_WORKSPACE, "decode needs %zu workspace bytes (got %zu%s)", need, workspace_bytes,
                 workspace ? "" : ", null pointer");
   return done(fa::launch_decode(q, kcache, vcache, seqlens, o, lse, S, H, Lmax, d, scale, window, chunk,
-                                workspace, dtype == FA_BF16, (hipStream_t)stream),
+                                workspace, elem_of(dtype), (hipStream_t)stream),
               "fa_decode");
 }
 
@@ -183,7 +190,7 @@ fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_page
                 workspace_bytes, workspace ? "" : ", null pointer");
   return done(fa::launch_decode_paged(q, k_pages, v_pages, block_table, seqlens, o, lse, S, H, d,
                                       num_pages, page_size, max_pages, scale, window, chunk, workspace,
-                                      dtype == FA_BF16, (hipStream_t)stream),
+                                      elem_of(dtype), (hipStream_t)stream),
               "fa_decode_paged");
 }
 
@@ -200,7 +207,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
     return fail(FA_ERR_INVALID_ARG, "every tensor pointer of fa_bwd must be non-null");
   fa_status st = check_dense(B, H, N, d, scale, causal, window, dtype);
   if (st != FA_OK) return st;
-  if (dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "backward supports bf16 inputs only");
+  if (dtype == FA_FP32) return fail(FA_ERR_UNSUPPORTED, "backward supports bf16 and fp16 inputs only");
   if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "backward supports d in {64, 128} (got %d)", d);
   if ((long long)N * d * 4 > kMaxBufferBytes)
     return fail(FA_ERR_UNSUPPORTED, "one (batch, head) slice of the float32 gradients exceeds 2 GiB");
@@ -214,8 +221,9 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   if (!workspace || workspace_bytes < need)
     return fail(FA_ERR_WORKSPACE, "backward needs %zu workspace bytes (got %zu%s)", need, workspace_bytes,
                 workspace ? "" : ", null pointer");
-  return done(fa::launch_bwd_bf16(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale,
-                                  fa::Mask{causal, window}, workspace, (hipStream_t)stream),
+  return done(fa::launch_bwd_mfma(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale,
+                                  fa::Mask{causal, window}, workspace, dtype == FA_FP16,
+                                  (hipStream_t)stream),
               "fa_bwd");
 }
 

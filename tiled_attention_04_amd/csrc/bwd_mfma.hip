@@ -1,4 +1,5 @@
-// bf16 backward that recomputes P from the stored logsumexp L.
+// 16-bit (bf16 or fp16) backward that recomputes P from the stored
+// logsumexp L.  Every kernel is written once for the element type T.
 //
 // Method: "Building Flash Attention from Scratch in Pure NumPy", Step 4 --
 // D = rowsum(dO * O) first, then an outer loop over key/value tiles and an
@@ -8,7 +9,7 @@
 //   P = exp(S - L),  dV += P^T dO,  dP = dO V^T,  dS = P * (dP - D),
 //   dK += scale * dS^T Q,  dQ += scale * dS K.
 //
-// Mapping onto CDNA4 (v_mfma_f32_32x32x16_bf16, fp32 accumulation), three
+// Mapping onto CDNA4 (v_mfma_f32_32x32x16_bf16 / _f16, fp32 accumulation), three
 // kernels on one stream:
 //  * bwd_pre: one 16-byte slice per lane, D reduced with DPP; it also stores
 //    L in log2 units so the other kernels need one exp2 per score.
@@ -51,9 +52,9 @@ __device__ __forceinline__ void interleave() {
   interleave_step<0, M, R, A, V, SYNC>();
 }
 
-template <int D>
+template <typename T, int D>
 __global__ __launch_bounds__(kPreThreads) void bwd_pre_kernel(
-    const bf16* __restrict__ o, const bf16* __restrict__ dO, const float* __restrict__ lse,
+    const T* __restrict__ o, const T* __restrict__ dO, const float* __restrict__ lse,
     float* __restrict__ Dv, float* __restrict__ L2, long long rows) {
   constexpr int LPR = D / 8;
   constexpr int RPB = kPreThreads / LPR;
@@ -67,8 +68,8 @@ __global__ __launch_bounds__(kPreThreads) void bwd_pre_kernel(
     const uint4 b = *(const uint4*)(dO + off);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p = __builtin_fmaf(bf16_lo(word(a, i)), bf16_lo(word(b, i)), p);
-      p = __builtin_fmaf(bf16_hi(word(a, i)), bf16_hi(word(b, i)), p);
+      p = __builtin_fmaf(lo16<T>(word(a, i)), lo16<T>(word(b, i)), p);
+      p = __builtin_fmaf(hi16<T>(word(a, i)), hi16<T>(word(b, i)), p);
     }
   }
   p = group_sum<LPR>(p);
@@ -108,10 +109,10 @@ struct BwdTile {
   static_assert(kQBytes % 1024 == 0 && kKBytes % 1024 == 0, "tiles must be whole 1 KB blocks");
 };
 
-template <int D>
+template <typename T, int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void bwd_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
-                     const bf16* __restrict__ v, const bf16* __restrict__ dO,
+void bwd_main_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                     const T* __restrict__ v, const T* __restrict__ dO,
                      const float* __restrict__ Dv, const float* __restrict__ L2,
                      float* __restrict__ dk, float* __restrict__ dv,
                      int BH, int N, int nkt, float scale, float scale_log2, int causal, int window) {
@@ -149,12 +150,12 @@ void bwd_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   // This wave's 32 value rows as B operands of dP: V[key][16 s + 8 h + 0..7].
   const int my_key = k0 + 32 * kb + l32;
-  bf16x8 vf[KS];
+  vec8<T> vf[KS];
   {
     const rsrc_t v_src = make_rsrc(v + base, head_bytes);
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      vf[s] = as_bf16x8(load16(v_src, (uint32_t)(my_key * D + 16 * s + 8 * h) * 2u));
+      vf[s] = as_vec8<T>(load16(v_src, (uint32_t)(my_key * D + 16 * s + 8 * h) * 2u));
   }
 
   // Query tiles that see at least one of this workgroup's keys.
@@ -238,12 +239,12 @@ void bwd_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      sacc = mfma32(*(const bf16x8*)(Qs + q_rd + 32 * s), *(const bf16x8*)(Kt + k_rd + 32 * s), sacc);
+      sacc = mfma32(*(const vec8<T>*)(Qs + q_rd + 32 * s), *(const vec8<T>*)(Kt + k_rd + 32 * s), sacc);
     interleave<KS, 2 * KS, 4, 0, 1>();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      dpacc = mfma32(*(const bf16x8*)(Os + q_rd + 32 * s), vf[s], dpacc);
+      dpacc = mfma32(*(const vec8<T>*)(Os + q_rd + 32 * s), vf[s], dpacc);
     float pv[16];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -267,15 +268,15 @@ void bwd_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     }
     uint32_t ppk[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) ppk[j] = pack_bf16(pv[2 * j], pv[2 * j + 1]);
+    for (int j = 0; j < 8; ++j) ppk[j] = pack2<T>(pv[2 * j], pv[2 * j + 1]);
     interleave<KS, KS, 4, 6, 2>();
     __builtin_amdgcn_sched_barrier(0);
     uint32_t dspk[8];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const float4 D4 = *(const float4*)(LD + kBQ + 32 * qb + 8 * g + 4 * h);
-      dspk[2 * g] = pack_bf16(pv[4 * g] * (dpacc[4 * g] - D4.x), pv[4 * g + 1] * (dpacc[4 * g + 1] - D4.y));
-      dspk[2 * g + 1] = pack_bf16(pv[4 * g + 2] * (dpacc[4 * g + 2] - D4.z),
+      dspk[2 * g] = pack2<T>(pv[4 * g] * (dpacc[4 * g] - D4.x), pv[4 * g + 1] * (dpacc[4 * g + 1] - D4.y));
+      dspk[2 * g + 1] = pack2<T>(pv[4 * g + 2] * (dpacc[4 * g + 2] - D4.z),
                                   pv[4 * g + 3] * (dpacc[4 * g + 3] - D4.w));
     }
     // P^T and dS^T rows: this lane's key, its 16 queries in A-operand order.
@@ -293,13 +294,13 @@ void bwd_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     //    step) for this wave's column blocks.
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const bf16x8 pa = *(const bf16x8*)(Pt + s_rd + 32 * s);
-      const bf16x8 da = *(const bf16x8*)(dSt + s_rd + 32 * s);
+      const vec8<T> pa = *(const vec8<T>*)(Pt + s_rd + 32 * s);
+      const vec8<T> da = *(const vec8<T>*)(dSt + s_rd + 32 * s);
 #pragma unroll
       for (int c = 0; c < NCB; ++c) {
         const int off = tr_q + 16 * s * QP + 64 * (NCB * qb + c);
-        dv_acc[c] = mfma32(pa, read_tr8<QP>(Os + off), dv_acc[c]);
-        dk_acc[c] = mfma32(da, read_tr8<QP>(Qs + off), dk_acc[c]);
+        dv_acc[c] = mfma32(pa, read_tr8<QP, T>(Os + off), dv_acc[c]);
+        dk_acc[c] = mfma32(da, read_tr8<QP, T>(Qs + off), dk_acc[c]);
       }
     }
     interleave<8 * NCB, 8 + 16 * NCB, 4, 0, 3>();
@@ -341,7 +342,7 @@ void bwd_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 //   P^T = exp2(S^T * scale * log2e - L2),  dS^T = P^T (dP^T - D)
 //                                 (L2 and D: one value per lane),
 //   dQ^T += K^T dS^T              (K^T by transpose reads of the K tile, dS^T
-//                                  packed to bf16 straight from the
+//                                  packed to T straight from the
 //                                  accumulators, as P in the forward).
 // K and V tiles are double-buffered in LDS and filled by direct loads.
 constexpr int kDqBK = 64;   // keys per tile
@@ -358,10 +359,10 @@ struct DqTile {
   static_assert(kKBytes % 1024 == 0 && kVBytes % 1024 == 0, "tiles must be whole 1 KB blocks");
 };
 
-template <int D>
+template <typename T, int D>
 __global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
-                   const bf16* __restrict__ v, const bf16* __restrict__ dO,
+void bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                   const T* __restrict__ v, const T* __restrict__ dO,
                    const float* __restrict__ Dv, const float* __restrict__ L2,
                    float* __restrict__ dq, int BH, int N, int nqt, float scale, float scale_log2,
                    int causal, int window) {
@@ -392,15 +393,15 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   // Q and dO rows of this lane as B fragments: [qi][16 s + 8 h + 0..7]
   // (rows past N read as zero), and the row's L2 and D.
-  bf16x8 qf[KS], of[KS];
+  vec8<T> qf[KS], of[KS];
   {
     const rsrc_t q_src = make_rsrc(q + base, (uint32_t)N * D * 2u);
     const rsrc_t o_src = make_rsrc(dO + base, (uint32_t)N * D * 2u);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const uint32_t off = (uint32_t)(qi * D + 16 * s + 8 * h) * 2u;
-      qf[s] = as_bf16x8(load16(q_src, off));
-      of[s] = as_bf16x8(load16(o_src, off));
+      qf[s] = as_vec8<T>(load16(q_src, off));
+      of[s] = as_vec8<T>(load16(o_src, off));
     }
   }
   const bool row_ok = qi < N;
@@ -463,8 +464,8 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       dpacc[kb2] = f32x16{};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        sacc[kb2] = mfma32(*(const bf16x8*)(Kc + k_rd + kb2 * 32 * KP + 32 * s), qf[s], sacc[kb2]);
-        dpacc[kb2] = mfma32(*(const bf16x8*)(Vc + v_rd + kb2 * 32 * VP + 32 * s), of[s], dpacc[kb2]);
+        sacc[kb2] = mfma32(*(const vec8<T>*)(Kc + k_rd + kb2 * 32 * KP + 32 * s), qf[s], sacc[kb2]);
+        dpacc[kb2] = mfma32(*(const vec8<T>*)(Vc + v_rd + kb2 * 32 * VP + 32 * s), of[s], dpacc[kb2]);
       }
     }
     // dS^T = P^T (dP^T - D), P^T = exp2(S^T c - L2) with hidden keys at 0
@@ -490,7 +491,7 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
       for (int r = 0; r < 16; r += 2)
-        dspk[kb2][r >> 1] = pack_bf16(sacc[kb2][r] * (dpacc[kb2][r] - Di),
+        dspk[kb2][r >> 1] = pack2<T>(sacc[kb2][r] * (dpacc[kb2][r] - Di),
                                       sacc[kb2][r + 1] * (dpacc[kb2][r + 1] - Di));
     // dQ^T += K^T dS^T, 16 keys per step.
 #pragma unroll
@@ -499,7 +500,7 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                         dspk[s >> 1][4 * (s & 1) + 2], dspk[s >> 1][4 * (s & 1) + 3]};
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
-        dqa[cb] = mfma32(read_tr8<KP>(Kc + k_tr + 16 * s * KP + 64 * cb), as_bf16x8(dw), dqa[cb]);
+        dqa[cb] = mfma32(read_tr8<KP, T>(Kc + k_tr + 16 * s * KP + 64 * cb), as_vec8<T>(dw), dqa[cb]);
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads of the next tile have landed
     __syncthreads();
@@ -563,10 +564,10 @@ __device__ __forceinline__ void pin_dq_phase(uint32_t (&ds)[2][8], f32x16 (&acc)
 #endif
 }
 
-template <int D>
+template <typename T, int D>
 __global__ __launch_bounds__(kDqPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void bwd_dq_pp_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
-                      const bf16* __restrict__ v, const bf16* __restrict__ dO,
+void bwd_dq_pp_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                      const T* __restrict__ v, const T* __restrict__ dO,
                       const float* __restrict__ Dv, const float* __restrict__ L2,
                       float* __restrict__ dq, int BH, int N, int nqt, float scale, float scale_log2,
                       int causal, int window) {
@@ -604,15 +605,15 @@ void bwd_dq_pp_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   // Q and dO rows of this lane as B fragments (rows past N read as zero), and
   // the row's L2 and D.
-  bf16x8 qf[KS], of[KS];
+  vec8<T> qf[KS], of[KS];
   {
     const rsrc_t q_src = make_rsrc(q + base, (uint32_t)N * D * 2u);
     const rsrc_t o_src = make_rsrc(dO + base, (uint32_t)N * D * 2u);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const uint32_t off = (uint32_t)(qi * D + 16 * s + 8 * h) * 2u;
-      qf[s] = as_bf16x8(load16(q_src, off));
-      of[s] = as_bf16x8(load16(o_src, off));
+      qf[s] = as_vec8<T>(load16(q_src, off));
+      of[s] = as_vec8<T>(load16(o_src, off));
     }
   }
   const bool row_ok = qi < N;
@@ -683,8 +684,8 @@ void bwd_dq_pp_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       dpc[kb2] = f32x16{};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        sc[kb2] = mfma32(*(const bf16x8*)(kn + kb2 * 32 * KP + 32 * s), qf[s], sc[kb2]);
-        dpc[kb2] = mfma32(*(const bf16x8*)(vn + kb2 * 32 * VP + 32 * s), of[s], dpc[kb2]);
+        sc[kb2] = mfma32(*(const vec8<T>*)(kn + kb2 * 32 * KP + 32 * s), qf[s], sc[kb2]);
+        dpc[kb2] = mfma32(*(const vec8<T>*)(vn + kb2 * 32 * VP + 32 * s), of[s], dpc[kb2]);
       }
     }
   };
@@ -730,7 +731,7 @@ void bwd_dq_pp_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int r = 0; r < 16; r += 2)
-          dspk[kb2][r >> 1] = pack_bf16(sc[kb2][r] * (dpc[kb2][r] - Di),
+          dspk[kb2][r >> 1] = pack2<T>(sc[kb2][r] * (dpc[kb2][r] - Di),
                                         sc[kb2][r + 1] * (dpc[kb2][r + 1] - Di));
     } else {
 #pragma unroll
@@ -753,7 +754,7 @@ void bwd_dq_pp_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                           dspk[s >> 1][4 * (s & 1) + 2], dspk[s >> 1][4 * (s & 1) + 3]};
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
-          dqa[cb] = mfma32(read_tr8<KP>(kc + 16 * s * KP + 64 * cb), as_bf16x8(dw), dqa[cb]);
+          dqa[cb] = mfma32(read_tr8<KP, T>(kc + 16 * s * KP + 64 * cb), as_vec8<T>(dw), dqa[cb]);
       }
     }
     if (act_next) scores(integral_constant<int, STN>{});
@@ -782,7 +783,7 @@ void bwd_dq_pp_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   }
 }
 
-template <int D>
+template <typename T, int D>
 hipError_t launch_t(const void* q, const void* k, const void* v, const void* o, const void* dO,
                     const float* lse, float* dq, float* dk, float* dv, int B, int H, int N,
                     float scale, Mask mask, void* ws, hipStream_t stream) {
@@ -790,14 +791,14 @@ hipError_t launch_t(const void* q, const void* k, const void* v, const void* o, 
   float* Dv = (float*)ws;
   float* L2 = Dv + rows;
   constexpr int RPB = kPreThreads / (D / 8);
-  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(kPreThreads),
-                     0, stream, (const bf16*)o, (const bf16*)dO, lse, Dv, L2, rows);
+  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(kPreThreads),
+                     0, stream, (const T*)o, (const T*)dO, lse, Dv, L2, rows);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int nkt = (N + kBKV - 1) / kBKV;
   const long long grid = (long long)nkt * B * H;
-  hipLaunchKernelGGL((bwd_main_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dO, Dv, L2, dk, dv,
+  hipLaunchKernelGGL((bwd_main_kernel<T, D>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                     (const T*)q, (const T*)k, (const T*)v, (const T*)dO, Dv, L2, dk, dv,
                      B * H, N, nkt, scale, scale * kLog2e, mask.causal, mask.window);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -805,14 +806,14 @@ hipError_t launch_t(const void* q, const void* k, const void* v, const void* o, 
   // still fills the chip, else the 4-wave kernel (128 rows).
   if ((long long)B * H * ((N + 255) / 256) >= 256) {
     const int nqt = (N + 255) / 256;
-    hipLaunchKernelGGL((bwd_dq_pp_kernel<D>), dim3((unsigned)((long long)nqt * B * H)), dim3(kDqPPThreads),
-                       0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dO, Dv,
+    hipLaunchKernelGGL((bwd_dq_pp_kernel<T, D>), dim3((unsigned)((long long)nqt * B * H)), dim3(kDqPPThreads),
+                       0, stream, (const T*)q, (const T*)k, (const T*)v, (const T*)dO, Dv,
                        L2, dq, B * H, N, nqt, scale, scale * kLog2e, mask.causal, mask.window);
   } else {
     constexpr int BQ = kDqThreads / 2;  // 32 query rows per wave
     const int nqt = (N + BQ - 1) / BQ;
-    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)((long long)nqt * B * H)), dim3(kDqThreads), 0,
-                       stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dO, Dv, L2,
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3((unsigned)((long long)nqt * B * H)), dim3(kDqThreads), 0,
+                       stream, (const T*)q, (const T*)k, (const T*)v, (const T*)dO, Dv, L2,
                        dq, B * H, N, nqt, scale, scale * kLog2e, mask.causal, mask.window);
   }
   return hipGetLastError();
@@ -825,12 +826,17 @@ size_t bwd_workspace_bytes(int B, int H, int N, int d) {
   return (size_t)B * H * N * 2 * sizeof(float);
 }
 
-hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const void* o,
                            const void* dO, const float* lse, float* dq, float* dk, float* dv,
-                           int B, int H, int N, int d, float scale, Mask mask, void* ws,
+                           int B, int H, int N, int d, float scale, Mask mask, void* ws, bool f16,
                            hipStream_t stream) {
-  if (d == 128) return launch_t<128>(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, scale, mask, ws, stream);
-  return launch_t<64>(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, scale, mask, ws, stream);
+  if (f16) {
+    if (d == 128)
+      return launch_t<fa::f16, 128>(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, scale, mask, ws, stream);
+    return launch_t<fa::f16, 64>(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, scale, mask, ws, stream);
+  }
+  if (d == 128) return launch_t<bf16, 128>(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, scale, mask, ws, stream);
+  return launch_t<bf16, 64>(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, scale, mask, ws, stream);
 }
 
 }  // namespace fa

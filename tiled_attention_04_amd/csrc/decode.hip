@@ -47,6 +47,16 @@ __device__ __forceinline__ void widen<bf16>(const uint4& u, float (&x)[8]) {
 }
 
 template <>
+__device__ __forceinline__ void widen<f16>(const uint4& u, float (&x)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = word(u, i);
+    x[2 * i] = f16_lo(w);
+    x[2 * i + 1] = f16_hi(w);
+  }
+}
+
+template <>
 __device__ __forceinline__ void widen<float>(const uint4& u, float (&x)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) x[i] = __builtin_bit_cast(float, word(u, i));
@@ -205,6 +215,8 @@ template <>
 __device__ __forceinline__ float from_float<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ bf16 from_float<bf16>(float x) { return (bf16)x; }
+template <>
+__device__ __forceinline__ f16 from_float<f16>(float x) { return (f16)x; }
 
 // One workgroup of D threads per (sequence, head): M = max m_c,
 // l = sum exp(m_c - M) l_c, o = sum exp(m_c - M) o_c / l, L = M ln2 + ln l.
@@ -275,34 +287,43 @@ size_t decode_workspace_bytes(int S, int H, int Lmax, int d, int chunk) {
 }
 
 namespace {
+template <typename T>
+hipError_t dispatch_t(const void* q, const void* kc, const void* vc, const int32_t* seqlens, void* o,
+                      float* lse, int S, int H, int Lmax, int d, float scale, int window, int chunk,
+                      void* ws, PagedCache pc, hipStream_t stream) {
+  if (d == 128)
+    return launch_t<T, 128>(q, kc, vc, seqlens, o, lse, S, H, Lmax, scale, window, chunk, ws, pc, stream);
+  return launch_t<T, 64>(q, kc, vc, seqlens, o, lse, S, H, Lmax, scale, window, chunk, ws, pc, stream);
+}
+
 hipError_t dispatch(const void* q, const void* kc, const void* vc, const int32_t* seqlens, void* o,
                     float* lse, int S, int H, int Lmax, int d, float scale, int window, int chunk,
-                    void* ws, bool is_bf16, PagedCache pc, hipStream_t stream) {
-  if (is_bf16) {
-    if (d == 128)
-      return launch_t<bf16, 128>(q, kc, vc, seqlens, o, lse, S, H, Lmax, scale, window, chunk, ws, pc, stream);
-    return launch_t<bf16, 64>(q, kc, vc, seqlens, o, lse, S, H, Lmax, scale, window, chunk, ws, pc, stream);
+                    void* ws, Elem elem, PagedCache pc, hipStream_t stream) {
+  switch (elem) {
+    case Elem::kBF16:
+      return dispatch_t<bf16>(q, kc, vc, seqlens, o, lse, S, H, Lmax, d, scale, window, chunk, ws, pc, stream);
+    case Elem::kF16:
+      return dispatch_t<f16>(q, kc, vc, seqlens, o, lse, S, H, Lmax, d, scale, window, chunk, ws, pc, stream);
+    default:
+      return dispatch_t<float>(q, kc, vc, seqlens, o, lse, S, H, Lmax, d, scale, window, chunk, ws, pc, stream);
   }
-  if (d == 128)
-    return launch_t<float, 128>(q, kc, vc, seqlens, o, lse, S, H, Lmax, scale, window, chunk, ws, pc, stream);
-  return launch_t<float, 64>(q, kc, vc, seqlens, o, lse, S, H, Lmax, scale, window, chunk, ws, pc, stream);
 }
 }  // namespace
 
 hipError_t launch_decode(const void* q, const void* kc, const void* vc, const int32_t* seqlens,
                          void* o, float* lse, int S, int H, int Lmax, int d, float scale,
-                         int window, int chunk, void* ws, bool is_bf16, hipStream_t stream) {
-  return dispatch(q, kc, vc, seqlens, o, lse, S, H, Lmax, d, scale, window, chunk, ws, is_bf16,
+                         int window, int chunk, void* ws, Elem elem, hipStream_t stream) {
+  return dispatch(q, kc, vc, seqlens, o, lse, S, H, Lmax, d, scale, window, chunk, ws, elem,
                   PagedCache{nullptr, 0, 0, 0}, stream);
 }
 
 hipError_t launch_decode_paged(const void* q, const void* k_pages, const void* v_pages,
                                const int32_t* block_table, const int32_t* seqlens, void* o, float* lse,
                                int S, int H, int d, int num_pages, int page_size, int max_pages,
-                               float scale, int window, int chunk, void* ws, bool is_bf16,
+                               float scale, int window, int chunk, void* ws, Elem elem,
                                hipStream_t stream) {
   return dispatch(q, k_pages, v_pages, seqlens, o, lse, S, H, max_pages * page_size, d, scale, window,
-                  chunk, ws, is_bf16, PagedCache{block_table, page_size, max_pages, num_pages}, stream);
+                  chunk, ws, elem, PagedCache{block_table, page_size, max_pages, num_pages}, stream);
 }
 
 }  // namespace fa

@@ -30,6 +30,44 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
+// ---------------------------------------------------------------- fp16 ----
+
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(f16, (uint16_t)w); }
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(f16, (uint16_t)(w >> 16));
+}
+
+// ------------------------------------------ 16-bit MFMA element types ----
+// The matrix-core kernels are written once for T = bf16 or f16: both are
+// 16-bit, so tiles, LDS layouts and transpose reads are identical; only the
+// MFMA opcode and the float <-> T conversions differ.
+template <typename T> struct Elem16;
+template <> struct Elem16<bf16> { typedef bf16x8 v8; typedef bf16x2 v2; };
+template <> struct Elem16<f16> { typedef f16x8 v8; typedef f16x2 v2; };
+template <typename T> using vec8 = typename Elem16<T>::v8;
+
+template <typename T>
+__device__ __forceinline__ vec8<T> as_vec8(uint4 u) { return __builtin_bit_cast(vec8<T>, u); }
+
+// Two floats -> packed pair of T (round to nearest even).
+template <typename T>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, typename Elem16<T>::v2));
+}
+
+// Low / high element of a packed pair of T, widened to float (exact).
+template <typename T> __device__ __forceinline__ float lo16(uint32_t w);
+template <typename T> __device__ __forceinline__ float hi16(uint32_t w);
+template <> __device__ __forceinline__ float lo16<bf16>(uint32_t w) { return bf16_lo(w); }
+template <> __device__ __forceinline__ float hi16<bf16>(uint32_t w) { return bf16_hi(w); }
+template <> __device__ __forceinline__ float lo16<f16>(uint32_t w) { return f16_lo(w); }
+template <> __device__ __forceinline__ float hi16<f16>(uint32_t w) { return f16_hi(w); }
+
 // 32-bit word i (compile-time after unrolling) of a 16-byte register value.
 __device__ __forceinline__ uint32_t word(const uint4& u, int i) {
   return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
@@ -68,6 +106,11 @@ __device__ __forceinline__ void store_f32(rsrc_t r, uint32_t byte_off, float x) 
 //                                 C[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32]
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// v_mfma_f32_32x32x16_f16: the same operand and accumulator layouts.
+__device__ __forceinline__ f32x16 mfma32(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 // Row index (within a 32 x 32 C block) of element r for a lane in half h.
@@ -179,17 +222,17 @@ __device__ __forceinline__ uint32_t block_src(int blk, int lane, int pitch) {
   return col < D * 2 ? (uint32_t)(row * D * 2 + col) : 0x80000000u;
 }
 
-// V^T-style operand of one 32x32x16 MFMA from a row-major bf16 tile in LDS:
+// V^T-style operand of one 32x32x16 MFMA from a row-major 16-bit tile in LDS:
 // two transpose reads, 8 rows apart, at this lane's address a.
-template <int PITCH>
-__device__ __forceinline__ bf16x8 read_tr8(const char* a) {
+template <int PITCH, typename T = bf16>
+__device__ __forceinline__ vec8<T> read_tr8(const char* a) {
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a);
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 8 * PITCH));
   const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-  return as_bf16x8(uint4{l2.x, l2.y, h2.x, h2.y});
+  return as_vec8<T>(uint4{l2.x, l2.y, h2.x, h2.y});
 }
 
-// This lane's transpose-read address in a row-major bf16 tile with
+// This lane's transpose-read address in a row-major 16-bit tile with
 // PITCH-byte rows.  With +16 s rows (a 16-row step) and +64 c bytes (a
 // 32-column block) read_tr8 yields, in lane l, 8 rows of column 32 c + l % 32
 // -- rows 16 s + {0..3, 8..11} in the lower half of the wave and

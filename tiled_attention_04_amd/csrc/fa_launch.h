@@ -16,33 +16,38 @@ struct Mask {
   int window;
 };
 
+// Element type of q, k, v, o (and dO, the caches).
+enum class Elem { kF32, kBF16, kF16 };
+
 // Generic float32 forward, any 1 <= d <= 128, tiles 1..64 x 1..64.
 hipError_t launch_fwd_fp32(const float* q, const float* k, const float* v, float* o, float* lse,
                            int B, int H, int N, int d, float scale, Mask mask, int block_q,
                            int block_k, hipStream_t stream);
 
-// bf16 MFMA forward, d in {64, 128}, block_q in {32, 64, 128}, block_k = 64.
-hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+// 16-bit MFMA forward (bf16, or fp16 when f16), d in {64, 128}, block_q in
+// {32, 64, 128, 256}, block_k = 64.
+hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int H, int N, int d, float scale, Mask mask, int block_q,
-                           hipStream_t stream);
+                           bool f16, hipStream_t stream);
 
-// Split-K decode (+ merge).  is_bf16 selects the element type; d in {64, 128}.
+// Split-K decode (+ merge), any Elem, d in {64, 128}.
 size_t decode_workspace_bytes(int S, int H, int Lmax, int d, int chunk);
 int decode_auto_chunk(int S, int H, int Lmax);
 hipError_t launch_decode(const void* q, const void* kc, const void* vc, const int32_t* seqlens,
                          void* o, float* lse, int S, int H, int Lmax, int d, float scale,
-                         int window, int chunk, void* ws, bool is_bf16, hipStream_t stream);
+                         int window, int chunk, void* ws, Elem elem, hipStream_t stream);
 hipError_t launch_decode_paged(const void* q, const void* k_pages, const void* v_pages,
                                const int32_t* block_table, const int32_t* seqlens, void* o, float* lse,
                                int S, int H, int d, int num_pages, int page_size, int max_pages,
-                               float scale, int window, int chunk, void* ws, bool is_bf16,
+                               float scale, int window, int chunk, void* ws, Elem elem,
                                hipStream_t stream);
 
-// bf16 backward (preprocess + K/V-stationary main kernel), d in {64, 128}.
+// 16-bit backward (bf16, or fp16 when f16): preprocess, dK/dV and dQ
+// kernels, d in {64, 128}.
 size_t bwd_workspace_bytes(int B, int H, int N, int d);
-hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const void* o,
                            const void* dO, const float* lse, float* dq, float* dk, float* dv,
-                           int B, int H, int N, int d, float scale, Mask mask, void* ws,
+                           int B, int H, int N, int d, float scale, Mask mask, void* ws, bool f16,
                            hipStream_t stream);
 
 }  // namespace fa

@@ -1,5 +1,8 @@
-// bf16 forward on gfx950 matrix cores (v_mfma_f32_32x32x16_bf16, fp32
-// accumulation).
+// 16-bit (bf16 or fp16) forward on gfx950 matrix cores
+// (v_mfma_f32_32x32x16_bf16 / _f16, fp32 accumulation).  Every kernel is
+// written once for the element type T; the two types share tiles, LDS
+// layouts and transpose reads and differ only in the MFMA opcode and the
+// conversions.
 //
 // Method: "Building Flash Attention from Scratch in Pure NumPy", Architecture
 // Overview and Steps 2-3 -- per query tile, walk the key/value tiles, keep the
@@ -19,7 +22,7 @@
 //    query column (lane % 32) and 16 of its keys, so the row max needs a
 //    single swap between the two 32-lane halves, the row sum is kept per lane
 //    and combined once at the end, and the rescale of O is one scalar per lane.
-//  * P (rounded to bf16) is already in the B-operand layout of O^T = V^T P^T.
+//  * P (rounded to T) is already in the B-operand layout of O^T = V^T P^T.
 //    The A operand V^T is read from the row-major V tile with the LDS
 //    transpose read ds_read_b64_tr_b16, whose 16-lane groups deliver 4
 //    consecutive keys of one column per lane; the two reads per MFMA step
@@ -33,7 +36,7 @@
 //    offset.
 //  * The exponentials use exp2 with scale*log2(e) folded into one FMA; the
 //    running max is taken on raw scores (a negative scale negates Q's bits
-//    instead); the row sum is accumulated in fp32 (a sum of the bf16-rounded
+//    instead); the row sum is accumulated in fp32 (a sum of the T-rounded
 //    P would cost L up to 2^-9 on rows with few keys).  L is converted back
 //    to natural log.
 //  * Workgroups are ordered so that all query tiles of one (batch, head) land
@@ -64,9 +67,9 @@ struct Tile {
 };
 
 // Issue this wave's share of the direct loads of one tile (rows k0.. of a
-// [N][D] bf16 matrix) into an LDS tile with `PITCH`-byte rows.
-template <int D, int NW, int NBLK, int PITCH, bool PRE, int NPRE>
-__device__ __forceinline__ void load_tile(const bf16* __restrict__ g, int k0, int N, char* lds_tile,
+// [N][D] 16-bit matrix) into an LDS tile with `PITCH`-byte rows.
+template <int D, int NW, int NBLK, int PITCH, bool PRE, int NPRE, typename T>
+__device__ __forceinline__ void load_tile(const T* __restrict__ g, int k0, int N, char* lds_tile,
                                           const uint32_t (&pre)[NPRE], int w, int lane) {
   const rsrc_t src = make_rsrc(g + (size_t)k0 * D, (uint32_t)max(0, N - k0) * D * 2u);
 #pragma unroll
@@ -108,7 +111,7 @@ constexpr float kSumFloor = 0x1p-60f;
 
 // One tile of the online softmax for this lane's query row ("Building Flash
 // Attention from Scratch in Pure NumPy", Step 2): raw scores s (16 keys per
-// 32-key block, in the accumulator's row order) -> bf16 P in pk, with the
+// 32-key block, in the accumulator's row order) -> P in T in pk, with the
 // running reference m_ref (log2 units) and sum l_run updated and O rescaled
 // by 2^(m_old - m_new) when the reference moves.
 //
@@ -123,7 +126,7 @@ constexpr float kSumFloor = 0x1p-60f;
 // and L = ref + log2(l) do not depend on the reference.
 // c = |scale| * log2(e), at least 1e-30 so that a hidden score (-inf) always
 // gives exp2(-inf * c - ref) = 0 exactly.
-template <int CB>
+template <typename T, int CB>
 __device__ __forceinline__ void softmax_tile(const f32x16 (&s)[2], uint32_t (&pk)[2][8],
                                              f32x16 (&oacc)[CB], float& m_ref, float& l_run,
                                              float c) {
@@ -135,7 +138,7 @@ __device__ __forceinline__ void softmax_tile(const f32x16 (&s)[2], uint32_t (&pk
       for (int r = 0; r < 16; r += 2) {
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][r], c, -ref));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][r + 1], c, -ref));
-        pk[kb2][r >> 1] = pack_bf16(p0, p1);
+        pk[kb2][r >> 1] = pack2<T>(p0, p1);
         sum += p0 + p1;
       }
     }
@@ -196,13 +199,13 @@ __device__ __forceinline__ void schedule_pipeline() {
   }
 }
 
-template <int D, int NW>
+template <typename T, int D, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1)))
-void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
-                     const bf16* __restrict__ v, bf16* __restrict__ o, float* __restrict__ lse,
+void fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                     const T* __restrict__ v, T* __restrict__ o, float* __restrict__ lse,
                      int BH, int N, int nqt, float c_log2, int negate_q, int causal, int window) {
   using TL = Tile<D>;
-  constexpr int T = 64 * NW;
+  constexpr int NT = 64 * NW;  // threads
   constexpr int BQ = 32 * NW;
   constexpr int KS = D / 16;  // MFMA steps over the head dimension
   constexpr int CB = D / 32;  // 32-column blocks of O
@@ -228,16 +231,16 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int qt = causal ? nqt - 1 - qr : qr;
   const int q0 = qt * BQ;
   const size_t base = (size_t)bh * (size_t)N * D;
-  const bf16* kg = k + base;
-  const bf16* vg = v + base;
+  const T* kg = k + base;
+  const T* vg = v + base;
   const int qi = q0 + 32 * w + l32;  // this lane's query row
 
   // Rows the direct loads may leave unwritten (past N) must hold finite values.
-  for (int i = t; i < TL::kKBytes / 16; i += T) {
+  for (int i = t; i < TL::kKBytes / 16; i += NT) {
     ((uint4*)Kb0)[i] = uint4{0u, 0u, 0u, 0u};
     ((uint4*)Kb1)[i] = uint4{0u, 0u, 0u, 0u};
   }
-  for (int i = t; i < TL::kVBytes / 16; i += T) {
+  for (int i = t; i < TL::kVBytes / 16; i += NT) {
     ((uint4*)Vb0)[i] = uint4{0u, 0u, 0u, 0u};
     ((uint4*)Vb1)[i] = uint4{0u, 0u, 0u, 0u};
   }
@@ -253,17 +256,17 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   // Q rows of this wave as MFMA B fragments: Q[qi][16 s + 8 h + 0..7]
   // (rows >= N read as zero).
   const rsrc_t q_src = make_rsrc(q + base, (uint32_t)N * D * 2u);
-  bf16x8 qf[KS];
+  vec8<T> qf[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     uint4 u = load16(q_src, (uint32_t)(qi * D + 16 * s + 8 * h) * 2u);
-    if (negate_q) {  // negative scale: S * scale = (-S) * |scale|, exact in bf16
+    if (negate_q) {  // negative scale: S * scale = (-S) * |scale|, exact in bf16 and fp16
       u.x ^= 0x80008000u;
       u.y ^= 0x80008000u;
       u.z ^= 0x80008000u;
       u.w ^= 0x80008000u;
     }
-    qf[s] = as_bf16x8(u);
+    qf[s] = as_vec8<T>(u);
   }
 
   // Key tiles holding at least one visible key for this query tile.
@@ -304,7 +307,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     s_a[kb2] = f32x16{};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const bf16x8 a = *(const bf16x8*)(Kb0 + k_rd + kb2 * 32 * TL::kKPitch + 32 * s);
+      const vec8<T> a = *(const vec8<T>*)(Kb0 + k_rd + kb2 * 32 * TL::kKPitch + 32 * s);
       s_a[kb2] = mfma32(a, qf[s], s_a[kb2]);
     }
   }
@@ -332,17 +335,17 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     // computed from whatever the buffer holds and discarded) ...
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
-      s_next[kb2] = mfma32(*(const bf16x8*)(k_next + k_rd + kb2 * 32 * TL::kKPitch), qf[0], f32x16{});
+      s_next[kb2] = mfma32(*(const vec8<T>*)(k_next + k_rd + kb2 * 32 * TL::kKPitch), qf[0], f32x16{});
 #pragma unroll
       for (int s = 1; s < KS; ++s) {
-        const bf16x8 a = *(const bf16x8*)(k_next + k_rd + kb2 * 32 * TL::kKPitch + 32 * s);
+        const vec8<T> a = *(const vec8<T>*)(k_next + k_rd + kb2 * 32 * TL::kKPitch + 32 * s);
         s_next[kb2] = mfma32(a, qf[s], s_next[kb2]);
       }
     }
 
     // ... while the vector ALUs run the softmax of this one.
     uint32_t pk[2][8];
-    softmax_tile<CB>(s_cur, pk, oacc, m_ref, l_run, c_log2);
+    softmax_tile<T, CB>(s_cur, pk, oacc, m_ref, l_run, c_log2);
 
     // O^T += V^T P^T, 16 keys per step.
     const char* vt = v_cur + v_rd;
@@ -350,14 +353,14 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     for (int s = 0; s < 4; ++s) {
       const uint4 pw = {pk[s >> 1][4 * (s & 1) + 0], pk[s >> 1][4 * (s & 1) + 1],
                         pk[s >> 1][4 * (s & 1) + 2], pk[s >> 1][4 * (s & 1) + 3]};
-      const bf16x8 pb = as_bf16x8(pw);
+      const vec8<T> pb = as_vec8<T>(pw);
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const char* p = vt + 16 * s * TL::kVPitch + 64 * cb;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * TL::kVPitch));
         const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-        const bf16x8 a = as_bf16x8(uint4{l2.x, l2.y, h2.x, h2.y});
+        const vec8<T> a = as_vec8<T>(uint4{l2.x, l2.y, h2.x, h2.y});
         oacc[cb] = mfma32(a, pb, oacc[cb]);
       }
     }
@@ -381,14 +384,14 @@ void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qi < N) {
-    bf16* orow = o + base + (size_t)qi * D;
+    T* orow = o + base + (size_t)qi * D;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         uint2 st;
-        st.x = pack_bf16(oacc[cb][4 * gq + 0] * inv, oacc[cb][4 * gq + 1] * inv);
-        st.y = pack_bf16(oacc[cb][4 * gq + 2] * inv, oacc[cb][4 * gq + 3] * inv);
+        st.x = pack2<T>(oacc[cb][4 * gq + 0] * inv, oacc[cb][4 * gq + 1] * inv);
+        st.y = pack2<T>(oacc[cb][4 * gq + 2] * inv, oacc[cb][4 * gq + 3] * inv);
         *(uint2*)(orow + cb * 32 + 8 * gq + 4 * h) = st;
       }
     }
@@ -464,10 +467,10 @@ __device__ __forceinline__ void pin_softmax_results(uint32_t (&pk)[2][8], f32x16
 constexpr int kPingPongStages = FA_PINGPONG_STAGES;
 
 
-template <int D>
+template <typename T, int D>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
-void fwd_pingpong_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
-                         const bf16* __restrict__ v, bf16* __restrict__ o, float* __restrict__ lse,
+void fwd_pingpong_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                         const T* __restrict__ v, T* __restrict__ o, float* __restrict__ lse,
                          int BH, int N, int nqt, float c_log2, int negate_q, int causal, int window) {
   using TL = Tile<D>;
   constexpr int NW = 8;
@@ -478,7 +481,7 @@ void fwd_pingpong_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   constexpr int VPER = (TL::kVBlocks + NW - 1) / NW;
   constexpr int NS = kPingPongStages;  // LDS stages; loads run NS-1 tiles ahead
   static_assert(NS == 3 || NS == 4, "3 or 4 stages");
-  // One LDS object per stage and matrix (see the alias note in fwd_bf16_kernel).
+  // One LDS object per stage and matrix (see the alias note in fwd_mfma_kernel).
   __shared__ __attribute__((aligned(1024))) char K0[TL::kKBytes];
   __shared__ __attribute__((aligned(1024))) char K1[TL::kKBytes];
   __shared__ __attribute__((aligned(1024))) char K2[TL::kKBytes];
@@ -499,8 +502,8 @@ void fwd_pingpong_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int qt = causal ? nqt - 1 - qr : qr;
   const int q0 = qt * BQ;
   const size_t base = (size_t)bh * (size_t)N * D;
-  const bf16* kg = k + base;
-  const bf16* vg = v + base;
+  const T* kg = k + base;
+  const T* vg = v + base;
   const int qi = q0 + 32 * w + l32;
 
   // (The stages need no clearing: a stage is read only after its tile has
@@ -520,7 +523,7 @@ void fwd_pingpong_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int v_nblk = (TL::kVBlocks - w + NW - 1) / NW;
 
   const rsrc_t q_src = make_rsrc(q + base, (uint32_t)N * D * 2u);
-  bf16x8 qf[KS];
+  vec8<T> qf[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     uint4 u = load16(q_src, (uint32_t)(qi * D + 16 * s + 8 * h) * 2u);
@@ -530,7 +533,7 @@ void fwd_pingpong_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       u.z ^= 0x80008000u;
       u.w ^= 0x80008000u;
     }
-    qf[s] = as_bf16x8(u);
+    qf[s] = as_vec8<T>(u);
   }
 
   const int q_hi = q0 + BQ - 1;
@@ -609,7 +612,7 @@ void fwd_pingpong_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     sc[kb2] = f32x16{};
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      sc[kb2] = mfma32(*(const bf16x8*)(K0 + k_rd + kb2 * 32 * TL::kKPitch + 32 * s), qf[s], sc[kb2]);
+      sc[kb2] = mfma32(*(const vec8<T>*)(K0 + k_rd + kb2 * 32 * TL::kKPitch + 32 * s), qf[s], sc[kb2]);
   }
   if (grp == 1) barrier_keep_loads();  // group 1 runs one phase behind
 
@@ -630,7 +633,7 @@ void fwd_pingpong_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       const bool need_mask = (k0 + kBK > N) || (causal && k0 + kBK - 1 > wq0) ||
                              (window >= 0 && k0 < wq1 - window);
       if (need_mask) mask_tile(sc, key_lo - k0, key_hi - k0, h);
-      softmax_tile<CB>(sc, pk, oacc, m_ref, l_run, c_log2);
+      softmax_tile<T, CB>(sc, pk, oacc, m_ref, l_run, c_log2);
     } else {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -653,24 +656,24 @@ void fwd_pingpong_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         for (int s = 0; s < 4; ++s) {
           const uint4 pw = {pk[s >> 1][4 * (s & 1) + 0], pk[s >> 1][4 * (s & 1) + 1],
                             pk[s >> 1][4 * (s & 1) + 2], pk[s >> 1][4 * (s & 1) + 3]};
-          const bf16x8 pb = as_bf16x8(pw);
+          const vec8<T> pb = as_vec8<T>(pw);
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb) {
             const char* p = vt + 16 * s * TL::kVPitch + 64 * cb;
             const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
             const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * TL::kVPitch));
             const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-            oacc[cb] = mfma32(as_bf16x8(uint4{l2.x, l2.y, h2.x, h2.y}), pb, oacc[cb]);
+            oacc[cb] = mfma32(as_vec8<T>(uint4{l2.x, l2.y, h2.x, h2.y}), pb, oacc[cb]);
           }
         }
       };
       auto qk = [&] __device__ () {
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) {
-          sc[kb2] = mfma32(*(const bf16x8*)(kn + kb2 * 32 * TL::kKPitch), qf[0], f32x16{});
+          sc[kb2] = mfma32(*(const vec8<T>*)(kn + kb2 * 32 * TL::kKPitch), qf[0], f32x16{});
 #pragma unroll
           for (int s = 1; s < KS; ++s)
-            sc[kb2] = mfma32(*(const bf16x8*)(kn + kb2 * 32 * TL::kKPitch + 32 * s), qf[s], sc[kb2]);
+            sc[kb2] = mfma32(*(const vec8<T>*)(kn + kb2 * 32 * TL::kKPitch + 32 * s), qf[s], sc[kb2]);
         }
       };
       if (act || act_next) {  // (a wave past all its keys does no matrix work)
@@ -701,14 +704,14 @@ void fwd_pingpong_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qi < N) {
-    bf16* orow = o + base + (size_t)qi * D;
+    T* orow = o + base + (size_t)qi * D;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         uint2 st;
-        st.x = pack_bf16(oacc[cb][4 * gq + 0] * inv, oacc[cb][4 * gq + 1] * inv);
-        st.y = pack_bf16(oacc[cb][4 * gq + 2] * inv, oacc[cb][4 * gq + 3] * inv);
+        st.x = pack2<T>(oacc[cb][4 * gq + 0] * inv, oacc[cb][4 * gq + 1] * inv);
+        st.y = pack2<T>(oacc[cb][4 * gq + 2] * inv, oacc[cb][4 * gq + 3] * inv);
         *(uint2*)(orow + cb * 32 + 8 * gq + 4 * h) = st;
       }
     }
@@ -718,46 +721,53 @@ void fwd_pingpong_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 }
 
 
-template <int D, int NW>
+template <typename T, int D, int NW>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                   int N, float scale, Mask mask, hipStream_t stream) {
   constexpr int BQ = 32 * NW;
   const int nqt = (N + BQ - 1) / BQ;
   const long long grid = (long long)nqt * B * H;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, stream,
-                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, B * H, N, nqt,
+  hipLaunchKernelGGL((fwd_mfma_kernel<T, D, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, stream,
+                     (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, B * H, N, nqt,
                      fmaxf(fabsf(scale) * kLog2e, 1e-30f), scale < 0.f ? 1 : 0, mask.causal,
                      mask.window);
   return hipGetLastError();
 }
 
-template <int D>
+template <typename T, int D>
 hipError_t launch_pingpong(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                            int H, int N, float scale, Mask mask, hipStream_t stream) {
   const int nqt = (N + 255) / 256;
   const long long grid = (long long)nqt * B * H;
-  hipLaunchKernelGGL((fwd_pingpong_kernel<D>), dim3((unsigned)grid), dim3(512), 0, stream,
-                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, B * H, N, nqt,
+  hipLaunchKernelGGL((fwd_pingpong_kernel<T, D>), dim3((unsigned)grid), dim3(512), 0, stream,
+                     (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, B * H, N, nqt,
                      fmaxf(fabsf(scale) * kLog2e, 1e-30f), scale < 0.f ? 1 : 0, mask.causal,
                      mask.window);
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t dispatch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                    int N, int d, float scale, Mask mask, int block_q, hipStream_t stream) {
+  if (d == 128) {
+    if (block_q == 256) return launch_pingpong<T, 128>(q, k, v, o, lse, B, H, N, scale, mask, stream);
+    if (block_q == 128) return launch<T, 128, 4>(q, k, v, o, lse, B, H, N, scale, mask, stream);
+    if (block_q == 64) return launch<T, 128, 2>(q, k, v, o, lse, B, H, N, scale, mask, stream);
+    return launch<T, 128, 1>(q, k, v, o, lse, B, H, N, scale, mask, stream);
+  }
+  if (block_q == 256) return launch_pingpong<T, 64>(q, k, v, o, lse, B, H, N, scale, mask, stream);
+  if (block_q == 128) return launch<T, 64, 4>(q, k, v, o, lse, B, H, N, scale, mask, stream);
+  if (block_q == 64) return launch<T, 64, 2>(q, k, v, o, lse, B, H, N, scale, mask, stream);
+  return launch<T, 64, 1>(q, k, v, o, lse, B, H, N, scale, mask, stream);
+}
+
 }  // namespace
 
-hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int H, int N, int d, float scale, Mask mask, int block_q,
-                           hipStream_t stream) {
-  if (d == 128) {
-    if (block_q == 256) return launch_pingpong<128>(q, k, v, o, lse, B, H, N, scale, mask, stream);
-    if (block_q == 128) return launch<128, 4>(q, k, v, o, lse, B, H, N, scale, mask, stream);
-    if (block_q == 64) return launch<128, 2>(q, k, v, o, lse, B, H, N, scale, mask, stream);
-    return launch<128, 1>(q, k, v, o, lse, B, H, N, scale, mask, stream);
-  }
-  if (block_q == 256) return launch_pingpong<64>(q, k, v, o, lse, B, H, N, scale, mask, stream);
-  if (block_q == 128) return launch<64, 4>(q, k, v, o, lse, B, H, N, scale, mask, stream);
-  if (block_q == 64) return launch<64, 2>(q, k, v, o, lse, B, H, N, scale, mask, stream);
-  return launch<64, 1>(q, k, v, o, lse, B, H, N, scale, mask, stream);
+                           bool f16, hipStream_t stream) {
+  if (f16) return dispatch<fa::f16>(q, k, v, o, lse, B, H, N, d, scale, mask, block_q, stream);
+  return dispatch<bf16>(q, k, v, o, lse, B, H, N, d, scale, mask, block_q, stream);
 }
 
 }  // namespace fa

@@ -18,9 +18,9 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa355.so")
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
-FA_FP32, FA_BF16 = 0, 1
+FA_FP32, FA_BF16, FA_FP16 = 0, 1, 2
 
-_DTYPE = {torch.float32: FA_FP32, torch.bfloat16: FA_BF16}
+_DTYPE = {torch.float32: FA_FP32, torch.bfloat16: FA_BF16, torch.float16: FA_FP16}
 
 _lib = None
 
@@ -100,7 +100,7 @@ def _default_scale(scale, d):
 
 def fa_fwd_ex(q, k, v, block_q: int = 0, block_k: int = 0, *, causal: bool = False,
               window: int = -1, scale=None, o=None, lse=None, stream=None):
-    """Forward pass; q, k, v: [B, H, N, d] GPU tensors (bf16 or fp32).
+    """Forward pass; q, k, v: [B, H, N, d] GPU tensors (bf16, fp16 or fp32).
     Returns (o [B,H,N,d] in the input dtype, lse [B,H,N] float32)."""
     B, H, N, d = q.shape
     dt = q.dtype

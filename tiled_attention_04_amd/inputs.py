@@ -9,8 +9,8 @@ test says otherwise):
 
 * dense attention: Q, then K, then V (then dO for the backward), each drawn
   as ``standard_normal(shape, dtype=float32)`` with shape [B, H, N, d] and
-  rounded to bf16 with round-to-nearest-even (torch's conversion) when the
-  workload is bf16;
+  rounded to bf16 (or fp16) with round-to-nearest-even (torch's
+  conversion) when the workload is 16-bit;
 * decode: the cache lengths first (``integers(lo, hi, endpoint=True)``), then
   the new queries [S, H, d], then for every sequence s in order its K rows
   [H, n_s, d] and its V rows [H, n_s, d].  Cache rows at or past n_s are not
@@ -37,7 +37,7 @@ WORKLOADS = {
     "bwd_b2_h16_n4096_d128_bf16": dict(B=2, H=16, N=4096, d=128, dtype="bf16"),
 }
 
-_TORCH_DTYPE = {"fp32": torch.float32, "bf16": torch.bfloat16}
+_TORCH_DTYPE = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}
 
 
 def torch_dtype(name: str) -> torch.dtype:
