@@ -64,7 +64,10 @@ def measured_traffic(kernel):
             rec = json.load(f).get(kernel)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("sources_sha256") != source_digest(rec["sources"]):
+    try:
+        if not rec or rec.get("sources_sha256") != source_digest(rec["sources"]):
+            return None
+    except OSError:  # a source was renamed or removed since
         return None
     return rec["bytes_per_launch"]
 

@@ -102,6 +102,47 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float*
                     fa_dtype dtype, void* stream, int block_q, int block_k);
 
 /*
+ * fa_fwd_tune -- measure the forward's tile shapes on this problem and let
+ * later automatic calls use the fastest.
+ *
+ * The tile shape chosen from measurement rather than fixed is the
+ * "profiling-driven auto-tuning" upgrade of "Build a FlashAttention-2
+ * Inference Kernel from Scratch in Pure Python", Extending It (there from
+ * hardware counters; here from the HIP event timestamps of each candidate).
+ * The NumPy page's roadmap (Extending It) asks for tile sizes justified by
+ * the on-chip memory: every candidate fits gfx950's 160 KB of LDS.
+ *
+ * For each block_q in {32, 64, 128, 256} (block_k = 64) the forward runs
+ * once to warm up and `reps` more times between two HIP events on
+ * `stream`; the mean time per call goes to times_ms[i] (if non-NULL, 4
+ * floats, candidate order as above) and the fastest block_q to
+ * *best_block_q (if non-NULL).  That choice is remembered for the process
+ * under the key (dtype, d, causal, window, B*H, N): fa_fwd (and fa_fwd_ex
+ * with block_q = 0) then uses it instead of the built-in heuristic.  On
+ * return o and lse hold the chosen tile's result for these inputs.
+ *
+ * Unlike every other call this one SYNCHRONISES `stream` and creates two
+ * HIP events (released before it returns); it is meant for set-up, not the
+ * hot loop.  The remembered table is guarded by a mutex.
+ *
+ * Arguments as fa_fwd, plus reps in [1, 1000].  FA_FP32: FA_ERR_UNSUPPORTED.
+ */
+fa_status fa_fwd_tune(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int N, int d, float scale, int causal, int window,
+                      fa_dtype dtype, void* stream, int reps, int* best_block_q, float* times_ms);
+
+/*
+ * The block_q an automatic fa_fwd call uses for this problem: the one
+ * fa_fwd_tune remembered (then *tuned = 1, if tuned is non-NULL), else the
+ * built-in heuristic's (*tuned = 0).  Returns 0 for invalid arguments.
+ */
+int fa_fwd_auto_block_q(int B, int H, int N, int d, int causal, int window, fa_dtype dtype,
+                        int* tuned);
+
+/* Forget every remembered tile choice (automatic calls use the heuristic again). */
+void fa_tune_reset(void);
+
+/*
  * fa_decode_workspace_size -- bytes of workspace fa_decode needs for these
  * sizes and this split length (chunk = 0 means the automatic choice).
  * Returns 0 for invalid sizes.

@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from tiled_attention_04_amd import build as fa_build
 from tiled_attention_04_amd import fa355
@@ -29,7 +30,7 @@ def declared_functions():
 
 def test_header_declares_the_expected_calls():
     names = declared_functions()
-    for must in ("fa_fwd", "fa_fwd_ex", "fa_decode", "fa_decode_paged", "fa_bwd", "fa_decode_workspace_size",
+    for must in ("fa_fwd", "fa_fwd_ex", "fa_fwd_tune", "fa_decode", "fa_decode_paged", "fa_bwd", "fa_decode_workspace_size",
                  "fa_bwd_workspace_size", "fa_status_str", "fa_last_error", "fa_version"):
         assert must in names
 
@@ -89,6 +90,28 @@ def test_decode_rejects_bad_arguments(lib):
     assert call(ws=None) == 3
     assert call(wsb=16) == 3
     assert "workspace" in fa355.last_error()
+
+
+def test_tune_rejects_bad_arguments_and_starts_empty(lib):
+    def call(**kw):
+        a = dict(q=FAKE, B=1, H=2, N=64, d=128, scale=0.1, causal=1, window=-1, dtype=1, reps=5)
+        a.update(kw)
+        return lib.fa_fwd_tune(a["q"], FAKE, FAKE, FAKE, None, a["B"], a["H"], a["N"], a["d"], a["scale"],
+                               a["causal"], a["window"], a["dtype"], None, a["reps"], None, None)
+    assert call(q=None) == 1
+    assert call(N=0) == 1
+    assert call(reps=0) == 1
+    assert call(reps=1001) == 1
+    assert call(window=-3) == 1
+    assert call(dtype=0) == 2
+    assert call(d=96) == 2
+    lib.fa_tune_reset()
+    # nothing tuned: the heuristic (256 rows only when the grid fills 256 CUs)
+    assert fa355.fa_fwd_auto_block_q(1, 2, 64, 128, causal=True) == (32, False)
+    assert fa355.fa_fwd_auto_block_q(4, 32, 4096, 128, causal=True) == (256, False)
+    assert fa355.fa_fwd_auto_block_q(4, 32, 4096, 128, causal=True, window=1024) == (128, False)
+    assert fa355.fa_fwd_auto_block_q(1, 1, 8, 4, dtype=torch.float32) == (64, False)
+    assert fa355.fa_fwd_auto_block_q(0, 1, 8, 4)[0] == 0
 
 
 def test_decode_paged_rejects_bad_arguments(lib):

@@ -10,6 +10,7 @@ from .fa355 import (  # noqa: F401
     FA_BF16,
     FA_FP16,
     FA_FP32,
+    TUNE_CANDIDATES,
     FaError,
     fa_bwd,
     fa_bwd_workspace_size,
@@ -18,6 +19,9 @@ from .fa355 import (  # noqa: F401
     fa_decode_workspace_size,
     fa_fwd,
     fa_fwd_ex,
+    fa_fwd_tune,
+    fa_fwd_auto_block_q,
+    fa_tune_reset,
     last_error,
     lib,
     status_str,

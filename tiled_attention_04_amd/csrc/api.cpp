@@ -9,6 +9,9 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <map>
+#include <mutex>
+#include <tuple>
 
 #include "fa_launch.h"
 
@@ -69,6 +72,25 @@ int auto_block_q(int B, int H, int N, int window) {
   return 32;
 }
 
+// Tile choices measured by fa_fwd_tune, by problem: automatic calls with
+// the same (dtype, d, causal, window, B*H, N) use them instead of the
+// heuristic above.
+using TuneKey = std::tuple<int, int, int, int, long long, int>;
+std::mutex g_tune_mu;
+std::map<TuneKey, int> g_tuned;
+
+TuneKey tune_key(fa_dtype dtype, int d, int causal, int window, int B, int H, int N) {
+  return TuneKey{(int)dtype, d, causal, window, (long long)B * H, N};
+}
+
+int tuned_block_q(const TuneKey& key) {
+  std::lock_guard<std::mutex> lock(g_tune_mu);
+  auto it = g_tuned.find(key);
+  return it == g_tuned.end() ? 0 : it->second;
+}
+
+constexpr int kTuneCandidates[4] = {32, 64, 128, 256};
+
 }  // namespace
 
 extern "C" {
@@ -108,6 +130,7 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float*
   }
   if (d != 64 && d != 128)
     return fail(FA_ERR_UNSUPPORTED, "%s forward supports d in {64, 128} (got %d)", dtype_name(dtype), d);
+  if (block_q == 0) block_q = tuned_block_q(tune_key(dtype, d, causal, window, B, H, N));
   if (block_q == 0) block_q = auto_block_q(B, H, N, window);
   if (block_k == 0) block_k = 64;
   if ((block_q != 32 && block_q != 64 && block_q != 128 && block_q != 256) || block_k != 64)
@@ -122,6 +145,81 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float*
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                  int N, int d, float scale, int causal, int window, fa_dtype dtype, void* stream) {
   return fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, window, dtype, stream, 0, 0);
+}
+
+fa_status fa_fwd_tune(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                      int N, int d, float scale, int causal, int window, fa_dtype dtype, void* stream,
+                      int reps, int* best_block_q, float* times_ms) {
+  if (!q || !k || !v || !o) return fail(FA_ERR_INVALID_ARG, "q, k, v and o must be non-null");
+  fa_status st = check_dense(B, H, N, d, scale, causal, window, dtype);
+  if (st != FA_OK) return st;
+  if (dtype == FA_FP32) return fail(FA_ERR_UNSUPPORTED, "tuning covers the 16-bit forward only");
+  if (d != 64 && d != 128)
+    return fail(FA_ERR_UNSUPPORTED, "%s forward supports d in {64, 128} (got %d)", dtype_name(dtype), d);
+  if (reps < 1 || reps > 1000) return fail(FA_ERR_INVALID_ARG, "reps must be 1..1000 (got %d)", reps);
+  for (int bq : kTuneCandidates) {  // every candidate's grid must be launchable
+    const long long wgs = (long long)B * H * ((N + bq - 1) / bq);
+    if (wgs * 2 * bq > kMaxThreadsPerLaunch) return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  }
+  const hipStream_t s = (hipStream_t)stream;
+  const fa::Mask mask{causal, window};
+  const bool f16 = dtype == FA_FP16;
+  hipEvent_t ev[2];
+  hipError_t err = hipEventCreate(&ev[0]);
+  if (err != hipSuccess) return done(err, "fa_fwd_tune (event)");
+  err = hipEventCreate(&ev[1]);
+  if (err != hipSuccess) {
+    (void)hipEventDestroy(ev[0]);
+    return done(err, "fa_fwd_tune (event)");
+  }
+  float best_ms = 0.f;
+  int best = 0;
+  for (int i = 0; i < 4 && err == hipSuccess; ++i) {
+    const int bq = kTuneCandidates[i];
+    err = fa::launch_fwd_mfma(q, k, v, o, lse, B, H, N, d, scale, mask, bq, f16, s);  // warm-up
+    if (err == hipSuccess) err = hipEventRecord(ev[0], s);
+    for (int r = 0; r < reps && err == hipSuccess; ++r)
+      err = fa::launch_fwd_mfma(q, k, v, o, lse, B, H, N, d, scale, mask, bq, f16, s);
+    if (err == hipSuccess) err = hipEventRecord(ev[1], s);
+    if (err == hipSuccess) err = hipEventSynchronize(ev[1]);
+    float ms = 0.f;
+    if (err == hipSuccess) err = hipEventElapsedTime(&ms, ev[0], ev[1]);
+    ms /= (float)reps;
+    if (times_ms) times_ms[i] = ms;
+    if (err == hipSuccess && (best == 0 || ms < best_ms)) {
+      best = bq;
+      best_ms = ms;
+    }
+  }
+  (void)hipEventDestroy(ev[0]);
+  (void)hipEventDestroy(ev[1]);
+  if (err != hipSuccess) return done(err, "fa_fwd_tune");
+  {
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    g_tuned[tune_key(dtype, d, causal, window, B, H, N)] = best;
+  }
+  if (best_block_q) *best_block_q = best;
+  // Leave o and lse holding the chosen tile's result.
+  return done(fa::launch_fwd_mfma(q, k, v, o, lse, B, H, N, d, scale, mask, best, f16, s),
+              "fa_fwd_tune");
+}
+
+int fa_fwd_auto_block_q(int B, int H, int N, int d, int causal, int window, fa_dtype dtype,
+                        int* tuned) {
+  if (tuned) *tuned = 0;
+  if (check_dense(B, H, N, d, 0.f, causal, window, dtype) != FA_OK) return 0;
+  if (dtype == FA_FP32) return 64;
+  const int t = tuned_block_q(tune_key(dtype, d, causal, window, B, H, N));
+  if (t != 0) {
+    if (tuned) *tuned = 1;
+    return t;
+  }
+  return auto_block_q(B, H, N, window);
+}
+
+void fa_tune_reset(void) {
+  std::lock_guard<std::mutex> lock(g_tune_mu);
+  g_tuned.clear();
 }
 
 size_t fa_decode_workspace_size(int S, int H, int Lmax, int d, int chunk) {

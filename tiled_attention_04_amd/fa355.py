@@ -32,6 +32,9 @@ SIGNATURES = {
     "fa_last_error": (ctypes.c_char_p, []),
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
     "fa_fwd_ex": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P, _I, _I]),
+    "fa_fwd_tune": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P, _I, _P, _P]),
+    "fa_fwd_auto_block_q": (_I, [_I, _I, _I, _I, _I, _I, _I, _P]),
+    "fa_tune_reset": (None, []),
     "fa_decode_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
     "fa_decode": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _I, _P]),
     "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _Z,
@@ -125,6 +128,48 @@ def fa_fwd(q, k, v, *, causal: bool = False, window: int = -1, scale=None, o=Non
     """Forward pass with the library's automatic tile choice."""
     return fa_fwd_ex(q, k, v, 0, 0, causal=causal, window=window, scale=scale, o=o, lse=lse,
                      stream=stream)
+
+
+TUNE_CANDIDATES = (32, 64, 128, 256)
+
+
+def fa_fwd_tune(q, k, v, *, causal: bool = False, window: int = -1, scale=None, reps: int = 10,
+                o=None, lse=None, stream=None):
+    """Time every query-tile size of the 16-bit forward on these inputs and
+    remember the fastest for later automatic calls (synchronises the stream).
+    Returns (best block_q, {block_q: mean ms per call}, o, lse)."""
+    B, H, N, d = q.shape
+    dt = q.dtype
+    if dt not in _DTYPE:
+        raise ValueError(f"unsupported dtype {dt}")
+    qp = _dev(q, "q", dt)
+    kp = _dev(k, "k", dt, q.shape)
+    vp = _dev(v, "v", dt, q.shape)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    op = _dev(o, "o", dt, q.shape)
+    lp = _dev(lse, "lse", torch.float32, (B, H, N))
+    best = ctypes.c_int(0)
+    times = (ctypes.c_float * 4)()
+    _check(lib().fa_fwd_tune(qp, kp, vp, op, lp, B, H, N, d, _default_scale(scale, d), int(causal),
+                             int(window), _DTYPE[dt], _stream(stream), int(reps), ctypes.byref(best),
+                             times))
+    return best.value, dict(zip(TUNE_CANDIDATES, list(times))), o, lse
+
+
+def fa_fwd_auto_block_q(B: int, H: int, N: int, d: int, *, causal: bool = False, window: int = -1,
+                        dtype=torch.bfloat16):
+    """(block_q an automatic fa_fwd call uses, whether it was tuned)."""
+    tuned = ctypes.c_int(0)
+    bq = lib().fa_fwd_auto_block_q(B, H, N, d, int(causal), int(window), _DTYPE[dtype],
+                                   ctypes.byref(tuned))
+    return int(bq), bool(tuned.value)
+
+
+def fa_tune_reset() -> None:
+    lib().fa_tune_reset()
 
 
 def fa_decode_workspace_size(S: int, H: int, Lmax: int, d: int, chunk: int = 0) -> int:
