@@ -68,6 +68,8 @@ def fwd(lib, q=FAKE, B=1, H=1, N=8, d=64, scale=0.125, causal=0, window=-1, dtyp
     (dict(dtype=2, bq=48), 1),
     (dict(bq=48), 1), (dict(bq=512), 1), (dict(bk=32), 1), (dict(dtype=0, bq=65, bk=4), 1), (dict(dtype=0, bq=0, bk=5), 1),
     (dict(B=1 << 16, H=1 << 16), 1),
+    (dict(N=1 << 23, d=128), 2),          # one slice of N*d bf16 above 2 GiB
+    (dict(N=1 << 22, d=128, dtype=0), 2),  # the same in float32
 ])
 def test_fwd_rejects_bad_arguments(lib, kw, status):
     assert fwd(lib, **kw) == status

@@ -200,3 +200,29 @@ def test_full_size_scale_zero_property(llama_layer, window):
     diff = o.double() - mean
     assert diff.abs().max().item() <= 2e-2
     assert (diff.norm() / mean.norm()).item() <= 1e-2
+
+
+# ------------------------------------------------ long sequences, one head
+
+@pytest.mark.parametrize("causal,window", [(True, -1), (True, 3000), (False, -1)])
+def test_long_sequence_sampled_rows(causal, window):
+    """N = 65536 in one (batch, head): the 256-row kernel's key loop runs 1024
+    tiles and the offsets inside the slice reach 16 MiB.  Sampled rows, each
+    computed on its own by the oracle."""
+    N, d = 65536, 128
+    q, k, v = attention_inputs(1, 1, N, d, "bf16", seed=12)
+    o, lse = run(q, k, v, causal, window, bq=256)
+    rows = [0, 1, 255, 256, 4095, 30001, 65534, 65535]
+    O, L = oracle.attention_rows_ref(q[0, 0], k[0, 0], v[0, 0], 1 / math.sqrt(d), rows, causal, window)
+    check_bf16(o[0, 0, rows], O, "O rows")
+    check_lse(lse[0, 0, rows], L, "L rows")
+
+
+def test_heads_not_multiple_of_eight_use_plain_order():
+    """B*H = 13: the XCD-aware tile order falls back to the plain one."""
+    q, k, v = attention_inputs(1, 13, 600, 64, "bf16", seed=13)
+    for bq in (128, 256):
+        o, lse = run(q, k, v, True, -1, bq=bq)
+        O, L = oracle.attention_ref(q, k, v, 1 / 8, True)
+        check_bf16(o, O, "O")
+        check_lse(lse, L, "L")
