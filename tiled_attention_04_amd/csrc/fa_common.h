@@ -166,17 +166,19 @@ __device__ __forceinline__ float pair_sum(float x) {
 // Workgroup id -> (head slice bh, tile rank r) for a grid of BH * ntiles
 // workgroups; rank 0 is dispatched first.  Consecutive ids go round-robin
 // over the 8 XCDs of the chip and, when BH is a multiple of 8, every head
-// stays on one XCD (its K/V are shared in that XCD's L2).  Two orders:
+// stays on one XCD (its K/V are shared in that XCD's L2).  Each XCD walks
+// its heads in groups, all ranks of a group before the next group, so only
+// the group's heads are live in its L2:
 //  * spread (for plain causal attention, where rank 0 is the most expensive
-//    tile and the cost falls with the rank): all heads rank by rank, so the
-//    last workgroups to start are the cheapest ones and the tail stays short;
-//  * grouped (work about the same for every tile): each XCD walks its heads
-//    in groups of two, all ranks of a group before the next group, so only a
-//    few heads are live per XCD and their K/V stay in its L2.
+//    tile and the cost falls with the rank): groups of four heads, rank by
+//    rank inside a group, so every group ends with its cheapest tiles and
+//    the tail stays short (measured 2-3% faster than one group of all
+//    heads, whose K/V leave the L2 between ranks, and than groups of two);
+//  * grouped (work about the same for every tile): groups of two heads.
 __device__ __forceinline__ void tile_order(int id, int BH, int ntiles, bool spread, int& bh, int& r) {
   if ((BH & 7) == 0) {
     const int xcd = id & 7, slot = id >> 3, nbh8 = BH >> 3;
-    const int G = spread ? nbh8 : 2;  // heads per group and XCD
+    const int G = spread ? (nbh8 < 4 ? nbh8 : 4) : 2;  // heads per group and XCD
     const int full = nbh8 / G;        // groups of G heads; a last group may hold fewer
     int grp, hh;
     if (slot < full * G * ntiles) {
