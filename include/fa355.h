@@ -236,7 +236,10 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d);
  *   workspace      : >= fa_bwd_workspace_size(B, H, N, d) bytes
  *
  * Supported: FA_BF16 and FA_FP16 with d in {64, 128}.  No atomics: dq, dk and dv are
- * each written once, so repeated calls give identical bits.
+ * each written once, so repeated calls give identical bits.  P and dS are
+ * rounded to the input type for the products that use them (fp32
+ * accumulation): with FA_FP16 a |dP - D| above 65504 overflows, as for
+ * any fp16 operand.
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
                  const float* lse, float* dq, float* dk, float* dv,
