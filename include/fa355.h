@@ -82,7 +82,7 @@ const char* fa_last_error(void);
  *   causal  : 0 or 1;  window : -1 (off) or >= 0
  *
  * Supported: FA_BF16 and FA_FP16 with d in {64, 128} (MFMA kernels);
- * FA_FP32 with 1 <= d <= 128 (generic kernel).  Other d: FA_ERR_UNSUPPORTED.
+ * FA_FP32 with 1 <= d <= 256 (generic kernel).  Other d: FA_ERR_UNSUPPORTED.
  * Sizes: B*H <= 2^31-1 and B*H*N*d < 2^63; N need not be a tile multiple.
  */
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -93,7 +93,9 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
  * fa_fwd_ex -- fa_fwd with an explicit tile shape (0, 0 = automatic).
  *   FA_FP32: 1 <= block_q <= 64, 1 <= block_k <= 64 (any values, e.g. 4 x 4
  *            for the worked example "FlashAttention Algorithm > Worked
- *            Example", Setting Up the Example).
+ *            Example", Setting Up the Example), with block_q * d and
+ *            block_k * d <= 8192 and block_k * (d + 1) <= 8256; automatic: 64 x 64 for
+ *            d <= 128, 32 x 32 above.
  *   FA_BF16, FA_FP16: block_q in {32, 64, 128, 256}, block_k = 64.
  * Any other pair: FA_ERR_INVALID_ARG.
  */

@@ -64,7 +64,8 @@ def fwd(lib, q=FAKE, B=1, H=1, N=8, d=64, scale=0.125, causal=0, window=-1, dtyp
     (dict(q=None), 1), (dict(B=0), 1), (dict(N=-3), 1), (dict(d=0), 1),
     (dict(causal=2), 1), (dict(window=-2), 1), (dict(scale=float("inf")), 1),
     (dict(scale=float("nan")), 1), (dict(dtype=7), 1),
-    (dict(d=96), 2), (dict(d=256, dtype=0), 2), (dict(d=96, dtype=2), 2), (dict(dtype=3), 1),
+    (dict(d=96), 2), (dict(d=257, dtype=0), 2), (dict(d=256, dtype=0, bq=64, bk=32), 1),
+    (dict(d=256, dtype=0, bq=32, bk=64), 1), (dict(d=171, dtype=0, bq=32, bk=48), 1), (dict(d=96, dtype=2), 2), (dict(dtype=3), 1),
     (dict(dtype=2, bq=48), 1),
     (dict(bq=48), 1), (dict(bq=512), 1), (dict(bk=32), 1), (dict(dtype=0, bq=65, bk=4), 1), (dict(dtype=0, bq=0, bk=5), 1),
     (dict(B=1 << 16, H=1 << 16), 1),

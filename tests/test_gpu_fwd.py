@@ -65,6 +65,17 @@ def test_fp32_shape_and_block_matrix(N, d, bq, bk, causal, window):
     check_fp32(lse, L, "L")
 
 
+@pytest.mark.parametrize("d,bq,bk", [(256, 0, 0), (256, 32, 31), (200, 40, 17), (129, 63, 63)])
+@pytest.mark.parametrize("causal,window", [(False, -1), (True, -1), (True, 50)])
+def test_fp32_large_head_dims(d, bq, bk, causal, window):
+    """Head sizes above 128 on the float32 kernel (tiles sized to its LDS)."""
+    q, k, v = attention_inputs(1, 2, 150, d, "fp32", seed=d)
+    o, lse = run(q, k, v, causal, window, bq=bq, bk=bk)
+    O, L = oracle.attention_ref(q, k, v, 1 / math.sqrt(d), causal, window)
+    check_fp32(o, O, "O")
+    check_fp32(lse, L, "L")
+
+
 # ------------------------------------------------------------------ bf16 ---
 
 @pytest.mark.parametrize("causal", [False, True])

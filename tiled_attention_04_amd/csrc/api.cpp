@@ -118,10 +118,13 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float*
   if (st != FA_OK) return st;
   const fa::Mask mask{causal, window};
   if (dtype == FA_FP32) {
-    if (d > 128) return fail(FA_ERR_UNSUPPORTED, "float32 forward supports d <= 128 (got %d)", d);
-    if (block_q == 0 && block_k == 0) block_q = block_k = 64;
+    if (d > 256) return fail(FA_ERR_UNSUPPORTED, "float32 forward supports d <= 256 (got %d)", d);
+    if (block_q == 0 && block_k == 0) block_q = block_k = d <= 128 ? 64 : 32;
     if (block_q < 1 || block_q > 64 || block_k < 1 || block_k > 64)
       return fail(FA_ERR_INVALID_ARG, "float32 tiles must be 1..64 x 1..64 (got %d x %d)", block_q, block_k);
+    if (block_q * d > 8192 || block_k * d > 8192 || block_k * (d + 1) > 64 * 129)
+      return fail(FA_ERR_INVALID_ARG, "float32 tiles of %d x %d rows do not fit LDS at d = %d", block_q,
+                  block_k, d);
     const long long wgs = (long long)B * H * ((N + block_q - 1) / block_q);
     if (wgs * 256 > kMaxThreadsPerLaunch) return fail(FA_ERR_UNSUPPORTED, "grid too large");
     return done(fa::launch_fwd_fp32((const float*)q, (const float*)k, (const float*)v, (float*)o, lse,

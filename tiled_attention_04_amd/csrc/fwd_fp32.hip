@@ -1,6 +1,8 @@
-// Generic float32 forward: any head size d <= 128 and any tile shape up to
-// 64 x 64, including the 4 x 4 tiles of the worked example ("FlashAttention
-// Algorithm > Worked Example", Setting Up the Example).
+// Generic float32 forward: any head size d <= 256 and any tile shape up to
+// 64 x 64 whose tiles fit the LDS staging buffers (block_q * d and
+// block_k * d at most 8192 floats: 64 x 64 tiles up to d = 128, 32 x 32 up
+// to d = 256), including the 4 x 4 tiles of the worked example
+// ("FlashAttention Algorithm > Worked Example", Setting Up the Example).
 //
 // One workgroup owns one query tile and walks the key/value tiles the mask
 // leaves visible, keeping the running max m, running sum l and unnormalised
@@ -16,17 +18,18 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxTile = 64;
-constexpr int kMaxD = 128;
+constexpr int kTileFloats = 8192;            // Q, V and O tiles: block * d floats at most
+constexpr int kKFloats = kMaxTile * 129;     // K tile, rows padded by one float
 constexpr int kSPitch = kMaxTile + 1;
 
 __global__ __launch_bounds__(kThreads) void fwd_fp32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, float* __restrict__ lse, int N, int d, int BQ, int BK, int nqt,
     float scale, int causal, int window) {
-  __shared__ float Qs[kMaxTile * kMaxD];
-  __shared__ float Ks[kMaxTile * (kMaxD + 1)];
-  __shared__ float Vs[kMaxTile * kMaxD];
-  __shared__ float Os[kMaxTile * kMaxD];
+  __shared__ float Qs[kTileFloats];
+  __shared__ float Ks[kKFloats];
+  __shared__ float Vs[kTileFloats];
+  __shared__ float Os[kTileFloats];
   __shared__ float Ss[kMaxTile * kSPitch];
   __shared__ float m_row[kMaxTile], l_row[kMaxTile], a_row[kMaxTile];
 
