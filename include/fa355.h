@@ -145,6 +145,21 @@ int fa_fwd_auto_block_q(int B, int H, int N, int d, int causal, int window, fa_d
 void fa_tune_reset(void);
 
 /*
+ * Save / restore the remembered tile choices, so that a process can start
+ * with the choices an earlier one measured.  A row is 7 int64 values:
+ * (dtype, d, causal, window, B*H, N, block_q).
+ *
+ * fa_tune_export writes up to max_rows rows to `rows` (host memory, 7 *
+ * max_rows values) and returns the number of remembered choices (rows may
+ * be NULL to query it).  fa_tune_import adds or replaces n_rows choices;
+ * it checks every row first (16-bit dtype, d in {64, 128}, causal 0/1,
+ * window >= -1, positive sizes, block_q a tuning candidate) and changes
+ * nothing on FA_ERR_INVALID_ARG.
+ */
+int fa_tune_export(int64_t* rows, int max_rows);
+fa_status fa_tune_import(const int64_t* rows, int n_rows);
+
+/*
  * fa_decode_workspace_size -- bytes of workspace fa_decode needs for these
  * sizes and this split length (chunk = 0 means the automatic choice).
  * Returns 0 for invalid sizes.

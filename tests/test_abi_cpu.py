@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_header_declares_the_expected_calls():
     names = declared_functions()
-    for must in ("fa_fwd", "fa_fwd_ex", "fa_fwd_tune", "fa_decode", "fa_decode_paged", "fa_bwd", "fa_decode_workspace_size",
+    for must in ("fa_fwd", "fa_fwd_ex", "fa_fwd_tune", "fa_tune_export", "fa_tune_import", "fa_decode", "fa_decode_paged", "fa_bwd", "fa_decode_workspace_size",
                  "fa_bwd_workspace_size", "fa_status_str", "fa_last_error", "fa_version"):
         assert must in names
 
@@ -115,6 +115,30 @@ def test_tune_rejects_bad_arguments_and_starts_empty(lib):
     assert fa355.fa_fwd_auto_block_q(4, 32, 4096, 128, causal=True, window=1024) == (128, False)
     assert fa355.fa_fwd_auto_block_q(1, 1, 8, 4, dtype=torch.float32) == (64, False)
     assert fa355.fa_fwd_auto_block_q(0, 1, 8, 4)[0] == 0
+
+
+def test_tune_table_export_import_round_trip(tmp_path, lib):
+    """The remembered tile table is host state: it round-trips through
+    export/import and a JSON file, and a bad row changes nothing."""
+    lib.fa_tune_reset()
+    rows = [dict(dtype=1, d=128, causal=1, window=-1, BH=128, N=4096, block_q=256),
+            dict(dtype=2, d=64, causal=0, window=100, BH=8, N=1024, block_q=128)]
+    fa355.fa_tune_import(rows)
+    assert sorted(fa355.fa_tune_export(), key=str) == sorted(rows, key=str)
+    assert fa355.fa_fwd_auto_block_q(1, 8, 1024, 64, window=100, dtype=torch.float16) == (128, True)
+    assert fa355.fa_fwd_auto_block_q(4, 32, 4096, 128, causal=True) == (256, True)
+    path = str(tmp_path / "tune.json")
+    fa355.save_tuning(path)
+    lib.fa_tune_reset()
+    assert fa355.fa_tune_export() == []
+    fa355.load_tuning(path)
+    assert sorted(fa355.fa_tune_export(), key=str) == sorted(rows, key=str)
+    for bad in (dict(rows[0], block_q=96), dict(rows[0], dtype=0), dict(rows[0], d=80),
+                dict(rows[0], causal=2), dict(rows[0], window=-2), dict(rows[0], N=0)):
+        with pytest.raises(fa355.FaError):
+            fa355.fa_tune_import([rows[1] | {"N": 7}, bad])
+        assert len(fa355.fa_tune_export()) == 2  # unchanged
+    lib.fa_tune_reset()
 
 
 def test_decode_paged_rejects_bad_arguments(lib):

@@ -21,7 +21,11 @@ from .fa355 import (  # noqa: F401
     fa_fwd_ex,
     fa_fwd_tune,
     fa_fwd_auto_block_q,
+    fa_tune_export,
+    fa_tune_import,
     fa_tune_reset,
+    load_tuning,
+    save_tuning,
     last_error,
     lib,
     status_str,

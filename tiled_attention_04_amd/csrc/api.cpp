@@ -225,6 +225,46 @@ void fa_tune_reset(void) {
   g_tuned.clear();
 }
 
+int fa_tune_export(int64_t* rows, int max_rows) {
+  std::lock_guard<std::mutex> lock(g_tune_mu);
+  const int n = (int)g_tuned.size();
+  if (!rows || max_rows <= 0) return n;
+  int i = 0;
+  for (const auto& kv : g_tuned) {
+    if (i >= max_rows) break;
+    int64_t* r = rows + 7 * (size_t)i;
+    r[0] = std::get<0>(kv.first);  // dtype
+    r[1] = std::get<1>(kv.first);  // d
+    r[2] = std::get<2>(kv.first);  // causal
+    r[3] = std::get<3>(kv.first);  // window
+    r[4] = std::get<4>(kv.first);  // B * H
+    r[5] = std::get<5>(kv.first);  // N
+    r[6] = kv.second;              // block_q
+    ++i;
+  }
+  return n;
+}
+
+fa_status fa_tune_import(const int64_t* rows, int n_rows) {
+  if (n_rows < 0 || (n_rows > 0 && !rows)) return fail(FA_ERR_INVALID_ARG, "rows must hold n_rows >= 0 rows");
+  for (int i = 0; i < n_rows; ++i) {  // validate everything before changing the table
+    const int64_t* r = rows + 7 * (size_t)i;
+    bool ok_bq = false;
+    for (int bq : kTuneCandidates) ok_bq |= r[6] == bq;
+    if ((r[0] != FA_BF16 && r[0] != FA_FP16) || (r[1] != 64 && r[1] != 128) || (r[2] != 0 && r[2] != 1) ||
+        r[3] < -1 || r[3] > INT_MAX || r[4] <= 0 || r[4] > INT_MAX || r[5] <= 0 || r[5] > INT_MAX || !ok_bq)
+      return fail(FA_ERR_INVALID_ARG, "tuning row %d is not a valid (dtype, d, causal, window, B*H, N, "
+                  "block_q) entry", i);
+  }
+  std::lock_guard<std::mutex> lock(g_tune_mu);
+  for (int i = 0; i < n_rows; ++i) {
+    const int64_t* r = rows + 7 * (size_t)i;
+    g_tuned[TuneKey{(int)r[0], (int)r[1], (int)r[2], (int)r[3], r[4], (int)r[5]}] = (int)r[6];
+  }
+  g_err[0] = '\0';
+  return FA_OK;
+}
+
 size_t fa_decode_workspace_size(int S, int H, int Lmax, int d, int chunk) {
   if (S <= 0 || H <= 0 || Lmax <= 0 || d <= 0 || chunk < 0 || chunk % 64 != 0) return 0;
   if (chunk == 0) chunk = fa::decode_auto_chunk(S, H, Lmax);

@@ -35,6 +35,8 @@ SIGNATURES = {
     "fa_fwd_tune": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P, _I, _P, _P]),
     "fa_fwd_auto_block_q": (_I, [_I, _I, _I, _I, _I, _I, _I, _P]),
     "fa_tune_reset": (None, []),
+    "fa_tune_export": (_I, [_P, _I]),
+    "fa_tune_import": (_I, [_P, _I]),
     "fa_decode_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
     "fa_decode": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _I, _P]),
     "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _Z,
@@ -170,6 +172,41 @@ def fa_fwd_auto_block_q(B: int, H: int, N: int, d: int, *, causal: bool = False,
 
 def fa_tune_reset() -> None:
     lib().fa_tune_reset()
+
+
+TUNE_FIELDS = ("dtype", "d", "causal", "window", "BH", "N", "block_q")
+
+
+def fa_tune_export() -> list:
+    """The remembered tile choices as dicts with the keys of TUNE_FIELDS."""
+    n = int(lib().fa_tune_export(None, 0))
+    buf = (ctypes.c_int64 * (7 * max(n, 1)))()
+    n = min(n, int(lib().fa_tune_export(buf, n)))
+    return [dict(zip(TUNE_FIELDS, buf[7 * i:7 * i + 7])) for i in range(n)]
+
+
+def fa_tune_import(entries) -> None:
+    """Add tile choices (dicts as returned by fa_tune_export)."""
+    entries = list(entries)
+    buf = (ctypes.c_int64 * (7 * max(len(entries), 1)))()
+    for i, e in enumerate(entries):
+        for j, f in enumerate(TUNE_FIELDS):
+            buf[7 * i + j] = int(e[f])
+    _check(lib().fa_tune_import(buf, len(entries)))
+
+
+def save_tuning(path: str) -> None:
+    """Write the remembered tile choices to a JSON file."""
+    import json
+    with open(path, "w") as f:
+        json.dump(fa_tune_export(), f, indent=1)
+
+
+def load_tuning(path: str) -> None:
+    """Load tile choices written by save_tuning."""
+    import json
+    with open(path) as f:
+        fa_tune_import(json.load(f))
 
 
 def fa_decode_workspace_size(S: int, H: int, Lmax: int, d: int, chunk: int = 0) -> int:
