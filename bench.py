@@ -8,6 +8,8 @@ batch (already resident in HBM when timing starts):
   4. causal backward,           B=2, H=16, N=4096, d=128, bf16 (from the forward's O and L)
   5. paged KV-cache decode,     the decode batch of 3 in 64-token pages scattered over a pool
   6. causal forward in fp16,    the shape of 1 with fp16 inputs (same seeds)
+  7. windowed decode,           the decode batch of 3 with a 1024-token sliding window
+  8. windowed backward,         the backward of 4 with a 1024-token sliding window
 
 The headline value is the causal forward's TFLOP/s (4*B*H*N^2*d/2 algorithmic
 flops per launch over its measured time); every stage is timed with HIP events
@@ -34,6 +36,10 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# Stages of one step, in the order they run.
+STAGES = ("fwd", "window", "decode", "bwd", "paged", "fwd16", "decw", "bwdw")
+W_DEC = 1024   # sliding window of the windowed decode stage
+W_BWD = 1024   # sliding window of the windowed backward stage
 
 
 def log(msg):
@@ -101,7 +107,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--stages", default="fwd,window,decode,bwd,paged,fwd16")
+    ap.add_argument("--stages", default=",".join(STAGES))
     ap.add_argument("--page-size", type=int, default=64)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, copy 1 GiB device-to-device three times: the reference "
@@ -139,7 +145,7 @@ def main():
         l7 = torch.empty_like(l3)
 
     w4 = WORKLOADS["decode_s64_h32_d128_len512to8192_bf16"]
-    if "decode" in stages or "paged" in stages:
+    if "decode" in stages or "paged" in stages or "decw" in stages:
         log("generating decode inputs (ragged KV cache)")
         inp4 = decode_inputs(w4["S"], w4["H"], w4["d"], w4["len_lo"], w4["len_hi"], seed=0)
         q4 = inp4.q.to(dev)
@@ -147,7 +153,10 @@ def main():
         o4 = torch.empty_like(q4)
         l4 = torch.empty(q4.shape[:2], dtype=torch.float32, device=dev)
         dec_bytes = inp4.valid_bytes(2) + 2 * q4.numel() * 2
-    if "decode" in stages:
+        # with a window the query reads only the last W+1 rows of each cache
+        seen = np.minimum(inp4.seqlens.astype(np.int64), W_DEC + 1)
+        decw_bytes = int(seen.sum()) * w4["H"] * w4["d"] * 2 * 2 + 2 * q4.numel() * 2
+    if "decode" in stages or "decw" in stages:
         kc4, vc4 = dense_cache(inp4, w4["Lmax"], device=dev)
         ws4 = torch.empty(fa.fa_decode_workspace_size(w4["S"], w4["H"], w4["Lmax"], w4["d"]),
                           dtype=torch.uint8, device=dev)
@@ -158,7 +167,7 @@ def main():
         l6 = torch.empty_like(l4)
         ws6 = torch.empty(fa.fa_decode_workspace_size(w4["S"], w4["H"], tb6.shape[1] * args.page_size,
                                                       w4["d"]), dtype=torch.uint8, device=dev)
-    if "decode" in stages or "paged" in stages:
+    if "decode" in stages or "paged" in stages or "decw" in stages:
         del inp4
 
     w5 = WORKLOADS["bwd_b2_h16_n4096_d128_bf16"]
@@ -170,34 +179,41 @@ def main():
         dq5, dk5, dv5 = (torch.empty(q5.shape, dtype=torch.float32, device=dev) for _ in range(3))
         ws5 = torch.empty(fa.fa_bwd_workspace_size(B5, H5, N5, d5), dtype=torch.uint8, device=dev)
 
-    # ---- one step -----------------------------------------------------------
+    if "bwdw" in stages:
+        if "bwd" not in stages:
+            q5, k5, v5, g5 = (t.to(dev) for t in attention_inputs(B5, H5, N5, d5, "bf16", seed=0,
+                                                                  with_grad=True))
+            dq5, dk5, dv5 = (torch.empty(q5.shape, dtype=torch.float32, device=dev) for _ in range(3))
+            ws5 = torch.empty(fa.fa_bwd_workspace_size(B5, H5, N5, d5), dtype=torch.uint8, device=dev)
+        o5w, l5w = fa.fa_fwd(q5, k5, v5, causal=True, window=W_BWD)
+
+    # ---- one step: every stage once, each bracketed by events -------------------
     flops3 = 4.0 * B3 * H3 * N3 * N3 * d3 / 2
     flops3w = 4.0 * d3 * B3 * H3 * window_pairs(N3, w3["window"])
     flops5 = 10.0 * B5 * H5 * N5 * N5 * d5 / 2
+    flops5w = 10.0 * d5 * B5 * H5 * window_pairs(N5, W_BWD)
+
+    calls = {
+        "fwd": lambda: fa.fa_fwd(q3, k3, v3, causal=True, o=o3, lse=l3),
+        "window": lambda: fa.fa_fwd(q3, k3, v3, causal=True, window=w3["window"], o=o3w, lse=l3w),
+        "decode": lambda: fa.fa_decode(q4, kc4, vc4, sl4, o=o4, lse=l4, workspace=ws4),
+        "bwd": lambda: fa.fa_bwd(q5, k5, v5, o5, g5, l5, causal=True, dq=dq5, dk=dk5, dv=dv5,
+                                 workspace=ws5),
+        "paged": lambda: fa.fa_decode_paged(q4, kp6, vp6, tb6, sl4, o=o6, lse=l6, workspace=ws6),
+        "fwd16": lambda: fa.fa_fwd(q7, k7, v7, causal=True, o=o7, lse=l7),
+        "decw": lambda: fa.fa_decode(q4, kc4, vc4, sl4, window=W_DEC, o=o4, lse=l4, workspace=ws4),
+        "bwdw": lambda: fa.fa_bwd(q5, k5, v5, o5w, g5, l5w, causal=True, window=W_BWD, dq=dq5, dk=dk5,
+                                  dv=dv5, workspace=ws5),
+    }
+    run = [n for n in STAGES if n in stages]
 
     def step(ev=None):
-        def mark(i):
+        for i, n in enumerate(run):
             if ev is not None:
                 ev[i].record()
-        mark(0)
-        if "fwd" in stages:
-            fa.fa_fwd(q3, k3, v3, causal=True, o=o3, lse=l3)
-        mark(1)
-        if "window" in stages:
-            fa.fa_fwd(q3, k3, v3, causal=True, window=w3["window"], o=o3w, lse=l3w)
-        mark(2)
-        if "decode" in stages:
-            fa.fa_decode(q4, kc4, vc4, sl4, o=o4, lse=l4, workspace=ws4)
-        mark(3)
-        if "bwd" in stages:
-            fa.fa_bwd(q5, k5, v5, o5, g5, l5, causal=True, dq=dq5, dk=dk5, dv=dv5, workspace=ws5)
-        mark(4)
-        if "paged" in stages:
-            fa.fa_decode_paged(q4, kp6, vp6, tb6, sl4, o=o6, lse=l6, workspace=ws6)
-        mark(5)
-        if "fwd16" in stages:
-            fa.fa_fwd(q7, k7, v7, causal=True, o=o7, lse=l7)
-        mark(6)
+            calls[n]()
+        if ev is not None:
+            ev[len(run)].record()
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -205,17 +221,17 @@ def main():
     torch.cuda.synchronize()
 
     log(f"timing {args.steps} steps")
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(run) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    comp = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(6)]
+    comp = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(len(run))]
                      for i in range(args.steps)])  # ms
-    ms = comp.mean(axis=0)
-    log("stage ms (mean): " + ", ".join(f"{n}={m:.4f}" for n, m in zip(("fwd", "window", "decode", "bwd", "paged", "fwd16"), ms)))
+    ms = dict(zip(run, comp.mean(axis=0)))
+    log("stage ms (mean): " + ", ".join(f"{n}={m:.4f}" for n, m in ms.items()))
 
     components = {}
 
@@ -227,28 +243,30 @@ def main():
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                          "traffic": measured_traffic(kernel)}}
 
-    if "fwd" in stages:
-        mfma_stage("fwd_causal_b4_h32_n4096_d128", flops3, ms[0], "fwd_bf16_causal")
-    if "window" in stages:
-        mfma_stage("fwd_window1024_b4_h32_n4096_d128", flops3w, ms[1], "fwd_bf16_window")
-    if "decode" in stages:
-        gbs = dec_bytes / (ms[2] * 1e-3) / 1e9
-        components["decode_s64_h32_d128_len512to8192"] = {
-            "ms": round(ms[2], 5), "GB/s": round(gbs, 1), "algorithmic_gb": round(dec_bytes / 1e9, 4),
+    def hbm_stage(name, nbytes, t_ms, kernel):
+        gbs = nbytes / (t_ms * 1e-3) / 1e9
+        components[name] = {
+            "ms": round(t_ms, 5), "GB/s": round(gbs, 1), "algorithmic_gb": round(nbytes / 1e9, 4),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode")}}
-    if "bwd" in stages:
-        mfma_stage("bwd_causal_b2_h16_n4096_d128", flops5, ms[3], "bwd_bf16")
-    if "paged" in stages:
-        gbs = dec_bytes / (ms[4] * 1e-3) / 1e9
-        components[f"decode_paged{args.page_size}_s64_h32_d128_len512to8192"] = {
-            "ms": round(ms[4], 5), "GB/s": round(gbs, 1), "algorithmic_gb": round(dec_bytes / 1e9, 4),
-            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": measured_traffic(f"decode_paged{args.page_size}")}}
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(kernel)}}
 
-    if "fwd16" in stages:
-        mfma_stage("fwd_causal_fp16_b4_h32_n4096_d128", flops3, ms[5], "fwd_fp16_causal")
+    if "fwd" in ms:
+        mfma_stage("fwd_causal_b4_h32_n4096_d128", flops3, ms["fwd"], "fwd_bf16_causal")
+    if "window" in ms:
+        mfma_stage("fwd_window1024_b4_h32_n4096_d128", flops3w, ms["window"], "fwd_bf16_window")
+    if "decode" in ms:
+        hbm_stage("decode_s64_h32_d128_len512to8192", dec_bytes, ms["decode"], "decode")
+    if "bwd" in ms:
+        mfma_stage("bwd_causal_b2_h16_n4096_d128", flops5, ms["bwd"], "bwd_bf16")
+    if "paged" in ms:
+        hbm_stage(f"decode_paged{args.page_size}_s64_h32_d128_len512to8192", dec_bytes, ms["paged"],
+                  f"decode_paged{args.page_size}")
+    if "fwd16" in ms:
+        mfma_stage("fwd_causal_fp16_b4_h32_n4096_d128", flops3, ms["fwd16"], "fwd_fp16_causal")
+    if "decw" in ms:
+        hbm_stage(f"decode_window{W_DEC}_s64_h32_d128_len512to8192", decw_bytes, ms["decw"], "decode_window")
+    if "bwdw" in ms:
+        mfma_stage(f"bwd_window{W_BWD}_b2_h16_n4096_d128", flops5w, ms["bwdw"], "bwd_bf16_window")
 
     if args.copy_calibration:
         log("copy calibration: 3 x 1 GiB device-to-device")
@@ -259,7 +277,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    value = flops3 / (ms[0] * 1e-3) / 1e12 if "fwd" in stages else None
+    value = flops3 / (ms["fwd"] * 1e-3) / 1e12 if "fwd" in ms else None
     result = {
         "metric": "causal fwd TFLOP/s & % bf16 MFMA peak (N=4096,d=128); decode % HBM BW",
         "value": round(value, 3) if value is not None else None,
@@ -270,8 +288,8 @@ def main():
         "dtype": "bf16", "data": "synthetic (seeded N(0,1), rounded to bf16)",
         "config": {"workload": "causal forward B=4 H=32 N=4096 d=128 bf16 (step also runs: window-1024 "
                                "forward, 64x32 ragged decode d=128 lengths U[512,8192] from a dense and "
-                               "from a 64-token paged cache, causal backward B=2 H=16 N=4096 d=128, the causal "
-                               "forward in fp16)",
+                               "from a 64-token paged cache and with a 1024 window, causal backward B=2 H=16 "
+                               "N=4096 d=128 without and with a 1024 window, the causal forward in fp16)",
                    "global_batch": B3, "seq_len": N3, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(value, 3) if value is not None else None,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
