@@ -78,6 +78,22 @@ def test_full_size_sampled_heads():
         check_bf16(dv[b, h], rv[0], f"dV[{b},{h}]")
 
 
+@pytest.mark.slow
+def test_full_size_window_sampled_heads():
+    """The windowed backward stage the bench times: B=2, H=16, N=4096, d=128,
+    causal with a 1024-token window; two whole heads against the oracle."""
+    w = WORKLOADS["bwd_b2_h16_n4096_d128_bf16"]
+    q, k, v, dO = attention_inputs(w["B"], w["H"], w["N"], w["d"], "bf16", seed=0, with_grad=True)
+    dq, dk, dv = run(q, k, v, dO, True, 1024)
+    s = 1 / math.sqrt(128)
+    for b, h in ((0, 3), (1, 15)):
+        rq, rk, rv = oracle.attention_bwd_ref(q[b, h][None], k[b, h][None], v[b, h][None],
+                                              dO[b, h][None], s, True, 1024)
+        check_bf16(dq[b, h], rq[0], f"dQ[{b},{h}]")
+        check_bf16(dk[b, h], rk[0], f"dK[{b},{h}]")
+        check_bf16(dv[b, h], rv[0], f"dV[{b},{h}]")
+
+
 @pytest.mark.parametrize("B,H,N,d", [(1, 3, 700, 128), (1, 2, 1100, 64)])
 @pytest.mark.parametrize("causal,window", [(False, -1), (True, -1), (True, 100), (False, 50)])
 def test_several_tiles_ragged(B, H, N, d, causal, window):

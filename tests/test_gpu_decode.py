@@ -102,6 +102,18 @@ def test_full_size_ragged_decode():
     check_lse(lse, L, "lse")
 
 
+@pytest.mark.slow
+def test_full_size_ragged_decode_window():
+    """The windowed decode stage the bench times: the ragged batch with a
+    1024-token window, every (sequence, head) against the oracle."""
+    w = WORKLOADS["decode_s64_h32_d128_len512to8192_bf16"]
+    inp = decode_inputs(w["S"], w["H"], w["d"], w["len_lo"], w["len_hi"], seed=0)
+    o, lse = run(inp, w["Lmax"], window=1024)
+    O, L = oracle_decode(inp, window=1024)
+    check_bf16(o, O, "o")
+    check_lse(lse, L, "lse")
+
+
 # ------------------------------------------------------------ paged cache --
 
 def run_paged(inp, page_size, window=-1, chunk=0, scale=None, spare=2, seed=0, hide=()):
