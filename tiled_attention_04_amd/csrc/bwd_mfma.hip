@@ -84,8 +84,8 @@ __global__ __launch_bounds__(kPreThreads) void bwd_pre_kernel(
 // owns 128 keys and walks the 64-row query tiles that see them.  Wave
 // w = (kb, qb), kb = w % 4 and qb = w / 4:
 //  * scores: S = Q K^T and dP = dO V^T for its 32 keys (block kb) and the
-//    tile's query rows 32 qb .. 32 qb + 31; Q, dO and K come from LDS as MFMA
-//    A / B operands, V from registers;
+//    tile's query rows 32 qb .. 32 qb + 31; Q and dO come from LDS as MFMA A
+//    operands, the wave's K and V rows stay in registers as B operands;
 //  * P = exp2(S c - L2) and dS = P (dP - D) on the vector ALUs, written to LDS
 //    (keys as rows) in the order of the MFMA A operand, so every wave reads
 //    P^T and dS^T of a key block for all 64 queries with 16-byte reads;
@@ -93,20 +93,18 @@ __global__ __launch_bounds__(kPreThreads) void bwd_pre_kernel(
 //    half of the columns, over all 64 queries (B operands by transpose reads
 //    of the row-major dO and Q tiles).
 // Q, dO, L2 and D of the next query tile stream into LDS by direct loads
-// while the current one is processed (two stages); the K tile is loaded once.
+// while the current one is processed (two stages); K and V are read once.
 // dQ is formed by its own kernel (below): accumulated here it would take one
 // float atomic per query row, column and key tile, and those atomics cost
 // about as much as all the rest of this kernel.
 template <int D>
 struct BwdTile {
-  static constexpr int kQPitch = D == 128 ? 304 : 144;  // bytes per Q / dO / K row in LDS
+  static constexpr int kQPitch = D == 128 ? 304 : 144;  // bytes per Q / dO row in LDS
   static constexpr int kSPitch = 144;                    // bytes per P^T / dS^T row (64 queries)
   static constexpr int kQBytes = kBQ * kQPitch;
-  static constexpr int kKBytes = kBKV * kQPitch;
   static constexpr int kSBytes = kBKV * kSPitch;
   static constexpr int kQBlocks = kQBytes / 1024;  // 1 KB per wave-wide direct load
-  static constexpr int kKBlocks = kKBytes / 1024;
-  static_assert(kQBytes % 1024 == 0 && kKBytes % 1024 == 0, "tiles must be whole 1 KB blocks");
+  static_assert(kQBytes % 1024 == 0, "tiles must be whole 1 KB blocks");
 };
 
 template <typename T, int D>
@@ -122,7 +120,6 @@ void bwd_main_kernel(const T* __restrict__ q, const T* __restrict__ k,
   constexpr int CB = D / 32;         // 32-column blocks of the head dimension
   constexpr int NCB = CB / 2;        // column blocks of dK / dV per wave
   constexpr int QPER = (TL::kQBlocks + NW - 1) / NW;
-  constexpr int KPER = (TL::kKBlocks + NW - 1) / NW;
   constexpr int QP = TL::kQPitch, SP = TL::kSPitch;
   // One LDS object per stage and matrix (the compiler then knows that direct
   // loads into one stage do not alias reads of the other).
@@ -130,7 +127,6 @@ void bwd_main_kernel(const T* __restrict__ q, const T* __restrict__ k,
   __shared__ __attribute__((aligned(1024))) char Q1[TL::kQBytes];
   __shared__ __attribute__((aligned(1024))) char O0[TL::kQBytes];
   __shared__ __attribute__((aligned(1024))) char O1[TL::kQBytes];
-  __shared__ __attribute__((aligned(1024))) char Kt[TL::kKBytes];
   __shared__ __attribute__((aligned(1024))) char Pt[TL::kSBytes];
   __shared__ __attribute__((aligned(1024))) char dSt[TL::kSBytes];
   __shared__ __attribute__((aligned(256))) float LD0[2 * kBQ];  // L2 then D of a query tile
@@ -148,14 +144,18 @@ void bwd_main_kernel(const T* __restrict__ q, const T* __restrict__ k,
   const size_t base = (size_t)bh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
 
-  // This wave's 32 value rows as B operands of dP: V[key][16 s + 8 h + 0..7].
+  // This wave's 32 key and value rows as B operands of S and dP:
+  // K[key][16 s + 8 h + 0..7] and V[key][16 s + 8 h + 0..7].
   const int my_key = k0 + 32 * kb + l32;
-  vec8<T> vf[KS];
+  vec8<T> kf[KS], vf[KS];
   {
+    const rsrc_t k_src = make_rsrc(k + base, head_bytes);
     const rsrc_t v_src = make_rsrc(v + base, head_bytes);
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
+    for (int s = 0; s < KS; ++s) {
+      kf[s] = as_vec8<T>(load16(k_src, (uint32_t)(my_key * D + 16 * s + 8 * h) * 2u));
       vf[s] = as_vec8<T>(load16(v_src, (uint32_t)(my_key * D + 16 * s + 8 * h) * 2u));
+    }
   }
 
   // Query tiles that see at least one of this workgroup's keys.
@@ -198,15 +198,7 @@ void bwd_main_kernel(const T* __restrict__ q, const T* __restrict__ k,
   };
 
   using std::integral_constant;
-  // Prologue: the K tile and the first query tile resident.
-  {
-    const rsrc_t ks = make_rsrc(k + base + (size_t)k0 * D, (uint32_t)max(0, N - k0) * D * 2u);
-#pragma unroll
-    for (int i = 0; i < KPER; ++i) {
-      const int blk = w + i * NW;
-      if (blk < TL::kKBlocks) load_lds16(ks, Kt + blk * 1024, block_src<D>(blk, lane, QP));
-    }
-  }
+  // Prologue: the first query tile resident.
   if (qt0 < qt1) load_qtile(qt0, integral_constant<int, 0>{});
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -218,7 +210,6 @@ void bwd_main_kernel(const T* __restrict__ q, const T* __restrict__ k,
     dv_acc[c] = f32x16{};
   }
   const int q_rd = (32 * qb + l32) * QP + 16 * h;       // A operands of S and dP
-  const int k_rd = (32 * kb + l32) * QP + 16 * h;       // B operands of S
   const int s_wr = (32 * kb + l32) * SP + (32 * qb + 8 * h) * 2;  // this lane's P / dS pieces
   const int s_rd = (32 * kb + l32) * SP + 16 * h;       // A operands of dV / dK
   const int tr_q = tr_addr<QP>(lane);                   // B operands of dV / dK
@@ -239,8 +230,8 @@ void bwd_main_kernel(const T* __restrict__ q, const T* __restrict__ k,
     f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      sacc = mfma32(*(const vec8<T>*)(Qs + q_rd + 32 * s), *(const vec8<T>*)(Kt + k_rd + 32 * s), sacc);
-    interleave<KS, 2 * KS, 4, 0, 1>();
+      sacc = mfma32(*(const vec8<T>*)(Qs + q_rd + 32 * s), kf[s], sacc);
+    interleave<KS, KS, 4, 0, 1>();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < KS; ++s)
