@@ -350,8 +350,12 @@ struct DqTile {
   static_assert(kKBytes % 1024 == 0 && kVBytes % 1024 == 0, "tiles must be whole 1 KB blocks");
 };
 
+// (d = 128 may run one wave per SIMD: this kernel serves grids too small for
+// the ping-pong kernel below, under two workgroups per CU anyway, and held to
+// two waves per SIMD its registers spilled to scratch -- 21-27% slower.
+// d = 64 fits two waves per SIMD and is faster so.)
 template <typename T, int D>
-__global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : 2, 2)))
 void bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k,
                    const T* __restrict__ v, const T* __restrict__ dO,
                    const float* __restrict__ Dv, const float* __restrict__ L2,
