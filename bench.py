@@ -10,6 +10,8 @@ batch (already resident in HBM when timing starts):
   6. causal forward in fp16,    the shape of 1 with fp16 inputs (same seeds)
   7. windowed decode,           the decode batch of 3 with a 1024-token sliding window
   8. windowed backward,         the backward of 4 with a 1024-token sliding window
+  9. decode in fp16,            the decode batch of 3 with fp16 inputs (same seeds)
+ 10. backward in fp16,          the backward of 4 with fp16 inputs (same seeds)
 
 The headline value is the causal forward's TFLOP/s (4*B*H*N^2*d/2 algorithmic
 flops per launch over its measured time); every stage is timed with HIP events
@@ -37,7 +39,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # Stages of one step, in the order they run.
-STAGES = ("fwd", "window", "decode", "bwd", "paged", "fwd16", "decw", "bwdw")
+STAGES = ("fwd", "window", "decode", "bwd", "paged", "fwd16", "decw", "bwdw", "dec16", "bwd16")
 W_DEC = 1024   # sliding window of the windowed decode stage
 W_BWD = 1024   # sliding window of the windowed backward stage
 
@@ -169,6 +171,17 @@ def main():
                                                       w4["d"]), dtype=torch.uint8, device=dev)
     if "decode" in stages or "paged" in stages or "decw" in stages:
         del inp4
+    if "dec16" in stages:
+        inp8 = decode_inputs(w4["S"], w4["H"], w4["d"], w4["len_lo"], w4["len_hi"], dtype="fp16", seed=0)
+        kc8, vc8 = dense_cache(inp8, w4["Lmax"], device=dev)
+        q8 = inp8.q.to(dev)
+        sl8 = torch.from_numpy(inp8.seqlens).to(dev)
+        o8 = torch.empty_like(q8)
+        l8 = torch.empty(q8.shape[:2], dtype=torch.float32, device=dev)
+        ws8 = torch.empty(fa.fa_decode_workspace_size(w4["S"], w4["H"], w4["Lmax"], w4["d"]),
+                          dtype=torch.uint8, device=dev)
+        dec16_bytes = inp8.valid_bytes(2) + 2 * q8.numel() * 2
+        del inp8
 
     w5 = WORKLOADS["bwd_b2_h16_n4096_d128_bf16"]
     B5, H5, N5, d5 = w5["B"], w5["H"], w5["N"], w5["d"]
@@ -186,6 +199,11 @@ def main():
             dq5, dk5, dv5 = (torch.empty(q5.shape, dtype=torch.float32, device=dev) for _ in range(3))
             ws5 = torch.empty(fa.fa_bwd_workspace_size(B5, H5, N5, d5), dtype=torch.uint8, device=dev)
         o5w, l5w = fa.fa_fwd(q5, k5, v5, causal=True, window=W_BWD)
+    if "bwd16" in stages:
+        q9, k9, v9, g9 = (t.to(dev) for t in attention_inputs(B5, H5, N5, d5, "fp16", seed=0, with_grad=True))
+        o9, l9 = fa.fa_fwd(q9, k9, v9, causal=True)
+        dq9, dk9, dv9 = (torch.empty(q9.shape, dtype=torch.float32, device=dev) for _ in range(3))
+        ws9 = torch.empty(fa.fa_bwd_workspace_size(B5, H5, N5, d5), dtype=torch.uint8, device=dev)
 
     # ---- one step: every stage once, each bracketed by events -------------------
     flops3 = 4.0 * B3 * H3 * N3 * N3 * d3 / 2
@@ -204,6 +222,9 @@ def main():
         "decw": lambda: fa.fa_decode(q4, kc4, vc4, sl4, window=W_DEC, o=o4, lse=l4, workspace=ws4),
         "bwdw": lambda: fa.fa_bwd(q5, k5, v5, o5w, g5, l5w, causal=True, window=W_BWD, dq=dq5, dk=dk5,
                                   dv=dv5, workspace=ws5),
+        "dec16": lambda: fa.fa_decode(q8, kc8, vc8, sl8, o=o8, lse=l8, workspace=ws8),
+        "bwd16": lambda: fa.fa_bwd(q9, k9, v9, o9, g9, l9, causal=True, dq=dq9, dk=dk9, dv=dv9,
+                                   workspace=ws9),
     }
     run = [n for n in STAGES if n in stages]
 
@@ -267,6 +288,10 @@ def main():
         hbm_stage(f"decode_window{W_DEC}_s64_h32_d128_len512to8192", decw_bytes, ms["decw"], "decode_window")
     if "bwdw" in ms:
         mfma_stage(f"bwd_window{W_BWD}_b2_h16_n4096_d128", flops5w, ms["bwdw"], "bwd_bf16_window")
+    if "dec16" in ms:
+        hbm_stage("decode_fp16_s64_h32_d128_len512to8192", dec16_bytes, ms["dec16"], "decode_fp16")
+    if "bwd16" in ms:
+        mfma_stage("bwd_causal_fp16_b2_h16_n4096_d128", flops5, ms["bwd16"], "bwd_fp16")
 
     if args.copy_calibration:
         log("copy calibration: 3 x 1 GiB device-to-device")
@@ -289,7 +314,8 @@ def main():
         "config": {"workload": "causal forward B=4 H=32 N=4096 d=128 bf16 (step also runs: window-1024 "
                                "forward, 64x32 ragged decode d=128 lengths U[512,8192] from a dense and "
                                "from a 64-token paged cache and with a 1024 window, causal backward B=2 H=16 "
-                               "N=4096 d=128 without and with a 1024 window, the causal forward in fp16)",
+                               "N=4096 d=128 without and with a 1024 window, the causal forward, the decode "
+                               "and the causal backward in fp16)",
                    "global_batch": B3, "seq_len": N3, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(value, 3) if value is not None else None,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
