@@ -96,7 +96,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   const int c_begin = c * chunk;
   if (c_begin >= n || c_begin + chunk <= lo) return;  // the merge skips this split too
 
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform: row ranges and pages per wave
   const int g = lane / LPR, e = lane % LPR;
   const size_t sh = (size_t)s * H + h;
   rsrc_t k_src, v_src;
@@ -132,7 +133,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
       // The buffer covers the page's valid rows only: rows at or past n read
       // as zero (a stale row could hold NaN, and 0 * NaN is NaN).
       const int slot = r0 / pc.page_size;
-      const int page = pc.table[(size_t)s * pc.max_pages + slot];
+      // (wave-uniform, so the buffer resource below lives in scalar registers)
+      const int page = __builtin_amdgcn_readfirstlane(pc.table[(size_t)s * pc.max_pages + slot]);
       page_ok = (uint32_t)page < (uint32_t)pc.num_pages;
       const int rows_here = min(pc.page_size, n - slot * pc.page_size);
       const size_t pbase = ((size_t)(page_ok ? page : 0) * H + h) * (size_t)pc.page_size * D;
@@ -148,6 +150,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
       kr[u] = load16(k_src, off);
       vr[u] = load16(v_src, off);
     }
+    // Every load of the trip is issued before any of them is used (left
+    // alone, the compiler interleaves fp16 loads with their mixed-precision
+    // FMAs and keeps far fewer bytes in flight).
+    __builtin_amdgcn_sched_barrier(0);
     float sc[kUnroll];
     float mx = kNegInf;
 #pragma unroll
