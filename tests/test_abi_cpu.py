@@ -163,6 +163,7 @@ def test_decode_paged_rejects_bad_arguments(lib):
     assert call(scale=float("nan")) == 1
     assert call(dtype=5) == 1
     assert call(d=80) == 2
+    assert call(page=1 << 24, max_pages=1, dtype=0) == 2  # one page of one head above 2 GiB
     assert call(ws=None) == 3
     need = fa355.fa_decode_workspace_size(2, 2, 4 * 64, 128, 0)
     assert call(wsb=need - 1) == 3

@@ -321,6 +321,8 @@ fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_page
     return fail(FA_ERR_INVALID_ARG, "chunk must be 0 (auto) or a positive multiple of 64 (got %d)", chunk);
   if (!valid_dtype(dtype)) return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
   if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "decode supports d in {64, 128} (got %d)", d);
+  if ((long long)page_size * d * (long long)elem_bytes(dtype) > kMaxBufferBytes)
+    return fail(FA_ERR_UNSUPPORTED, "one page of one head exceeds 2 GiB");
   const int Lmax = max_pages * page_size;
   if (chunk == 0) chunk = fa::decode_auto_chunk(S, H, Lmax);
   const long long nchunk = (Lmax + chunk - 1) / chunk;
