@@ -89,12 +89,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   const int id = blockIdx.x;
   const int h = id % H;
   const int s = (id / H) % S;
-  const int c = id / (H * S);
   int n = seqlens[s];
   clamp_len(n, Lmax);
   const int lo = window >= 0 ? max(0, n - 1 - window) : 0;
+  // With a window the grid covers only the splits a window can touch,
+  // counted from the one holding its first row; without, all of them.
+  const int c = id / (H * S) + (window >= 0 ? lo / chunk : 0);
   const int c_begin = c * chunk;
-  if (c_begin >= n || c_begin + chunk <= lo) return;  // the merge skips this split too
+  if (c >= nchunk || c_begin >= n || c_begin + chunk <= lo) return;  // the merge skips this split too
 
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform: row ranges and pages per wave
@@ -259,7 +261,9 @@ hipError_t launch_t(const void* q, const void* kc, const void* vc, const int32_t
   const int nchunk = (Lmax + chunk - 1) / chunk;
   float* ws_o = (float*)ws;
   float* ws_ml = ws_o + (size_t)S * H * nchunk * D;
-  const long long grid = (long long)nchunk * S * H;
+  // A window of W rows touches at most ceil(W / chunk) + 1 splits.
+  const int nsplit = window >= 0 ? min(nchunk, (window + chunk) / chunk + 1) : nchunk;
+  const long long grid = (long long)nsplit * S * H;
   if (pc.table)
     hipLaunchKernelGGL((decode_split_kernel<T, D, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
                        (const T*)q, (const T*)kc, (const T*)vc, seqlens, ws_o, ws_ml, S, H, Lmax,
