@@ -604,7 +604,8 @@ void fwd_pingpong_kernel(const T* __restrict__ q, const T* __restrict__ k,
     if (kt0 + 2 < kt1) load_share(kt0 + 2, integral_constant<int, 2>{});
     wait_vm(n_loads(kt0 + 2));
   } else {
-    wait_vm(0);
+    // Q and K of the first tile; its V and the second tile may still land.
+    wait_vm(v_nblk + (kt0 + 1 < kt1 ? k_nblk + v_nblk : 0));
   }
   barrier_keep_loads();
 #pragma unroll
@@ -614,7 +615,12 @@ void fwd_pingpong_kernel(const T* __restrict__ q, const T* __restrict__ k,
     for (int s = 0; s < KS; ++s)
       sc[kb2] = mfma32(*(const vec8<T>*)(K0 + k_rd + kb2 * 32 * TL::kKPitch + 32 * s), qf[s], sc[kb2]);
   }
-  if (grp == 1) barrier_keep_loads();  // group 1 runs one phase behind
+  if (grp == 1) {  // group 1 runs one phase behind
+    // Its shares of V of the first tile and K of the second must have landed
+    // before group 0's first matrix phase (the barrier below opens it).
+    if constexpr (NS == 3) wait_vm(kt0 + 1 < kt1 ? v_nblk : 0);
+    barrier_keep_loads();
+  }
 
   // One tile: softmax phase, barrier, matrix phase, barrier.  Stage of tile
   // kt is ST (compile time); tile kt+1 is in stage (ST+1)%NS and tile
