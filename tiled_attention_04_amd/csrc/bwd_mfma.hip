@@ -686,12 +686,19 @@ void bwd_dq_pp_kernel(const T* __restrict__ q, const T* __restrict__ k,
   };
 
   using std::integral_constant;
+  const int nblk = (TL::kKBlocks - w + NW - 1) / NW + (TL::kVBlocks - w + NW - 1) / NW;
   load_share(kt0, integral_constant<int, 0>{});
   if (kt0 + 1 < kt1) load_share(kt0 + 1, integral_constant<int, 1>{});
-  wait_vm(0);
+  wait_vm(kt0 + 1 < kt1 ? nblk : 0);  // tile kt0 only; tile kt0+1 may still land
   barrier_keep_loads();
   if (active(kt0)) scores(integral_constant<int, 0>{});
-  if (grp == 1) barrier_keep_loads();  // group 1 runs one phase behind
+  if (grp == 1) {  // group 1 runs one phase behind
+    // Its shares of tile kt0+1 must have landed before group 0's first
+    // matrix phase (the barrier below opens it); group 0 waits for its own
+    // shares before that barrier in its first vector phase.
+    wait_vm(0);
+    barrier_keep_loads();
+  }
 
   // Tile kt in stage ST: vector phase (P, dS of tile kt), barrier, matrix
   // phase (dQ of tile kt, S and dP of tile kt+1), barrier.
