@@ -617,8 +617,8 @@ void fwd_pingpong_kernel(const T* __restrict__ q, const T* __restrict__ k,
   using std::integral_constant;
   // Loads of tile t by this wave (0 past the end).
   auto n_loads = [&] __device__ (int tile) { return tile < kt1 ? k_nblk + v_nblk : 0; };
-  // Prologue: tiles kt0 .. kt0+NS-2 in flight, the first two resident, then
-  // the scores of tile kt0.
+  // Prologue: tiles kt0 .. kt0+NS-2 in flight, then the scores of tile kt0
+  // as soon as Q and its K have landed.
   load_share(kt0, integral_constant<int, 0>{});
   if (kt0 + 1 < kt1) load_share(kt0 + 1, integral_constant<int, 1>{});
   if constexpr (NS > 3) {
