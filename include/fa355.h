@@ -161,7 +161,8 @@ fa_status fa_tune_import(const int64_t* rows, int n_rows);
 
 /*
  * fa_decode_workspace_size -- bytes of workspace fa_decode needs for these
- * sizes and this split length (chunk = 0 means the automatic choice).
+ * sizes and this split length (chunk = 0: enough for the automatic choice,
+ * which may use shorter splits under a window, so size for any window).
  * Returns 0 for invalid sizes.
  */
 size_t fa_decode_workspace_size(int S, int H, int Lmax, int d, int chunk);

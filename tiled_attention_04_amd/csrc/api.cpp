@@ -267,7 +267,7 @@ fa_status fa_tune_import(const int64_t* rows, int n_rows) {
 
 size_t fa_decode_workspace_size(int S, int H, int Lmax, int d, int chunk) {
   if (S <= 0 || H <= 0 || Lmax <= 0 || d <= 0 || chunk < 0 || chunk % 64 != 0) return 0;
-  if (chunk == 0) chunk = fa::decode_auto_chunk(S, H, Lmax);
+  if (chunk == 0) chunk = fa::decode_auto_chunk(S, H, Lmax, 0);  // the windowed choice: smallest splits, largest workspace
   return fa::decode_workspace_bytes(S, H, Lmax, d, chunk);
 }
 
@@ -288,7 +288,7 @@ fa_status fa_decode(const void* q, const void* kcache, const void* vcache, const
   if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "decode supports d in {64, 128} (got %d)", d);
   if ((long long)Lmax * d * (long long)elem_bytes(dtype) > kMaxBufferBytes)
     return fail(FA_ERR_UNSUPPORTED, "one (sequence, head) cache slice exceeds 2 GiB");
-  if (chunk == 0) chunk = fa::decode_auto_chunk(S, H, Lmax);
+  if (chunk == 0) chunk = fa::decode_auto_chunk(S, H, Lmax, window);
   const long long nchunk = (Lmax + chunk - 1) / chunk;
   if (nchunk * S * H * 256 > kMaxThreadsPerLaunch) return fail(FA_ERR_UNSUPPORTED, "grid too large");
   const size_t need = fa::decode_workspace_bytes(S, H, Lmax, d, chunk);
@@ -324,7 +324,7 @@ fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_page
   if ((long long)page_size * d * (long long)elem_bytes(dtype) > kMaxBufferBytes)
     return fail(FA_ERR_UNSUPPORTED, "one page of one head exceeds 2 GiB");
   const int Lmax = max_pages * page_size;
-  if (chunk == 0) chunk = fa::decode_auto_chunk(S, H, Lmax);
+  if (chunk == 0) chunk = fa::decode_auto_chunk(S, H, Lmax, window);
   const long long nchunk = (Lmax + chunk - 1) / chunk;
   if (nchunk * S * H * 256 > kMaxThreadsPerLaunch) return fail(FA_ERR_UNSUPPORTED, "grid too large");
   const size_t need = fa::decode_workspace_bytes(S, H, Lmax, d, chunk);

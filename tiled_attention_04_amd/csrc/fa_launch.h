@@ -32,7 +32,7 @@ hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, void* o,
 
 // Split-K decode (+ merge), any Elem, d in {64, 128}.
 size_t decode_workspace_bytes(int S, int H, int Lmax, int d, int chunk);
-int decode_auto_chunk(int S, int H, int Lmax);
+int decode_auto_chunk(int S, int H, int Lmax, int window);
 hipError_t launch_decode(const void* q, const void* kc, const void* vc, const int32_t* seqlens,
                          void* o, float* lse, int S, int H, int Lmax, int d, float scale,
                          int window, int chunk, void* ws, Elem elem, hipStream_t stream);
