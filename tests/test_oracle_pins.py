@@ -348,6 +348,44 @@ def test_I9_constant_v():
         np.testing.assert_allclose(O, -2.75, atol=1e-14)
 
 
+SHIFTS = np.array([-800.0, -45.0, -17.0, 0.0, 10.0, 750.0, -300.0, 60.0, -1.5, 400.0, -600.0])
+
+
+def _shifted(Q, K, offsets, scale):
+    """Q, K with one extra column: 1 in every key, offsets / scale in the
+    queries, so that row i's scaled scores move by offsets[i] exactly."""
+    col_k = np.ones(K.shape[:-1] + (1,))
+    col_q = (offsets / scale)[:, None] * np.ones(Q.shape[:-1] + (1,))
+    return np.concatenate([Q, col_q], axis=-1), np.concatenate([K, col_k], axis=-1)
+
+
+@pytest.mark.parametrize("causal,window", [(False, -1), (True, -1), (True, 4)])
+def test_shift_invariance_far_offsets(causal, window):
+    """A per-row constant added to the scores leaves O unchanged and moves L by
+    exactly that constant (NumPy page, Step 1: the stable softmax subtracts
+    the row max) -- also at offsets where exp of the raw scores overflows or
+    underflows in float64."""
+    rng = np.random.default_rng(31)
+    N, d = len(SHIFTS), 6
+    Q, K, V = (rng.standard_normal((2, N, d)) for _ in range(3))
+    scale = 0.4
+    O0, L0 = oracle.attention_ref(Q, K, V, scale, causal, window)
+    Qs, Ks = _shifted(Q, K, SHIFTS, scale)
+    O1, L1 = oracle.attention_ref(Qs, Ks, V, scale, causal, window)
+    assert np.isfinite(O1).all() and np.isfinite(L1).all()
+    np.testing.assert_allclose(O1, O0, atol=1e-12)
+    np.testing.assert_allclose(L1 - SHIFTS, L0, atol=1e-9)
+    # The exact gradients move only in the extra columns: dQ, dV and the
+    # original columns of dK are unchanged.
+    G = rng.standard_normal((2, N, d))
+    g0 = oracle.attention_bwd_ref(Q, K, V, G, scale, causal, window)
+    g1 = oracle.attention_bwd_ref(Qs, Ks, V, G, scale, causal, window)
+    np.testing.assert_allclose(g1[0][..., :d], g0[0], atol=1e-9)
+    np.testing.assert_allclose(g1[0][..., d], 0.0, atol=1e-9)
+    np.testing.assert_allclose(g1[1][..., :d], g0[1], atol=1e-9)
+    np.testing.assert_allclose(g1[2], g0[2], atol=1e-9)
+
+
 def test_empty_rows_give_zero_output_and_neg_inf_lse():
     """Non-causal window with more keys hidden than exist cannot empty a row,
     but a query row with no visible key (reading R4) is O=0, L=-inf."""
@@ -406,6 +444,20 @@ def test_planted_strict_causal_mask_is_caught(monkeypatch):
     monkeypatch.setattr(oa, "allowed_mask", _mask_strict_causal)
     with pytest.raises(AssertionError):
         test_worked_example_causal_closed_forms()
+
+
+def _softmax_without_max(S, ok):
+    S = np.where(ok, S, -np.inf)
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+        E = np.exp(S)  # planted: the row max is not subtracted
+        ell = E.sum(axis=1)
+        return E / ell[:, None], np.log(ell)
+
+
+def test_planted_unstable_softmax_fails_shift_pin(monkeypatch):
+    monkeypatch.setattr(oa, "_softmax_rows", _softmax_without_max)
+    with pytest.raises(AssertionError):
+        test_shift_invariance_far_offsets(False, -1)
 
 
 def test_planted_window_off_by_one_is_caught(monkeypatch):

@@ -108,6 +108,19 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int lo, int hi, int h)
 // everything may have underflowed.
 constexpr float kSumCap = 16384.f;
 constexpr float kSumFloor = 0x1p-60f;
+// fp16 keeps P in 5 exponent bits: below 2^-14 it is subnormal (absolute
+// spacing 2^-24) and below 2^-25 it rounds to zero.  A reference far above
+// the row's scores (the initial 0 against scores all near -20, say) would
+// pass the floor above with every P subnormal or zero while l, summed in
+// fp32, stays right: O would collapse towards 0.  For fp16 the fast path is
+// therefore kept only while each lane's running sum against the reference
+// (earlier tiles included) is at least 1/2, so the row's sum l is at least
+// 1 and each P's rounding error, at most 2^-25 absolute, is at most 2^-25
+// of l.  (A lane whose half of the row sums below 1/2 while the row as a
+// whole is fine takes the exact path for nothing: a rare cost, and cheaper
+// than a cross-lane sum on every tile, which pushed the 8-wave kernel's
+// registers over its budget.)
+constexpr float kLaneSumFloorF16 = 0.5f;
 
 // One tile of the online softmax for this lane's query row ("Building Flash
 // Attention from Scratch in Pure NumPy", Step 2): raw scores s (16 keys per
@@ -117,9 +130,10 @@ constexpr float kSumFloor = 0x1p-60f;
 //
 // The reference is lazy: P = 2^(x - ref) is first computed against the
 // current reference (0 for a row that has none yet), and kept when every
-// lane's partial sum lies in [kSumFloor, kSumCap] -- then no P exceeds 2^14
-// and none that matters has underflowed, and the tile costs no max and no
-// rescale.  Otherwise (a row's first scores, a jump of the running max, or
+// lane's partial sum lies in [kSumFloor, kSumCap] (for fp16: at most kSumCap,
+// and the lane's running sum at least kLaneSumFloorF16) -- then no P exceeds
+// 2^14 and none that matters has underflowed or lost precision, and the
+// tile costs no max and no rescale.  Otherwise (a row's first scores, a jump of the running max, or
 // keys all hidden so far) the wave takes the exact path: tile max, raise the
 // reference when the max exceeds it by more than kTau, rescale l and O, and
 // recompute P.  Rows that passed the test keep their reference and P.  O / l
@@ -167,7 +181,11 @@ __device__ __forceinline__ void softmax_tile(const f32x16 (&s)[2], uint32_t (&pk
   };
   if (m_ref == kNegInf) m_ref = 0.f;
   const float fast = exps(m_ref);
-  const bool keep = fast <= kSumCap && l_run + fast >= kSumFloor;
+  bool keep;
+  if constexpr (std::is_same<T, f16>::value)
+    keep = fast <= kSumCap && l_run + fast >= kLaneSumFloorF16;
+  else
+    keep = fast <= kSumCap && l_run + fast >= kSumFloor;
   if (__builtin_amdgcn_ballot_w64(!keep) == 0) {
     l_run += fast;
     return;
