@@ -12,11 +12,18 @@ batch (already resident in HBM when timing starts):
   8. windowed backward,         the backward of 4 with a 1024-token sliding window
   9. decode in fp16,            the decode batch of 3 with fp16 inputs (same seeds)
  10. backward in fp16,          the backward of 4 with fp16 inputs (same seeds)
+ 11. small forward,             B=1, H=8, N=1024, d=64, bf16, 64 x 64 tiles, full attention
+ 12. small causal forward,      the same, causal
 
 The headline value is the causal forward's TFLOP/s (4*B*H*N^2*d/2 algorithmic
-flops per launch over its measured time); every stage is timed with HIP events
-recorded on the stream the kernels run on.  The fp64 oracle is timed on the
-host on a bounded sample of the causal forward (a few heads) as the CPU baseline.
+flops per launch over its median time per step); every stage is timed with HIP
+events recorded on the stream the kernels run on, and each stage reports the
+median, 10th and 90th percentile over the timed steps.  After the timed steps
+the causal forward and the two small forwards are also timed back to back
+(many launches between one pair of events, no event between launches).  The
+GFX clock is sampled (amdsmi) while the steps run.  The fp64 oracle is timed
+on the host on a bounded sample of the causal forward (a few heads) as the CPU
+baseline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -39,7 +46,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # Stages of one step, in the order they run.
-STAGES = ("fwd", "window", "decode", "bwd", "paged", "fwd16", "decw", "bwdw", "dec16", "bwd16")
+STAGES = ("fwd", "window", "decode", "bwd", "paged", "fwd16", "decw", "bwdw", "dec16", "bwd16", "c2", "c2c")
 W_DEC = 1024   # sliding window of the windowed decode stage
 W_BWD = 1024   # sliding window of the windowed backward stage
 
@@ -67,6 +74,11 @@ def measured_traffic(kernel):
     """HBM bytes per launch from the committed counter runs (FETCH_SIZE +
     WRITE_SIZE, scaled by a plain copy kernel), or None if the kernel's
     sources changed since they were taken."""
+    rec = traffic_record(kernel)
+    return rec["bytes_per_launch"] if rec else None
+
+
+def traffic_record(kernel):
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f).get(kernel)
@@ -77,7 +89,81 @@ def measured_traffic(kernel):
             return None
     except OSError:  # a source was renamed or removed since
         return None
-    return rec["bytes_per_launch"]
+    return rec
+
+
+def traffic_note(kernel):
+    rec = traffic_record(kernel)
+    if rec is None:
+        return "null: no counter run of the current kernel sources"
+    return (f"stored, not measured in this run: rocprofv3 --pmc FETCH_SIZE then WRITE_SIZE per "
+            f"dispatch, scaled by a plain copy's counts (profiles/traffic.json, kernel sources sha256 "
+            f"{rec['sources_sha256']})")
+
+
+class ClockSampler:
+    """Samples the GPU's GFX clock on a background thread (amdsmi GPU
+    metrics: the per-XCD current clocks when reported, else the current or
+    average clock), tagging each sample with the phase the run is in."""
+
+    def __init__(self, period_s=0.005):
+        import threading
+        self.period, self.samples, self.phase, self.source = period_s, [], None, None
+        self._stop = threading.Event()
+        self._thread = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+            if self._read() is None:
+                self._smi = None
+        except Exception as e:  # no amdsmi, no permission, no device: report without clocks
+            self._smi = None
+            self.error = f"{type(e).__name__}: {e}"
+        if self._smi is not None:
+            self._thread = threading.Thread(target=self._loop, daemon=True)
+            self._thread.start()
+
+    def _read(self):
+        try:
+            m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+        except Exception as e:
+            self.error = f"{type(e).__name__}: {e}"
+            return None
+        for key in ("current_gfxclks", "current_gfxclk", "average_gfxclk_frequency"):
+            v = m.get(key)
+            if isinstance(v, (list, tuple)):
+                v = [x for x in v if isinstance(x, (int, float)) and 0 < x < 0xFFFF]
+                if v:
+                    self.source = f"amdsmi gpu_metrics {key} (mean over {len(v)} XCDs)"
+                    return float(sum(v)) / len(v)
+            elif isinstance(v, (int, float)) and 0 < v < 0xFFFF:
+                self.source = f"amdsmi gpu_metrics {key}"
+                return float(v)
+        return None
+
+    def _loop(self):
+        while not self._stop.is_set():
+            if self.phase is not None:
+                v = self._read()
+                if v is not None:
+                    self.samples.append((self.phase, v))
+            self._stop.wait(self.period)
+
+    def stop(self):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+
+    def summary(self, phase):
+        v = np.array([x for p, x in self.samples if p == phase])
+        if self._smi is None:
+            return {"available": False, "why": getattr(self, "error", "amdsmi unavailable")}
+        if len(v) == 0:
+            return {"available": True, "samples": 0}
+        return {"median_mhz": float(np.median(v)), "min_mhz": float(v.min()), "max_mhz": float(v.max()),
+                "samples": int(len(v)), "source": self.source}
 
 
 def cpu_baseline(q, k, v, budget_s=12.0):
@@ -96,9 +182,12 @@ def cpu_baseline(q, k, v, budget_s=12.0):
         if time.perf_counter() - t0 >= budget_s or heads >= B * H:
             break
     dt = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    info = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    threads = max([p.get("num_threads", 1) for p in info] or [1])
+    blas = ", ".join(f"{p.get('internal_api')} {p.get('version')} ({p.get('threading_layer')}, "
+                     f"{p.get('num_threads')} threads)" for p in info) or "none found"
     return {"value": round(heads * flops_head / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "blas": blas, "host_cpus": len(os.sched_getaffinity(0)),
             "sample": f"{heads} of {B * H} (batch, head) slices of the causal N={N}, d={d} forward, "
                       f"fp64 NumPy, {dt:.1f} s"}
 
@@ -205,11 +294,20 @@ def main():
         dq9, dk9, dv9 = (torch.empty(q9.shape, dtype=torch.float32, device=dev) for _ in range(3))
         ws9 = torch.empty(fa.fa_bwd_workspace_size(B5, H5, N5, d5), dtype=torch.uint8, device=dev)
 
+    w2 = WORKLOADS["fwd_b1_h8_n1024_d64_bf16"]
+    B2, H2, N2, d2, T2 = w2["B"], w2["H"], w2["N"], w2["d"], w2["block"]
+    if "c2" in stages or "c2c" in stages:
+        q2, k2, v2 = (t.to(dev) for t in attention_inputs(B2, H2, N2, d2, "bf16", seed=0))
+        o2, o2c = torch.empty_like(q2), torch.empty_like(q2)
+        l2 = torch.empty((B2, H2, N2), dtype=torch.float32, device=dev)
+        l2c = torch.empty_like(l2)
+
     # ---- one step: every stage once, each bracketed by events -------------------
     flops3 = 4.0 * B3 * H3 * N3 * N3 * d3 / 2
     flops3w = 4.0 * d3 * B3 * H3 * window_pairs(N3, w3["window"])
     flops5 = 10.0 * B5 * H5 * N5 * N5 * d5 / 2
     flops5w = 10.0 * d5 * B5 * H5 * window_pairs(N5, W_BWD)
+    flops2 = 4.0 * B2 * H2 * N2 * N2 * d2
 
     calls = {
         "fwd": lambda: fa.fa_fwd(q3, k3, v3, causal=True, o=o3, lse=l3),
@@ -225,6 +323,8 @@ def main():
         "dec16": lambda: fa.fa_decode(q8, kc8, vc8, sl8, o=o8, lse=l8, workspace=ws8),
         "bwd16": lambda: fa.fa_bwd(q9, k9, v9, o9, g9, l9, causal=True, dq=dq9, dk=dk9, dv=dv9,
                                    workspace=ws9),
+        "c2": lambda: fa.fa_fwd_ex(q2, k2, v2, T2, T2, o=o2, lse=l2),
+        "c2c": lambda: fa.fa_fwd_ex(q2, k2, v2, T2, T2, causal=True, o=o2c, lse=l2c),
     }
     run = [n for n in STAGES if n in stages]
 
@@ -236,7 +336,9 @@ def main():
         if ev is not None:
             ev[len(run)].record()
 
+    clock = ClockSampler()
     log(f"warmup {args.warmup} steps")
+    clock.phase = "warmup"
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -244,54 +346,97 @@ def main():
     log(f"timing {args.steps} steps")
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(run) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
+    clock.phase = "timed"
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clock.phase = None
     comp = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(len(run))]
                      for i in range(args.steps)])  # ms
-    ms = dict(zip(run, comp.mean(axis=0)))
-    log("stage ms (mean): " + ", ".join(f"{n}={m:.4f}" for n, m in ms.items()))
+    stats = {n: {"median": float(np.median(comp[:, j])), "p10": float(np.percentile(comp[:, j], 10)),
+                 "p90": float(np.percentile(comp[:, j], 90)), "mean": float(comp[:, j].mean())}
+             for j, n in enumerate(run)}
+    ms = {n: st["median"] for n, st in stats.items()}
+    log("stage ms (median [p10, p90]): " + ", ".join(
+        f"{n}={st['median']:.4f} [{st['p10']:.4f}, {st['p90']:.4f}]" for n, st in stats.items()))
+
+    # Back to back: many launches between one pair of events, so that no
+    # event sits between two launches; the median over repetitions.
+    b2b = {}
+    clock.phase = "b2b"
+    for n, launches in (("fwd", 20), ("c2", 200), ("c2c", 200)):
+        if n not in run:
+            continue
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+        for a, b in pairs:
+            a.record()
+            for _ in range(launches):
+                calls[n]()
+            b.record()
+        torch.cuda.synchronize()
+        per = np.array([a.elapsed_time(b) / launches for a, b in pairs])
+        b2b[n] = {"ms_per_launch_median": float(np.median(per)), "min": float(per.min()),
+                  "max": float(per.max()), "launches": launches, "repetitions": len(pairs)}
+    clock.phase = None
+    clock.stop()
+    if b2b:
+        log("back to back ms per launch (median): " + ", ".join(
+            f"{n}={r['ms_per_launch_median']:.4f}" for n, r in b2b.items()))
 
     components = {}
 
-    def mfma_stage(name, flops, t_ms, kernel):
-        tf = flops / (t_ms * 1e-3) / 1e12
+    def stage_stats(key):
+        st = stats[key]
+        return {"ms": round(st["median"], 5), "ms_p10": round(st["p10"], 5), "ms_p90": round(st["p90"], 5),
+                "ms_mean": round(st["mean"], 5)}
+
+    def mfma_stage(name, flops, key, kernel):
+        tf = flops / (ms[key] * 1e-3) / 1e12
         components[name] = {
-            "ms": round(t_ms, 5), "TFLOP/s": round(tf, 2), "algorithmic_tflop": round(flops / 1e12, 5),
+            **stage_stats(key), "TFLOP/s": round(tf, 2), "algorithmic_tflop": round(flops / 1e12, 5),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                          "traffic": measured_traffic(kernel)}}
+        if key in b2b:
+            t = b2b[key]["ms_per_launch_median"]
+            components[name]["back_to_back"] = {**b2b[key], "TFLOP/s": round(flops / (t * 1e-3) / 1e12, 2)}
 
-    def hbm_stage(name, nbytes, t_ms, kernel):
-        gbs = nbytes / (t_ms * 1e-3) / 1e9
+    def hbm_stage(name, nbytes, key, kernel):
+        gbs = nbytes / (ms[key] * 1e-3) / 1e9
         components[name] = {
-            "ms": round(t_ms, 5), "GB/s": round(gbs, 1), "algorithmic_gb": round(nbytes / 1e9, 4),
+            **stage_stats(key), "GB/s": round(gbs, 1), "algorithmic_gb": round(nbytes / 1e9, 4),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(kernel)}}
 
     if "fwd" in ms:
-        mfma_stage("fwd_causal_b4_h32_n4096_d128", flops3, ms["fwd"], "fwd_bf16_causal")
+        mfma_stage("fwd_causal_b4_h32_n4096_d128", flops3, "fwd", "fwd_bf16_causal")
     if "window" in ms:
-        mfma_stage("fwd_window1024_b4_h32_n4096_d128", flops3w, ms["window"], "fwd_bf16_window")
+        mfma_stage("fwd_window1024_b4_h32_n4096_d128", flops3w, "window", "fwd_bf16_window")
     if "decode" in ms:
-        hbm_stage("decode_s64_h32_d128_len512to8192", dec_bytes, ms["decode"], "decode")
+        hbm_stage("decode_s64_h32_d128_len512to8192", dec_bytes, "decode", "decode")
     if "bwd" in ms:
-        mfma_stage("bwd_causal_b2_h16_n4096_d128", flops5, ms["bwd"], "bwd_bf16")
+        mfma_stage("bwd_causal_b2_h16_n4096_d128", flops5, "bwd", "bwd_bf16")
     if "paged" in ms:
-        hbm_stage(f"decode_paged{args.page_size}_s64_h32_d128_len512to8192", dec_bytes, ms["paged"],
+        hbm_stage(f"decode_paged{args.page_size}_s64_h32_d128_len512to8192", dec_bytes, "paged",
                   f"decode_paged{args.page_size}")
     if "fwd16" in ms:
-        mfma_stage("fwd_causal_fp16_b4_h32_n4096_d128", flops3, ms["fwd16"], "fwd_fp16_causal")
+        mfma_stage("fwd_causal_fp16_b4_h32_n4096_d128", flops3, "fwd16", "fwd_fp16_causal")
     if "decw" in ms:
-        hbm_stage(f"decode_window{W_DEC}_s64_h32_d128_len512to8192", decw_bytes, ms["decw"], "decode_window")
+        hbm_stage(f"decode_window{W_DEC}_s64_h32_d128_len512to8192", decw_bytes, "decw", "decode_window")
     if "bwdw" in ms:
-        mfma_stage(f"bwd_window{W_BWD}_b2_h16_n4096_d128", flops5w, ms["bwdw"], "bwd_bf16_window")
+        mfma_stage(f"bwd_window{W_BWD}_b2_h16_n4096_d128", flops5w, "bwdw", "bwd_bf16_window")
     if "dec16" in ms:
-        hbm_stage("decode_fp16_s64_h32_d128_len512to8192", dec16_bytes, ms["dec16"], "decode_fp16")
+        hbm_stage("decode_fp16_s64_h32_d128_len512to8192", dec16_bytes, "dec16", "decode_fp16")
     if "bwd16" in ms:
-        mfma_stage("bwd_causal_fp16_b2_h16_n4096_d128", flops5, ms["bwd16"], "bwd_fp16")
+        mfma_stage("bwd_causal_fp16_b2_h16_n4096_d128", flops5, "bwd16", "bwd_fp16")
+    # The small forward is cache-resident and launch-bound: reported as is,
+    # not a roofline target.
+    if "c2" in ms:
+        mfma_stage(f"fwd_b1_h8_n1024_d64_tile{T2}", flops2, "c2", None)
+    if "c2c" in ms:
+        mfma_stage(f"fwd_causal_b1_h8_n1024_d64_tile{T2}", flops2 / 2, "c2c", None)
 
     if args.copy_calibration:
         log("copy calibration: 3 x 1 GiB device-to-device")
@@ -303,6 +448,10 @@ def main():
         del src, dst
 
     value = flops3 / (ms["fwd"] * 1e-3) / 1e12 if "fwd" in ms else None
+    bq3, tuned3 = fa.fa_fwd_auto_block_q(B3, H3, N3, d3, causal=True)
+    kernel3 = (f"fwd_pingpong_kernel<bf16, {d3}>" if bq3 == 256 else
+               f"fwd_mfma_kernel<bf16, {d3}, {bq3 // 32}>")
+    kernel3 += f" ({bq3} query rows per workgroup, {'tuned' if tuned3 else 'heuristic'} choice)"
     result = {
         "metric": "causal fwd TFLOP/s & % bf16 MFMA peak (N=4096,d=128); decode % HBM BW",
         "value": round(value, 3) if value is not None else None,
@@ -315,13 +464,17 @@ def main():
                                "forward, 64x32 ragged decode d=128 lengths U[512,8192] from a dense and "
                                "from a 64-token paged cache and with a 1024 window, causal backward B=2 H=16 "
                                "N=4096 d=128 without and with a 1024 window, the causal forward, the decode "
-                               "and the causal backward in fp16)",
+                               "and the causal backward in fp16, and the B=1 H=8 N=1024 d=64 forward with "
+                               "64x64 tiles, full and causal)",
                    "global_batch": B3, "seq_len": N3, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(value, 3) if value is not None else None,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(value / PEAK_BF16_TFLOPS, 4) if value is not None else None,
                      "traffic": measured_traffic("fwd_bf16_causal"),
-                     "kernel": "fwd_pingpong_kernel<128> (causal; the automatic tile for this shape is 256 query rows)"},
+                     "kernel": kernel3, "time": "median over the timed steps of the stage's event pair",
+                     "traffic_source": traffic_note("fwd_bf16_causal")},
+        "gpu_clock": {"timed_steps": clock.summary("timed"), "back_to_back": clock.summary("b2b"),
+                      "warmup": clock.summary("warmup")},
         "components": components,
     }
     if not args.no_cpu_baseline and "fwd" in stages:
