@@ -198,6 +198,35 @@ fa_status fa_decode(const void* q, const void* kcache, const void* vcache,
                     void* workspace, size_t workspace_bytes, fa_dtype dtype, void* stream);
 
 /*
+ * fa_decode_noalloc -- fa_decode that allocates nothing and takes no
+ * workspace, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same operation, arguments (minus the workspace), layouts, kernels and
+ * results as fa_decode.  The split partials go to a static device array of
+ * FA_DECODE_NOALLOC_SCRATCH_BYTES (32 MiB) that the library holds on every
+ * device it runs on until the process ends; its address is looked up on the
+ * first call on each device (that call must be made with the device
+ * current).  The array needs no clearing between calls.
+ *
+ *   Limit: fa_decode_workspace_size(S, H, Lmax, d, chunk) must not exceed
+ *   FA_DECODE_NOALLOC_SCRATCH_BYTES; larger requests return
+ *   FA_ERR_WORKSPACE before any HIP call (e.g. d = 128 with splits of 1024
+ *   tokens covers S * H * ceil(Lmax / 1024) up to 64,527 partials).
+ *   `stream` must belong to the current device (else FA_ERR_HIP).
+ *   Concurrency: every call on one device shares that device's array, so
+ *   calls that can overlap on one device (different streams, or other host
+ *   threads) race and give wrong results; serialise them.
+ *
+ * Supported: as fa_decode.
+ */
+#define FA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+fa_status fa_decode_noalloc(const void* q, const void* kcache, const void* vcache,
+                            const int32_t* seqlens, void* o, float* lse,
+                            int S, int H, int Lmax, int d, float scale, int window, int chunk,
+                            fa_dtype dtype, void* stream);
+
+/*
  * fa_decode_paged -- fa_decode over a paged KV cache.
  *
  * The cache of "Build a FlashAttention Kernel with Online Softmax and KV

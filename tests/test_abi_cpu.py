@@ -95,6 +95,29 @@ def test_decode_rejects_bad_arguments(lib):
     assert "workspace" in fa355.last_error()
 
 
+def test_decode_noalloc_rejects_bad_arguments_and_oversized_requests(lib):
+    def call(**kw):
+        a = dict(q=FAKE, kc=FAKE, vc=FAKE, sl=FAKE, o=FAKE, S=2, H=2, L=128, d=128, scale=0.1,
+                 window=-1, chunk=0, dtype=1)
+        a.update(kw)
+        return lib.fa_decode_noalloc(a["q"], a["kc"], a["vc"], a["sl"], a["o"], None, a["S"], a["H"],
+                                     a["L"], a["d"], a["scale"], a["window"], a["chunk"], a["dtype"], None)
+    assert call(q=None) == 1
+    assert call(S=0) == 1
+    assert call(chunk=100) == 1
+    assert call(window=-5) == 1
+    assert call(scale=float("inf")) == 1
+    assert call(d=96) == 2
+    # 64 x 32 caches of 8192 rows in 64-token splits: 136 MB of partials, above
+    # the 32 MiB static scratch -- refused before any HIP call
+    assert call(S=64, H=32, L=8192, chunk=64) == 3
+    assert "static scratch" in fa355.last_error()
+    # the largest request that fits (d = 128, 1024-token splits): 64,527 partials
+    assert fa355.fa_decode_workspace_size(64527, 1, 1024, 128, 1024) <= 32 << 20
+    assert fa355.fa_decode_workspace_size(64528, 1, 1024, 128, 1024) > 32 << 20
+    assert call(S=64528, H=1, L=1024, chunk=1024) == 3
+
+
 def test_tune_rejects_bad_arguments_and_starts_empty(lib):
     def call(**kw):
         a = dict(q=FAKE, B=1, H=2, N=64, d=128, scale=0.1, causal=1, window=-1, dtype=1, reps=5)

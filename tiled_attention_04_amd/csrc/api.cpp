@@ -91,6 +91,30 @@ int tuned_block_q(const TuneKey& key) {
 
 constexpr int kTuneCandidates[4] = {32, 64, 128, 256};
 
+// Checks of a dense decode call; on success `chunk` holds the split length
+// the call will use (the automatic one when it was 0).
+fa_status check_decode(const void* q, const void* kcache, const void* vcache, const int32_t* seqlens,
+                       const void* o, int S, int H, int Lmax, int d, float scale, int window,
+                       int& chunk, int dtype) {
+  if (!q || !kcache || !vcache || !seqlens || !o)
+    return fail(FA_ERR_INVALID_ARG, "q, kcache, vcache, seqlens and o must be non-null");
+  if (S <= 0 || H <= 0 || Lmax <= 0 || d <= 0)
+    return fail(FA_ERR_INVALID_ARG, "sizes must be positive (S=%d H=%d Lmax=%d d=%d)", S, H, Lmax, d);
+  if ((long long)S * H > INT_MAX) return fail(FA_ERR_INVALID_ARG, "S*H exceeds 2^31-1");
+  if (window < -1) return fail(FA_ERR_INVALID_ARG, "window must be -1 (off) or >= 0 (got %d)", window);
+  if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite");
+  if (chunk < 0 || chunk % 64 != 0)
+    return fail(FA_ERR_INVALID_ARG, "chunk must be 0 (auto) or a positive multiple of 64 (got %d)", chunk);
+  if (!valid_dtype(dtype)) return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "decode supports d in {64, 128} (got %d)", d);
+  if ((long long)Lmax * d * (long long)elem_bytes((fa_dtype)dtype) > kMaxBufferBytes)
+    return fail(FA_ERR_UNSUPPORTED, "one (sequence, head) cache slice exceeds 2 GiB");
+  if (chunk == 0) chunk = fa::decode_auto_chunk(S, H, Lmax, window);
+  const long long nchunk = (Lmax + chunk - 1) / chunk;
+  if (nchunk * S * H * 256 > kMaxThreadsPerLaunch) return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -275,22 +299,9 @@ fa_status fa_decode(const void* q, const void* kcache, const void* vcache, const
                     void* o, float* lse, int S, int H, int Lmax, int d, float scale, int window,
                     int chunk, void* workspace, size_t workspace_bytes, fa_dtype dtype,
                     void* stream) {
-  if (!q || !kcache || !vcache || !seqlens || !o)
-    return fail(FA_ERR_INVALID_ARG, "q, kcache, vcache, seqlens and o must be non-null");
-  if (S <= 0 || H <= 0 || Lmax <= 0 || d <= 0)
-    return fail(FA_ERR_INVALID_ARG, "sizes must be positive (S=%d H=%d Lmax=%d d=%d)", S, H, Lmax, d);
-  if ((long long)S * H > INT_MAX) return fail(FA_ERR_INVALID_ARG, "S*H exceeds 2^31-1");
-  if (window < -1) return fail(FA_ERR_INVALID_ARG, "window must be -1 (off) or >= 0 (got %d)", window);
-  if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite");
-  if (chunk < 0 || chunk % 64 != 0)
-    return fail(FA_ERR_INVALID_ARG, "chunk must be 0 (auto) or a positive multiple of 64 (got %d)", chunk);
-  if (!valid_dtype(dtype)) return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
-  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "decode supports d in {64, 128} (got %d)", d);
-  if ((long long)Lmax * d * (long long)elem_bytes(dtype) > kMaxBufferBytes)
-    return fail(FA_ERR_UNSUPPORTED, "one (sequence, head) cache slice exceeds 2 GiB");
-  if (chunk == 0) chunk = fa::decode_auto_chunk(S, H, Lmax, window);
-  const long long nchunk = (Lmax + chunk - 1) / chunk;
-  if (nchunk * S * H * 256 > kMaxThreadsPerLaunch) return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  const fa_status st = check_decode(q, kcache, vcache, seqlens, o, S, H, Lmax, d, scale, window, chunk,
+                                    (int)dtype);
+  if (st != FA_OK) return st;
   const size_t need = fa::decode_workspace_bytes(S, H, Lmax, d, chunk);
   if (!workspace || workspace_bytes < need)
     return fail(FA_ERR_WORKSPACE, "decode needs %zu workspace bytes (got %zu%s)", need, workspace_bytes,
@@ -298,6 +309,26 @@ fa_status fa_decode(const void* q, const void* kcache, const void* vcache, const
   return done(fa::launch_decode(q, kcache, vcache, seqlens, o, lse, S, H, Lmax, d, scale, window, chunk,
                                 workspace, elem_of(dtype), (hipStream_t)stream),
               "fa_decode");
+}
+
+fa_status fa_decode_noalloc(const void* q, const void* kcache, const void* vcache,
+                            const int32_t* seqlens, void* o, float* lse, int S, int H, int Lmax, int d,
+                            float scale, int window, int chunk, fa_dtype dtype, void* stream) {
+  static_assert(fa::kDecodeScratchBytes == FA_DECODE_NOALLOC_SCRATCH_BYTES,
+                "the header states the scratch size");
+  const fa_status st = check_decode(q, kcache, vcache, seqlens, o, S, H, Lmax, d, scale, window, chunk,
+                                    (int)dtype);
+  if (st != FA_OK) return st;
+  const size_t need = fa::decode_workspace_bytes(S, H, Lmax, d, chunk);
+  if (need > fa::kDecodeScratchBytes)
+    return fail(FA_ERR_WORKSPACE,
+                "fa_decode_noalloc: %d splits of %d tokens for %d x %d (sequence, head) pairs need %zu "
+                "bytes of partials, above its %zu-byte static scratch (use fa_decode with a workspace, "
+                "or longer splits)",
+                (int)((Lmax + chunk - 1) / chunk), chunk, S, H, need, (size_t)fa::kDecodeScratchBytes);
+  return done(fa::launch_decode_noalloc(q, kcache, vcache, seqlens, o, lse, S, H, Lmax, d, scale, window,
+                                        chunk, elem_of(dtype), (hipStream_t)stream),
+              "fa_decode_noalloc");
 }
 
 fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_pages,

@@ -26,6 +26,8 @@
 #include "fa_common.h"
 #include "fa_launch.h"
 
+#include <mutex>
+
 namespace fa {
 namespace {
 
@@ -328,6 +330,57 @@ hipError_t dispatch(const void* q, const void* kc, const void* vc, const int32_t
 hipError_t launch_decode(const void* q, const void* kc, const void* vc, const int32_t* seqlens,
                          void* o, float* lse, int S, int H, int Lmax, int d, float scale,
                          int window, int chunk, void* ws, Elem elem, hipStream_t stream) {
+  return dispatch(q, kc, vc, seqlens, o, lse, S, H, Lmax, d, scale, window, chunk, ws, elem,
+                  PagedCache{nullptr, 0, 0, 0}, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Decode without a caller workspace, for callers that cannot allocate.  The
+// split partials go to `scratch`, a fixed array in device memory: the loader
+// places one copy on every device the library runs on, and it stays until the
+// process ends.  Its device address is looked up once per device with
+// hipGetSymbolAddress (in host code the array's name is only a stand-in, not
+// an address a kernel can use) and kept in `g_scratch_ptr`.  Every call on a
+// device shares that device's copy, so calls that overlap on one device race;
+// nothing in it needs clearing, because the merge kernel reads only the
+// partials its own split kernel wrote in the same call.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_ptr(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (stream != nullptr) {  // the partials must live on the stream's device
+    int sdev = 0;
+    err = hipStreamGetDevice(stream, &sdev);
+    if (err != hipSuccess) return err;
+    if (sdev != dev) return hipErrorInvalidDevice;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_decode_noalloc(const void* q, const void* kc, const void* vc, const int32_t* seqlens,
+                                 void* o, float* lse, int S, int H, int Lmax, int d, float scale,
+                                 int window, int chunk, Elem elem, hipStream_t stream) {
+  void* ws = nullptr;
+  const hipError_t err = scratch_ptr(stream, &ws);
+  if (err != hipSuccess) return err;
   return dispatch(q, kc, vc, seqlens, o, lse, S, H, Lmax, d, scale, window, chunk, ws, elem,
                   PagedCache{nullptr, 0, 0, 0}, stream);
 }

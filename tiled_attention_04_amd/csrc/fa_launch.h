@@ -42,6 +42,15 @@ hipError_t launch_decode_paged(const void* q, const void* k_pages, const void* v
                                float scale, int window, int chunk, void* ws, Elem elem,
                                hipStream_t stream);
 
+// The same dense decode with its partials in a static device array of
+// kDecodeScratchBytes per device instead of a caller workspace (the caller
+// has checked that decode_workspace_bytes fits).  No allocation; calls that
+// overlap on one device race on the array.
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+hipError_t launch_decode_noalloc(const void* q, const void* kc, const void* vc, const int32_t* seqlens,
+                                 void* o, float* lse, int S, int H, int Lmax, int d, float scale,
+                                 int window, int chunk, Elem elem, hipStream_t stream);
+
 // 16-bit backward (bf16, or fp16 when f16): preprocess, dK/dV and dQ
 // kernels, d in {64, 128}.
 size_t bwd_workspace_bytes(int B, int H, int N, int d);

@@ -39,6 +39,7 @@ SIGNATURES = {
     "fa_tune_import": (_I, [_P, _I]),
     "fa_decode_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
     "fa_decode": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _I, _P]),
+    "fa_decode_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
     "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _Z,
                              _I, _P]),
     "fa_bwd_workspace_size": (_Z, [_I, _I, _I, _I]),
@@ -239,6 +240,31 @@ def fa_decode(q, kcache, vcache, seqlens, *, scale=None, window: int = -1, chunk
     _check(lib().fa_decode(qp, kp, vp, sp, op, lp, S, H, Lmax, d, _default_scale(scale, d),
                            int(window), int(chunk), wp, workspace.numel() * workspace.element_size(),
                            _DTYPE[dt], _stream(stream)))
+    return o, lse
+
+
+def fa_decode_noalloc(q, kcache, vcache, seqlens, *, scale=None, window: int = -1, chunk: int = 0,
+                      o=None, lse=None, stream=None):
+    """fa_decode without a workspace: the library keeps the split partials in
+    a static 32 MiB device array (calls that overlap on one device race).
+    Allocates only the outputs when o / lse are not given."""
+    S, H, d = q.shape
+    Lmax = kcache.shape[2]
+    dt = q.dtype
+    if dt not in _DTYPE:
+        raise ValueError(f"unsupported dtype {dt}")
+    qp = _dev(q, "q", dt)
+    kp = _dev(kcache, "kcache", dt, (S, H, Lmax, d))
+    vp = _dev(vcache, "vcache", dt, (S, H, Lmax, d))
+    sp = _dev(seqlens, "seqlens", torch.int32, (S,))
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((S, H), dtype=torch.float32, device=q.device)
+    op = _dev(o, "o", dt, q.shape)
+    lp = _dev(lse, "lse", torch.float32, (S, H))
+    _check(lib().fa_decode_noalloc(qp, kp, vp, sp, op, lp, S, H, Lmax, d, _default_scale(scale, d),
+                                   int(window), int(chunk), _DTYPE[dt], _stream(stream)))
     return o, lse
 
 
