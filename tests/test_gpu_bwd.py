@@ -129,3 +129,41 @@ def test_many_heads_256_row_dq_tiles(B, H, N, d, causal, window):
         check_bf16(dq[:, h:h + 1], rq, f"dQ[h={h}]")
         check_bf16(dk[:, h:h + 1], rk, f"dK[h={h}]")
         check_bf16(dv[:, h:h + 1], rv, f"dV[h={h}]")
+
+
+@pytest.mark.parametrize("N,d", [(65, 128), (300, 64)])
+def test_outputs_written_only_in_bounds(N, d):
+    """Guard bands after dq, dk, dv and the workspace stay untouched."""
+    B, H = 1, 2
+    q, k, v, dO = (t.cuda() for t in attention_inputs(B, H, N, d, "bf16", seed=N, with_grad=True))
+    o, lse = fa.fa_fwd(q, k, v, causal=True)
+    n = B * H * N * d
+    bufs = [torch.full((n + 4096,), 7.0, dtype=torch.float32, device="cuda") for _ in range(3)]
+    need = fa.fa_bwd_workspace_size(B, H, N, d)
+    wbuf = torch.full((need // 4 + 4096,), 7.0, dtype=torch.float32, device="cuda")
+    dq, dk, dv = (b[:n].view(B, H, N, d) for b in bufs)
+    fa.fa_bwd(q, k, v, o, dO, lse, causal=True, dq=dq, dk=dk, dv=dv, workspace=wbuf[:need // 4])
+    torch.cuda.synchronize()
+    for b, name in zip(bufs, ("dq", "dk", "dv")):
+        assert torch.all(b[n:] == 7.0), name
+    assert torch.all(wbuf[need // 4:] == 7.0)
+    rq, rk, rv = oracle.attention_bwd_ref(q.cpu(), k.cpu(), v.cpu(), dO.cpu(), 1 / math.sqrt(d), True)
+    check_bf16(dq.cpu(), rq, "dQ")
+    check_bf16(dk.cpu(), rk, "dK")
+    check_bf16(dv.cpu(), rv, "dV")
+
+
+@pytest.mark.parametrize("factor", [0.0, -1.0, 0.6])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal,window", [(True, -1), (True, 40), (False, 30), (False, -1)])
+def test_scale_values(factor, d, causal, window):
+    """Zero and negative scales (legal: the scale is taken as given); the
+    masks must still hide their pairs exactly.  Magnitudes stay at the
+    default 1/sqrt(d) or below, where the bf16 bar applies."""
+    scale = factor / math.sqrt(d)
+    q, k, v, dO = attention_inputs(1, 2, 200, d, "bf16", seed=21 + d, with_grad=True)
+    dq, dk, dv = run(q, k, v, dO, causal, window, scale)
+    rq, rk, rv = oracle.attention_bwd_ref(q, k, v, dO, scale, causal, window)
+    check_bf16(dq, rq, "dQ")
+    check_bf16(dk, rk, "dK")
+    check_bf16(dv, rv, "dV")

@@ -195,3 +195,34 @@ def test_full_size_ragged_paged_decode():
                                        1 / math.sqrt(w["d"]))
         check_bf16(o[s], O[0], f"o[{s}]")
         check_lse(lse[s], L[0], f"lse[{s}]")
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("window", [-1, 50])
+def test_outputs_written_only_in_bounds(paged, window):
+    """Guard bands after o, lse and the workspace stay untouched."""
+    lens = [1, 130, 257, 64]
+    S, H, d = len(lens), 3, 128
+    inp = decode_inputs(S, H, d, 1, 257, seed=9, seqlens=lens)
+    sl = torch.from_numpy(inp.seqlens).cuda()
+    n = S * H * d
+    obuf = torch.full((n + 4096,), 7.0, dtype=torch.bfloat16, device="cuda")
+    lbuf = torch.full((S * H + 1024,), 7.0, dtype=torch.float32, device="cuda")
+    o, lse = obuf[:n].view(S, H, d), lbuf[:S * H].view(S, H)
+    if paged:
+        kp, vp, table = paged_cache(inp, 64, device="cuda", seed=3, spare_pages=1)
+        need = fa.fa_decode_workspace_size(S, H, table.shape[1] * 64, d)
+        wbuf = torch.full((need // 4 + 4096,), 7.0, dtype=torch.float32, device="cuda")
+        fa.fa_decode_paged(inp.q.cuda(), kp, vp, table, sl, window=window, o=o, lse=lse,
+                           workspace=wbuf[:need // 4])
+    else:
+        kc, vc = dense_cache(inp, 257, device="cuda")
+        need = fa.fa_decode_workspace_size(S, H, 257, d)
+        wbuf = torch.full((need // 4 + 4096,), 7.0, dtype=torch.float32, device="cuda")
+        fa.fa_decode(inp.q.cuda(), kc, vc, sl, window=window, o=o, lse=lse, workspace=wbuf[:need // 4])
+    torch.cuda.synchronize()
+    assert torch.all(obuf[n:] == 7.0) and torch.all(lbuf[S * H:] == 7.0)
+    assert torch.all(wbuf[need // 4:] == 7.0)
+    O, L = oracle_decode(inp, window)
+    check_bf16(o.cpu(), O, "o")
+    check_lse(lse.cpu(), L, "lse")

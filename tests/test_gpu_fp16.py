@@ -132,3 +132,39 @@ def test_fp16_decode(d, window, paged):
     O, L = _decode_oracle(inp, window)
     check_bf16(o.cpu(), O, "o")
     check_lse(lse.cpu(), L, "lse")
+
+
+# ------------------------------------------- full size: the timed fp16 stages
+
+@pytest.mark.slow
+def test_fp16_full_size_ragged_decode():
+    """The fp16 decode stage the bench times: 64 sequences x 32 heads, d=128,
+    lengths U[512, 8192], automatic splits (1024 tokens); every (s, h)."""
+    from tiled_attention_04_amd.inputs import WORKLOADS
+    w = WORKLOADS["decode_s64_h32_d128_len512to8192_bf16"]
+    inp = decode_inputs(w["S"], w["H"], w["d"], w["len_lo"], w["len_hi"], dtype="fp16", seed=0)
+    kc, vc = dense_cache(inp, w["Lmax"], device="cuda")
+    sl = torch.from_numpy(inp.seqlens).cuda()
+    o, lse = fa.fa_decode(inp.q.cuda(), kc, vc, sl)
+    torch.cuda.synchronize()
+    del kc, vc
+    O, L = _decode_oracle(inp, -1)
+    check_bf16(o.cpu(), O, "o")
+    check_lse(lse.cpu(), L, "lse")
+
+
+@pytest.mark.slow
+def test_fp16_full_size_backward_sampled_heads():
+    """The fp16 backward stage the bench times: B=2, H=16, N=4096, d=128,
+    causal (the 256-row dQ kernel); two whole heads against the oracle."""
+    q, k, v, dO = attention_inputs(2, 16, 4096, 128, "fp16", seed=0, with_grad=True)
+    qd, kd, vd, gd = (t.cuda() for t in (q, k, v, dO))
+    o, lse = fa.fa_fwd(qd, kd, vd, causal=True)
+    dq, dk, dv = fa.fa_bwd(qd, kd, vd, o, gd, lse, causal=True)
+    torch.cuda.synchronize()
+    for b, h in ((0, 4), (1, 13)):
+        rq, rk, rv = oracle.attention_bwd_ref(q[b, h][None], k[b, h][None], v[b, h][None],
+                                              dO[b, h][None], 1 / math.sqrt(128), True)
+        check_bf16(dq[b, h].cpu(), rq[0], f"dQ[{b},{h}]")
+        check_bf16(dk[b, h].cpu(), rk[0], f"dK[{b},{h}]")
+        check_bf16(dv[b, h].cpu(), rv[0], f"dV[{b},{h}]")

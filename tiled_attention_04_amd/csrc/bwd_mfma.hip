@@ -200,6 +200,14 @@ void bwd_main_kernel(const T* __restrict__ q, const T* __restrict__ k,
   using std::integral_constant;
   // Prologue: the first query tile resident.
   if (qt0 < qt1) load_qtile(qt0, integral_constant<int, 0>{});
+  // The K and V rows above must be in flight together with this tile's
+  // loads: left to itself the compiler issued them only after the wait
+  // below, so the two round trips to memory ran one after the other.  An
+  // empty asm that reads them here keeps them ahead of the wait.
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+  for (int s = 0; s < KS; ++s) asm volatile("" : "+v"(kf[s]), "+v"(vf[s]));
+#endif
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 

@@ -293,20 +293,17 @@ void fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k,
   }
 
   // Q rows of this wave as MFMA B fragments: Q[qi][16 s + 8 h + 0..7]
-  // (rows >= N read as zero).
+  // (rows >= N read as zero).  The loads are issued here together with the
+  // first K/V tiles; the sign flip for a negative scale (S * scale =
+  // (-S) * |scale|, exact in bf16 and fp16) is applied once they have landed,
+  // without a branch: a branch on each loaded value made every load wait
+  // for the one before it.
   const rsrc_t q_src = make_rsrc(q + base, (uint32_t)N * D * 2u);
-  vec8<T> qf[KS];
+  const uint32_t q_neg = negate_q ? 0x80008000u : 0u;
+  uint4 q_raw[KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    uint4 u = load16(q_src, (uint32_t)(qi * D + 16 * s + 8 * h) * 2u);
-    if (negate_q) {  // negative scale: S * scale = (-S) * |scale|, exact in bf16 and fp16
-      u.x ^= 0x80008000u;
-      u.y ^= 0x80008000u;
-      u.z ^= 0x80008000u;
-      u.w ^= 0x80008000u;
-    }
-    qf[s] = as_vec8<T>(u);
-  }
+  for (int s = 0; s < KS; ++s) q_raw[s] = load16(q_src, (uint32_t)(qi * D + 16 * s + 8 * h) * 2u);
+  vec8<T> qf[KS];
 
   // Key tiles holding at least one visible key for this query tile.
   const int q_hi = q0 + BQ - 1;
@@ -338,6 +335,9 @@ void fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k,
     load_tile<D, NW, TL::kKBlocks, TL::kKPitch, PRE>(kg, (kt0 + 1) * kBK, N, Kb1, kpre, w, lane);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+    qf[s] = as_vec8<T>(uint4{q_raw[s].x ^ q_neg, q_raw[s].y ^ q_neg, q_raw[s].z ^ q_neg, q_raw[s].w ^ q_neg});
 
   // S^T = K Q^T of the first tile for its two 32-key blocks.
   f32x16 s_a[2];
@@ -561,19 +561,13 @@ void fwd_pingpong_kernel(const T* __restrict__ q, const T* __restrict__ k,
   const int k_nblk = (TL::kKBlocks - w + NW - 1) / NW;  // K / V blocks this wave loads per tile
   const int v_nblk = (TL::kVBlocks - w + NW - 1) / NW;
 
+  // Q rows (sign-flipped after the prologue's wait, as in fwd_mfma_kernel).
   const rsrc_t q_src = make_rsrc(q + base, (uint32_t)N * D * 2u);
-  vec8<T> qf[KS];
+  const uint32_t q_neg = negate_q ? 0x80008000u : 0u;
+  uint4 q_raw[KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    uint4 u = load16(q_src, (uint32_t)(qi * D + 16 * s + 8 * h) * 2u);
-    if (negate_q) {
-      u.x ^= 0x80008000u;
-      u.y ^= 0x80008000u;
-      u.z ^= 0x80008000u;
-      u.w ^= 0x80008000u;
-    }
-    qf[s] = as_vec8<T>(u);
-  }
+  for (int s = 0; s < KS; ++s) q_raw[s] = load16(q_src, (uint32_t)(qi * D + 16 * s + 8 * h) * 2u);
+  vec8<T> qf[KS];
 
   const int q_hi = q0 + BQ - 1;
   const int kmin = window >= 0 ? max(0, q0 - window) : 0;
@@ -647,6 +641,9 @@ void fwd_pingpong_kernel(const T* __restrict__ q, const T* __restrict__ k,
     wait_vm(v_nblk + (kt0 + 1 < kt1 ? k_nblk + v_nblk : 0));
   }
   barrier_keep_loads();
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+    qf[s] = as_vec8<T>(uint4{q_raw[s].x ^ q_neg, q_raw[s].y ^ q_neg, q_raw[s].z ^ q_neg, q_raw[s].w ^ q_neg});
 #pragma unroll
   for (int kb2 = 0; kb2 < 2; ++kb2) {
     sc[kb2] = f32x16{};
