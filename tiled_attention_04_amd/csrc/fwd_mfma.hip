@@ -64,6 +64,8 @@ struct Tile {
   static constexpr int kVBlocks = kVBytes / 1024;
   static_assert(kKBytes % 1024 == 0 && kVBytes % 1024 == 0, "tiles must be whole 1 KB blocks");
   static constexpr int kSmem = 2 * (kKBytes + kVBytes);
+  // Two waves' O blocks (32 rows of 2 D + 16 bytes each) fit a K tile.
+  static_assert(2 * 32 * (2 * D + 16) <= kKBytes && 2 * 32 * (2 * D + 16) <= kVBytes, "O staging");
 };
 
 // Issue this wave's share of the direct loads of one tile (rows k0.. of a
@@ -212,6 +214,39 @@ __device__ __forceinline__ void softmax_tile(const f32x16 (&s)[2], uint32_t (&pk
     for (int cb = 0; cb < CB; ++cb) oacc[cb] *= alpha;
   }
   l_run += exps(m_ref);
+}
+
+// Store this wave's 32 x D block of O (rows r0 .. r0 + 31 of the slice at
+// o_slice; rows at or past N dropped), normalised by inv, through `stage`,
+// a region of 32 * (2 D + 16) bytes of LDS that only this wave uses.  The
+// accumulator layout gives each lane 8-byte pieces of 32 different rows, so
+// storing from it directly splits every store instruction into 32 partial
+// cache lines; written to LDS in that layout and read back row by row, each
+// store instruction writes whole 2D-byte rows instead.  (Rows padded by 16
+// bytes: 16-byte aligned reads, at most 2-way conflicts on the writes.)
+template <typename T, int D, int CB>
+__device__ __forceinline__ void store_o_rows(const f32x16 (&oacc)[CB], float inv, char* stage,
+                                             T* __restrict__ o_slice, int r0, int N, int lane) {
+  constexpr int P = 2 * D + 16;
+  constexpr int CPR = D / 8;      // 16-byte chunks per row
+  constexpr int RPP = 64 / CPR;   // rows per wave-wide read
+  const int h = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      uint2 st;
+      st.x = pack2<T>(oacc[cb][4 * gq + 0] * inv, oacc[cb][4 * gq + 1] * inv);
+      st.y = pack2<T>(oacc[cb][4 * gq + 2] * inv, oacc[cb][4 * gq + 3] * inv);
+      *(uint2*)(stage + l32 * P + (cb * 32 + 8 * gq + 4 * h) * 2) = st;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 32 / RPP; ++i) {
+    const int row = i * RPP + lane / CPR, ch = lane % CPR;
+    const uint4 u = *(const uint4*)(stage + row * P + ch * 16);
+    if (r0 + row < N) *(uint4*)((char*)(o_slice + (size_t)(r0 + row) * D) + ch * 16) = u;
+  }
 }
 
 // Scheduling groups (masks of __builtin_amdgcn_sched_group_barrier).
@@ -422,21 +457,12 @@ void fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k,
   // Epilogue: O = O / l, L = m ln2 + ln l.
   const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (qi < N) {
-    T* orow = o + base + (size_t)qi * D;
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        uint2 st;
-        st.x = pack2<T>(oacc[cb][4 * gq + 0] * inv, oacc[cb][4 * gq + 1] * inv);
-        st.y = pack2<T>(oacc[cb][4 * gq + 2] * inv, oacc[cb][4 * gq + 3] * inv);
-        *(uint2*)(orow + cb * 32 + 8 * gq + 4 * h) = st;
-      }
-    }
-    if (h == 0 && lse != nullptr)
-      lse[(size_t)bh * N + qi] = l_tot > 0.f ? m_ref * kLn2 + logf(l_tot) : kNegInf;
-  }
+  // O through LDS (the loop's last barrier freed the K buffers): two waves
+  // per buffer.
+  store_o_rows<T, D, CB>(oacc, inv, (w < 2 ? Kb0 : Kb1) + (w & 1) * 32 * (2 * D + 16), o + base,
+                         q0 + 32 * w, N, lane);
+  if (qi < N && h == 0 && lse != nullptr)
+    lse[(size_t)bh * N + qi] = l_tot > 0.f ? m_ref * kLn2 + logf(l_tot) : kNegInf;
 }
 
 // ---------------------------------------------------------------------------
@@ -745,21 +771,12 @@ void fwd_pingpong_kernel(const T* __restrict__ q, const T* __restrict__ k,
 
   const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (qi < N) {
-    T* orow = o + base + (size_t)qi * D;
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        uint2 st;
-        st.x = pack2<T>(oacc[cb][4 * gq + 0] * inv, oacc[cb][4 * gq + 1] * inv);
-        st.y = pack2<T>(oacc[cb][4 * gq + 2] * inv, oacc[cb][4 * gq + 3] * inv);
-        *(uint2*)(orow + cb * 32 + 8 * gq + 4 * h) = st;
-      }
-    }
-    if (h == 0 && lse != nullptr)
-      lse[(size_t)bh * N + qi] = l_tot > 0.f ? m_ref * kLn2 + logf(l_tot) : kNegInf;
-  }
+  // O through LDS (after the last barrier no wave reads the stages): two
+  // waves per K stage, the last two in V stage 0.
+  store_o_rows<T, D, CB>(oacc, inv, (w < 2 ? K0 : w < 4 ? K1 : w < 6 ? K2 : V0) + (w & 1) * 32 * (2 * D + 16),
+                         o + base, q0 + 32 * w, N, lane);
+  if (qi < N && h == 0 && lse != nullptr)
+    lse[(size_t)bh * N + qi] = l_tot > 0.f ? m_ref * kLn2 + logf(l_tot) : kNegInf;
 }
 
 
