@@ -333,6 +333,41 @@ void bwd_main_kernel(const T* __restrict__ q, const T* __restrict__ k,
   }
 }
 
+// Store this wave's 32 x D block of dQ (rows r0 .. r0 + 31 of the slice,
+// rows at or past N dropped), scaled, through `stage`: 32 * (2 D + 16) bytes
+// of LDS that only this wave uses, half of the columns at a time.  In the
+// accumulator layout a lane holds 16-byte pieces of 32 different rows, so
+// storing from it directly splits every store instruction into 32 pieces of
+// 32 bytes; read back row by row from LDS each store instruction writes
+// whole half-rows of 2 D bytes.
+template <int D, int CB>
+__device__ __forceinline__ void store_dq_rows(const f32x16 (&dqa)[CB], float scale, char* stage,
+                                              float* __restrict__ dq_slice, int r0, int N, int lane) {
+  constexpr int P = 2 * D + 16;
+  constexpr int HB = CB / 2;          // 32-column blocks per half
+  constexpr int CPR = 2 * D / 16;     // 16-byte chunks per half row
+  constexpr int RPP = 64 / CPR;       // half rows per wave-wide read
+  const int h = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int c = 0; c < HB; ++c)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x16& a = dqa[half * HB + c];
+        *(float4*)(stage + l32 * P + (32 * c + 8 * g + 4 * h) * 4) =
+            float4{scale * a[4 * g], scale * a[4 * g + 1], scale * a[4 * g + 2], scale * a[4 * g + 3]};
+      }
+#pragma unroll
+    for (int i = 0; i < 32 / RPP; ++i) {
+      const int row = i * RPP + lane / CPR, ch = lane % CPR;
+      const uint4 u = *(const uint4*)(stage + row * P + ch * 16);
+      if (r0 + row < N)
+        *(uint4*)((char*)(dq_slice + (size_t)(r0 + row) * D + half * (D / 2)) + ch * 16) = u;
+    }
+  }
+}
+
 // dQ kernel: dQ = scale * dS K without atomics.  A workgroup of 4 waves owns
 // 128 query rows (32 per wave, one per lane pair as in the forward kernels)
 // and walks the 64-key tiles they see, recomputing per tile
@@ -356,6 +391,8 @@ struct DqTile {
   static constexpr int kKBlocks = kKBytes / 1024;
   static constexpr int kVBlocks = kVBytes / 1024;
   static_assert(kKBytes % 1024 == 0 && kVBytes % 1024 == 0, "tiles must be whole 1 KB blocks");
+  // Two waves' dQ half-blocks (32 rows of 2 D + 16 bytes each) fit a tile.
+  static_assert(2 * 32 * (2 * D + 16) <= kKBytes && 2 * 32 * (2 * D + 16) <= kVBytes, "dQ staging");
 };
 
 // (d = 128 may run one wave per SIMD: this kernel serves grids too small for
@@ -517,16 +554,10 @@ void bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k,
 
   // dQ row qi: element r of block cb is column 32 cb + c_row(r, h); four
   // consecutive columns per 16-byte store.
-  if (row_ok) {
-    float* drow = dq + base + (size_t)qi * D;
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *(float4*)(drow + 32 * cb + 8 * g + 4 * h) =
-            float4{scale * dqa[cb][4 * g], scale * dqa[cb][4 * g + 1], scale * dqa[cb][4 * g + 2],
-                   scale * dqa[cb][4 * g + 3]};
-  }
+  // dQ through LDS (the loop's last barrier freed the K tiles): two waves
+  // per tile.
+  store_dq_rows<D, CB>(dqa, scale, (w < 2 ? Kb0 : Kb1) + (w & 1) * 32 * (2 * D + 16), dq + base,
+                       q0 + 32 * w, N, lane);
 }
 
 // Ping-pong dQ kernel for long sequences: 8 waves, 256 query rows per
@@ -550,6 +581,8 @@ struct DqPPTile {
   static constexpr int kKBlocks = kKBytes / 1024;
   static constexpr int kVBlocks = kVBytes / 1024;
   static_assert(kKBytes % 1024 == 0 && kVBytes % 1024 == 0, "tiles must be whole 1 KB blocks");
+  // Two waves' dQ half-blocks (32 rows of 2 D + 16 bytes each) fit a tile.
+  static_assert(2 * 32 * (2 * D + 16) <= kKBytes && 2 * 32 * (2 * D + 16) <= kVBytes, "dQ staging");
 };
 
 // Keeps the vector-ALU results of a phase on their side of the barrier that
@@ -781,16 +814,10 @@ void bwd_dq_pp_kernel(const T* __restrict__ q, const T* __restrict__ k,
   }
   if (grp == 0) barrier_keep_loads();  // match group 1's extra barrier
 
-  if (row_ok) {
-    float* drow = dq + base + (size_t)qi * D;
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *(float4*)(drow + 32 * cb + 8 * g + 4 * h) =
-            float4{scale * dqa[cb][4 * g], scale * dqa[cb][4 * g + 1], scale * dqa[cb][4 * g + 2],
-                   scale * dqa[cb][4 * g + 3]};
-  }
+  // dQ through LDS (after the last barrier no wave reads the stages): two
+  // waves per K stage, the last two in V stage 0.
+  store_dq_rows<D, CB>(dqa, scale, (w < 2 ? K0 : w < 4 ? K1 : w < 6 ? K2 : V0) + (w & 1) * 32 * (2 * D + 16),
+                       dq + base, q0 + 32 * w, N, lane);
 }
 
 template <typename T, int D>
