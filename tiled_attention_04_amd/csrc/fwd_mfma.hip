@@ -586,6 +586,8 @@ void fwd_pingpong_kernel(const T* __restrict__ q, const T* __restrict__ k,
   for (int i = 0; i < VPER; ++i) vpre[i] = block_src<D>(w + i * NW, lane, TL::kVPitch);
   const int k_nblk = (TL::kKBlocks - w + NW - 1) / NW;  // K / V blocks this wave loads per tile
   const int v_nblk = (TL::kVBlocks - w + NW - 1) / NW;
+  constexpr int kVMin = TL::kVBlocks / NW;  // fewest V blocks of any wave
+  static_assert(kVMin >= 1, "every wave loads a V block");
 
   // Q rows (sign-flipped after the prologue's wait, as in fwd_mfma_kernel).
   const rsrc_t q_src = make_rsrc(q + base, (uint32_t)N * D * 2u);
@@ -710,8 +712,19 @@ void fwd_pingpong_kernel(const T* __restrict__ q, const T* __restrict__ k,
     }
     pin_softmax_results<CB>(pk, oacc, l_run, m_ref);
     // Group 0: tile kt+1's K must be resident for its matrix phase; its V
-    // and the tiles after it may stay in flight.
-    if (grp == 0) wait_vm((NS > 3 ? n_loads(kt + 2) : 0) + (kt + 1 < kt1 ? v_nblk : 0));
+    // and the tiles after it may stay in flight.  With three stages the
+    // count is the fewest V blocks any wave loads: loads complete in order
+    // and V_{kt+1} was issued last, so waiting until that many remain covers
+    // K_{kt+1} in every wave (a wave with one V block more waits for a load
+    // issued a whole tile ago), and past the last tile there is nothing to
+    // wait for.  A constant keeps the wait a single instruction (a count
+    // known only at run time costs a chain of compares and branches).
+    if (grp == 0) {
+      if constexpr (NS == 3)
+        wait_vm(kVMin);
+      else
+        wait_vm(n_loads(kt + 2) + (kt + 1 < kt1 ? v_nblk : 0));
+    }
     barrier_keep_loads();
     // ---- matrix phase (group 0 issues its loads of tile kt+NS-1 here)
     if (grp == 0 && load_far) load_share(far, integral_constant<int, STF>{});
@@ -751,8 +764,14 @@ void fwd_pingpong_kernel(const T* __restrict__ q, const T* __restrict__ k,
       }
     }
     // Group 1: its K of tile kt+2 must have landed before group 0 needs it in
-    // the next matrix phase; V_{kt+2} and later tiles may stay in flight.
-    if (grp == 1) wait_vm((NS > 3 ? n_loads(kt + 3) : 0) + (kt + 2 < kt1 ? v_nblk : 0));
+    // the next matrix phase; V_{kt+2} and later tiles may stay in flight
+    // (the same constant count as above).
+    if (grp == 1) {
+      if constexpr (NS == 3)
+        wait_vm(kVMin);
+      else
+        wait_vm(n_loads(kt + 3) + (kt + 2 < kt1 ? v_nblk : 0));
+    }
     barrier_keep_loads();
   };
 
