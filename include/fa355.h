@@ -141,21 +141,35 @@ fa_status fa_fwd_tune(const void* q, const void* k, const void* v, void* o, floa
 int fa_fwd_auto_block_q(int B, int H, int N, int d, int causal, int window, fa_dtype dtype,
                         int* tuned);
 
-/* Forget every remembered tile choice (automatic calls use the heuristic again). */
-void fa_tune_reset(void);
-
 /*
- * Save / restore the remembered tile choices, so that a process can start
- * with the choices an earlier one measured.  A row is 7 int64 values:
- * (dtype, d, causal, window, B*H, N, block_q).
+ * Remembered tuning choices.  fa_fwd_tune, fa_decode_tune and fa_bwd_tune
+ * each remember their fastest candidate for the problem they measured;
+ * automatic calls on the same problem then use it.  A choice is a row of
+ * FA_TUNE_ROW int64 values:
+ *   (kind, dtype, d, causal, window, rows, n, value)
+ * with, per kind,
+ *   FA_TUNE_FWD_BLOCK_Q : rows = B * H, n = N, value = block_q
+ *   FA_TUNE_DECODE_CHUNK: causal = 0, rows = S * H, n = Lmax, value = chunk
+ *                         (dense, no-allocation and paged decode alike; for
+ *                         the paged call Lmax = max_pages * page_size)
+ *   FA_TUNE_BWD_DQ_ROWS : rows = B * H, n = N, value = query rows per
+ *                         workgroup of the dQ kernel (128 or 256)
+ * The table is process state guarded by a mutex.
  *
- * fa_tune_export writes up to max_rows rows to `rows` (host memory, 7 *
- * max_rows values) and returns the number of remembered choices (rows may
- * be NULL to query it).  fa_tune_import adds or replaces n_rows choices;
- * it checks every row first (16-bit dtype, d in {64, 128}, causal 0/1,
- * window >= -1, positive sizes, block_q a tuning candidate) and changes
- * nothing on FA_ERR_INVALID_ARG.
+ * fa_tune_reset forgets every choice (automatic calls use the built-in
+ * heuristics again).  fa_tune_export writes up to max_rows rows to `rows`
+ * (host memory, FA_TUNE_ROW * max_rows values) and returns the number of
+ * remembered choices (rows may be NULL to query it).  fa_tune_import adds
+ * or replaces n_rows choices; it checks every row first (known kind,
+ * 16-bit dtype, d in {64, 128}, causal 0/1 (0 for decode), window >= -1,
+ * positive sizes, value a candidate of its kind) and changes nothing on
+ * FA_ERR_INVALID_ARG.
  */
+#define FA_TUNE_FWD_BLOCK_Q 0
+#define FA_TUNE_DECODE_CHUNK 1
+#define FA_TUNE_BWD_DQ_ROWS 2
+#define FA_TUNE_ROW 8
+void fa_tune_reset(void);
 int fa_tune_export(int64_t* rows, int max_rows);
 fa_status fa_tune_import(const int64_t* rows, int n_rows);
 
@@ -196,6 +210,43 @@ fa_status fa_decode(const void* q, const void* kcache, const void* vcache,
                     const int32_t* seqlens, void* o, float* lse,
                     int S, int H, int Lmax, int d, float scale, int window, int chunk,
                     void* workspace, size_t workspace_bytes, fa_dtype dtype, void* stream);
+
+/*
+ * fa_decode_tune -- measure the split length on this problem and let later
+ * automatic decode calls (chunk = 0) use the fastest.
+ *
+ * The split length of the split-K decode ("Build a FlashAttention Kernel
+ * with Online Softmax and KV Cache in Pure Python", Steps 4-5) chosen by
+ * measurement: the "profiling-driven auto-tuning" upgrade of "Build a
+ * FlashAttention-2 Inference Kernel from Scratch in Pure Python", Extending
+ * It.  Candidates: FA_DECODE_TUNE_CANDIDATES splits of 256, 512, 1024, 2048
+ * and 4096 tokens, skipping those shorter than the shortest automatic split
+ * (so that fa_decode_workspace_size(S, H, Lmax, d, 0) stays enough for
+ * every automatic call) and those that repeat the one-split case.  Each
+ * runs once to warm up and `reps` more times between two HIP events on
+ * `stream`; times_ms[i] (if non-NULL, FA_DECODE_TUNE_CANDIDATES floats in
+ * the order above) gets the mean ms per call, or -1 for a skipped
+ * candidate, and *best_chunk (if non-NULL) the fastest.  The choice is
+ * remembered under (dtype, d, window, S * H, Lmax).  On return o and lse
+ * hold the chosen split's result.
+ *
+ * Arguments as fa_decode (minus chunk), plus reps in [1, 1000]; the
+ * workspace must hold fa_decode_workspace_size(S, H, Lmax, d, 0) bytes.
+ * Like fa_fwd_tune it SYNCHRONISES `stream` and creates two HIP events.
+ */
+#define FA_DECODE_TUNE_CANDIDATES 5
+fa_status fa_decode_tune(const void* q, const void* kcache, const void* vcache,
+                         const int32_t* seqlens, void* o, float* lse,
+                         int S, int H, int Lmax, int d, float scale, int window,
+                         void* workspace, size_t workspace_bytes, fa_dtype dtype, void* stream,
+                         int reps, int* best_chunk, float* times_ms);
+
+/*
+ * The split length an automatic decode call uses for this problem: the one
+ * fa_decode_tune remembered (*tuned = 1), else the built-in choice
+ * (*tuned = 0).  Returns 0 for invalid arguments.
+ */
+int fa_decode_auto_chunk(int S, int H, int Lmax, int d, int window, fa_dtype dtype, int* tuned);
 
 /*
  * fa_decode_noalloc -- fa_decode that allocates nothing and takes no
@@ -292,6 +343,40 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  const float* lse, float* dq, float* dk, float* dv,
                  int B, int H, int N, int d, float scale, int causal, int window,
                  void* workspace, size_t workspace_bytes, fa_dtype dtype, void* stream);
+
+/*
+ * fa_bwd_tune -- measure the backward's two dQ kernels on this problem and
+ * let later fa_bwd calls use the faster.
+ *
+ * dQ is formed by its own kernel, in the forward's loop order (a workgroup
+ * owns query rows and walks the key tiles); it comes with 256 query rows per
+ * workgroup (8 waves, two groups one phase apart) or 128 (4 waves).  Which
+ * is faster depends on how well each grid fills the chip, so the choice is
+ * measured: the "profiling-driven auto-tuning" upgrade of "Build a
+ * FlashAttention-2 Inference Kernel from Scratch in Pure Python", Extending
+ * It.  The whole backward runs once to warm up and `reps` more times per
+ * candidate between two HIP events on `stream`; times_ms[0] / [1] (if
+ * non-NULL) get the mean ms per call with 128 / 256 rows and *best_dq_rows
+ * (if non-NULL) the faster, remembered under (dtype, d, causal, window,
+ * B * H, N).  On return dq, dk and dv hold the chosen kernel's result
+ * (both give identical dk and dv; dq agrees to rounding order).
+ *
+ * Arguments as fa_bwd, plus reps in [1, 1000].  Like fa_fwd_tune it
+ * SYNCHRONISES `stream` and creates two HIP events.
+ */
+fa_status fa_bwd_tune(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                      const float* lse, float* dq, float* dk, float* dv,
+                      int B, int H, int N, int d, float scale, int causal, int window,
+                      void* workspace, size_t workspace_bytes, fa_dtype dtype, void* stream,
+                      int reps, int* best_dq_rows, float* times_ms);
+
+/*
+ * The dQ kernel (query rows per workgroup, 128 or 256) an fa_bwd call uses
+ * for this problem: the one fa_bwd_tune remembered (*tuned = 1), else the
+ * built-in choice (*tuned = 0).  Returns 0 for invalid arguments.
+ */
+int fa_bwd_auto_dq_rows(int B, int H, int N, int d, int causal, int window, fa_dtype dtype,
+                        int* tuned);
 
 #ifdef __cplusplus
 }

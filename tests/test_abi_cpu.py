@@ -30,8 +30,10 @@ def declared_functions():
 
 def test_header_declares_the_expected_calls():
     names = declared_functions()
-    for must in ("fa_fwd", "fa_fwd_ex", "fa_fwd_tune", "fa_tune_export", "fa_tune_import", "fa_decode", "fa_decode_paged", "fa_bwd", "fa_decode_workspace_size",
-                 "fa_bwd_workspace_size", "fa_status_str", "fa_last_error", "fa_version"):
+    for must in ("fa_fwd", "fa_fwd_ex", "fa_fwd_tune", "fa_tune_export", "fa_tune_import", "fa_decode_tune",
+                 "fa_decode_auto_chunk", "fa_bwd_tune", "fa_bwd_auto_dq_rows", "fa_decode", "fa_decode_paged",
+                 "fa_bwd", "fa_decode_workspace_size", "fa_bwd_workspace_size", "fa_status_str", "fa_last_error",
+                 "fa_version"):
         assert must in names
 
 
@@ -141,27 +143,82 @@ def test_tune_rejects_bad_arguments_and_starts_empty(lib):
 
 
 def test_tune_table_export_import_round_trip(tmp_path, lib):
-    """The remembered tile table is host state: it round-trips through
-    export/import and a JSON file, and a bad row changes nothing."""
+    """The remembered tuning table is host state: it round-trips through
+    export/import and a JSON file, every kind's rows steer the matching
+    automatic choice, and a bad row changes nothing."""
     lib.fa_tune_reset()
-    rows = [dict(dtype=1, d=128, causal=1, window=-1, BH=128, N=4096, block_q=256),
-            dict(dtype=2, d=64, causal=0, window=100, BH=8, N=1024, block_q=128)]
+    K = fa355.TUNE_KINDS
+    rows = [dict(kind=K["fwd_block_q"], dtype=1, d=128, causal=1, window=-1, rows=128, n=4096, value=256),
+            dict(kind=K["fwd_block_q"], dtype=2, d=64, causal=0, window=100, rows=8, n=1024, value=128),
+            dict(kind=K["decode_chunk"], dtype=1, d=128, causal=0, window=-1, rows=2048, n=8192, value=2048),
+            dict(kind=K["bwd_dq_rows"], dtype=1, d=128, causal=1, window=-1, rows=32, n=4096, value=128)]
     fa355.fa_tune_import(rows)
     assert sorted(fa355.fa_tune_export(), key=str) == sorted(rows, key=str)
     assert fa355.fa_fwd_auto_block_q(1, 8, 1024, 64, window=100, dtype=torch.float16) == (128, True)
     assert fa355.fa_fwd_auto_block_q(4, 32, 4096, 128, causal=True) == (256, True)
+    assert fa355.fa_decode_auto_chunk(64, 32, 8192, 128) == (2048, True)
+    assert fa355.fa_decode_auto_chunk(64, 32, 8192, 128, window=1024) == (512, False)
+    assert fa355.fa_bwd_auto_dq_rows(2, 16, 4096, 128, causal=True) == (128, True)
+    assert fa355.fa_bwd_auto_dq_rows(2, 16, 4096, 128, causal=False) == (256, False)
     path = str(tmp_path / "tune.json")
     fa355.save_tuning(path)
     lib.fa_tune_reset()
     assert fa355.fa_tune_export() == []
+    assert fa355.fa_decode_auto_chunk(64, 32, 8192, 128) == (1024, False)
     fa355.load_tuning(path)
     assert sorted(fa355.fa_tune_export(), key=str) == sorted(rows, key=str)
-    for bad in (dict(rows[0], block_q=96), dict(rows[0], dtype=0), dict(rows[0], d=80),
-                dict(rows[0], causal=2), dict(rows[0], window=-2), dict(rows[0], N=0)):
+    for bad in (dict(rows[0], value=96), dict(rows[0], dtype=0), dict(rows[0], d=80),
+                dict(rows[0], causal=2), dict(rows[0], window=-2), dict(rows[0], n=0), dict(rows[0], kind=3),
+                dict(rows[2], value=300), dict(rows[2], value=8192), dict(rows[2], causal=1),
+                dict(rows[3], value=64), dict(rows[3], value=256 + 128)):
         with pytest.raises(fa355.FaError):
-            fa355.fa_tune_import([rows[1] | {"N": 7}, bad])
-        assert len(fa355.fa_tune_export()) == 2  # unchanged
+            fa355.fa_tune_import([rows[1] | {"n": 7}, bad])
+        assert len(fa355.fa_tune_export()) == 4  # unchanged
     lib.fa_tune_reset()
+
+
+def test_decode_and_bwd_tune_reject_bad_arguments(lib):
+    """Argument checks of the decode and backward tuning calls happen before
+    any HIP call (so they run here, without a GPU), and the automatic choices
+    with nothing tuned are the built-in ones."""
+    lib.fa_tune_reset()
+
+    def dec(**kw):
+        a = dict(q=FAKE, S=2, H=2, L=256, d=128, scale=0.1, window=-1, ws=FAKE, wsb=1 << 30, dtype=1, reps=3)
+        a.update(kw)
+        return lib.fa_decode_tune(a["q"], FAKE, FAKE, FAKE, FAKE, None, a["S"], a["H"], a["L"], a["d"],
+                                  a["scale"], a["window"], a["ws"], a["wsb"], a["dtype"], None, a["reps"],
+                                  None, None)
+    assert dec(q=None) == 1
+    assert dec(S=0) == 1
+    assert dec(reps=0) == 1
+    assert dec(reps=1001) == 1
+    assert dec(window=-2) == 1
+    assert dec(d=96) == 2
+    assert dec(ws=None) == 3
+    assert dec(wsb=16) == 3
+
+    def bwd(**kw):
+        a = dict(q=FAKE, B=1, H=2, N=64, d=128, scale=0.1, causal=1, window=-1, ws=FAKE, wsb=1 << 30,
+                 dtype=1, reps=3)
+        a.update(kw)
+        return lib.fa_bwd_tune(a["q"], FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["B"], a["H"], a["N"],
+                               a["d"], a["scale"], a["causal"], a["window"], a["ws"], a["wsb"], a["dtype"],
+                               None, a["reps"], None, None)
+    assert bwd(q=None) == 1
+    assert bwd(N=0) == 1
+    assert bwd(reps=0) == 1
+    assert bwd(dtype=0) == 2
+    assert bwd(d=96) == 2
+    assert bwd(ws=None) == 3
+    # built-in choices: 1024-token splits without a window on the 64 x 32 batch, 512 under one;
+    # the 256-row dQ kernel while its grid fills 256 CUs
+    assert fa355.fa_decode_auto_chunk(64, 32, 8192, 128) == (1024, False)
+    assert fa355.fa_decode_auto_chunk(64, 32, 8192, 128, window=1024) == (512, False)
+    assert fa355.fa_decode_auto_chunk(0, 32, 8192, 128)[0] == 0
+    assert fa355.fa_bwd_auto_dq_rows(2, 16, 4096, 128, causal=True) == (256, False)
+    assert fa355.fa_bwd_auto_dq_rows(1, 8, 1024, 64) == (128, False)
+    assert fa355.fa_bwd_auto_dq_rows(1, 8, 1024, 64, dtype=torch.float32)[0] == 0
 
 
 def test_decode_paged_rejects_bad_arguments(lib):

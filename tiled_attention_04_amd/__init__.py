@@ -10,12 +10,20 @@ from .fa355 import (  # noqa: F401
     FA_BF16,
     FA_FP16,
     FA_FP32,
+    BWD_TUNE_CANDIDATES,
+    DECODE_TUNE_CANDIDATES,
     TUNE_CANDIDATES,
+    TUNE_FIELDS,
+    TUNE_KINDS,
     FaError,
     fa_bwd,
+    fa_bwd_auto_dq_rows,
+    fa_bwd_tune,
     fa_bwd_workspace_size,
     fa_decode,
+    fa_decode_auto_chunk,
     fa_decode_noalloc,
+    fa_decode_tune,
     fa_decode_paged,
     fa_decode_workspace_size,
     fa_fwd,

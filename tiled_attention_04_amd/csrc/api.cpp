@@ -72,24 +72,83 @@ int auto_block_q(int B, int H, int N, int window) {
   return 32;
 }
 
-// Tile choices measured by fa_fwd_tune, by problem: automatic calls with
-// the same (dtype, d, causal, window, B*H, N) use them instead of the
-// heuristic above.
-using TuneKey = std::tuple<int, int, int, int, long long, int>;
+// Choices measured by the tuning calls, by kind and problem: automatic calls
+// with the same key use them instead of the built-in heuristics.  Key:
+// (kind, dtype, d, causal, window, B*H or S*H, N or Lmax).
+enum TuneKind {
+  kTuneFwd = FA_TUNE_FWD_BLOCK_Q,
+  kTuneDecode = FA_TUNE_DECODE_CHUNK,
+  kTuneBwd = FA_TUNE_BWD_DQ_ROWS
+};
+using TuneKey = std::tuple<int, int, int, int, int, long long, int>;
 std::mutex g_tune_mu;
 std::map<TuneKey, int> g_tuned;
 
-TuneKey tune_key(fa_dtype dtype, int d, int causal, int window, int B, int H, int N) {
-  return TuneKey{(int)dtype, d, causal, window, (long long)B * H, N};
+TuneKey tune_key(TuneKind kind, fa_dtype dtype, int d, int causal, int window, long long rows, int n) {
+  return TuneKey{(int)kind, (int)dtype, d, causal, window, rows, n};
 }
 
-int tuned_block_q(const TuneKey& key) {
+int tuned_value(const TuneKey& key) {
   std::lock_guard<std::mutex> lock(g_tune_mu);
   auto it = g_tuned.find(key);
   return it == g_tuned.end() ? 0 : it->second;
 }
 
+void remember(const TuneKey& key, int value) {
+  std::lock_guard<std::mutex> lock(g_tune_mu);
+  g_tuned[key] = value;
+}
+
+int tuned_block_q(fa_dtype dtype, int d, int causal, int window, int B, int H, int N) {
+  return tuned_value(tune_key(kTuneFwd, dtype, d, causal, window, (long long)B * H, N));
+}
+
+// The split length of an automatic decode call: the tuned one, else the
+// heuristic.  (Tuning only tries splits at least as long as the shortest
+// automatic one, so fa_decode_workspace_size(..., 0) stays enough.)
+int auto_decode_chunk(fa_dtype dtype, int d, int window, int S, int H, int Lmax) {
+  const int t = tuned_value(tune_key(kTuneDecode, dtype, d, 0, window, (long long)S * H, Lmax));
+  return t != 0 ? t : fa::decode_auto_chunk(S, H, Lmax, window);
+}
+
+int auto_dq_rows(fa_dtype dtype, int d, int causal, int window, int B, int H, int N) {
+  const int t = tuned_value(tune_key(kTuneBwd, dtype, d, causal, window, (long long)B * H, N));
+  return t != 0 ? t : fa::bwd_auto_dq_rows(B, H, N);
+}
+
+// One timing loop of a tuning call: a warm-up launch, then reps launches
+// between two events; the mean ms per launch, or a negative value with err
+// set on failure.
+template <typename Launch>
+float time_launches(hipEvent_t ev0, hipEvent_t ev1, hipStream_t s, int reps, hipError_t& err,
+                    Launch&& launch) {
+  err = launch();
+  if (err == hipSuccess) err = hipEventRecord(ev0, s);
+  for (int r = 0; r < reps && err == hipSuccess; ++r) err = launch();
+  if (err == hipSuccess) err = hipEventRecord(ev1, s);
+  if (err == hipSuccess) err = hipEventSynchronize(ev1);
+  float ms = 0.f;
+  if (err == hipSuccess) err = hipEventElapsedTime(&ms, ev0, ev1);
+  return err == hipSuccess ? ms / (float)reps : -1.f;
+}
+
+// Two timing events, destroyed with the object.
+struct EventPair {
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  hipError_t err = hipSuccess;
+  EventPair() {
+    err = hipEventCreate(&ev[0]);
+    if (err == hipSuccess) err = hipEventCreate(&ev[1]);
+  }
+  ~EventPair() {
+    if (ev[0]) (void)hipEventDestroy(ev[0]);
+    if (ev[1]) (void)hipEventDestroy(ev[1]);
+  }
+};
+
 constexpr int kTuneCandidates[4] = {32, 64, 128, 256};
+constexpr int kDecodeTuneChunks[FA_DECODE_TUNE_CANDIDATES] = {256, 512, 1024, 2048, 4096};
+constexpr int kDecodeTuneCount = FA_DECODE_TUNE_CANDIDATES;
 
 // Checks of a dense decode call; on success `chunk` holds the split length
 // the call will use (the automatic one when it was 0).
@@ -109,9 +168,35 @@ fa_status check_decode(const void* q, const void* kcache, const void* vcache, co
   if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "decode supports d in {64, 128} (got %d)", d);
   if ((long long)Lmax * d * (long long)elem_bytes((fa_dtype)dtype) > kMaxBufferBytes)
     return fail(FA_ERR_UNSUPPORTED, "one (sequence, head) cache slice exceeds 2 GiB");
-  if (chunk == 0) chunk = fa::decode_auto_chunk(S, H, Lmax, window);
+  if (chunk == 0) chunk = auto_decode_chunk((fa_dtype)dtype, d, window, S, H, Lmax);
   const long long nchunk = (Lmax + chunk - 1) / chunk;
   if (nchunk * S * H * 256 > kMaxThreadsPerLaunch) return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  return FA_OK;
+}
+
+// Checks of a backward call (fa_bwd and fa_bwd_tune).
+fa_status check_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                    const float* lse, const float* dq, const float* dk, const float* dv, int B, int H,
+                    int N, int d, float scale, int causal, int window, const void* workspace,
+                    size_t workspace_bytes, fa_dtype dtype) {
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv)
+    return fail(FA_ERR_INVALID_ARG, "every tensor pointer of fa_bwd must be non-null");
+  fa_status st = check_dense(B, H, N, d, scale, causal, window, dtype);
+  if (st != FA_OK) return st;
+  if (dtype == FA_FP32) return fail(FA_ERR_UNSUPPORTED, "backward supports bf16 and fp16 inputs only");
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "backward supports d in {64, 128} (got %d)", d);
+  if ((long long)N * d * 4 > kMaxBufferBytes)
+    return fail(FA_ERR_UNSUPPORTED, "one (batch, head) slice of the float32 gradients exceeds 2 GiB");
+  const long long rows = (long long)B * H * N;
+  const long long pre_rows_per_block = 2048 / d;  // 256 threads, d / 8 per row
+  const long long pre_threads = (rows + pre_rows_per_block - 1) / pre_rows_per_block * 256;
+  const long long main_threads = (long long)((N + 127) / 128) * B * H * 512;  // 128 keys per workgroup
+  if (pre_threads > kMaxThreadsPerLaunch || main_threads > kMaxThreadsPerLaunch)
+    return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  const size_t need = fa::bwd_workspace_bytes(B, H, N, d);
+  if (!workspace || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "backward needs %zu workspace bytes (got %zu%s)", need, workspace_bytes,
+                workspace ? "" : ", null pointer");
   return FA_OK;
 }
 
@@ -157,7 +242,7 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float*
   }
   if (d != 64 && d != 128)
     return fail(FA_ERR_UNSUPPORTED, "%s forward supports d in {64, 128} (got %d)", dtype_name(dtype), d);
-  if (block_q == 0) block_q = tuned_block_q(tune_key(dtype, d, causal, window, B, H, N));
+  if (block_q == 0) block_q = tuned_block_q(dtype, d, causal, window, B, H, N);
   if (block_q == 0) block_q = auto_block_q(B, H, N, window);
   if (block_k == 0) block_k = 64;
   if ((block_q != 32 && block_q != 64 && block_q != 128 && block_q != 256) || block_k != 64)
@@ -191,40 +276,24 @@ fa_status fa_fwd_tune(const void* q, const void* k, const void* v, void* o, floa
   const hipStream_t s = (hipStream_t)stream;
   const fa::Mask mask{causal, window};
   const bool f16 = dtype == FA_FP16;
-  hipEvent_t ev[2];
-  hipError_t err = hipEventCreate(&ev[0]);
-  if (err != hipSuccess) return done(err, "fa_fwd_tune (event)");
-  err = hipEventCreate(&ev[1]);
-  if (err != hipSuccess) {
-    (void)hipEventDestroy(ev[0]);
-    return done(err, "fa_fwd_tune (event)");
-  }
+  EventPair evs;
+  if (evs.err != hipSuccess) return done(evs.err, "fa_fwd_tune (event)");
+  hipError_t err = hipSuccess;
   float best_ms = 0.f;
   int best = 0;
   for (int i = 0; i < 4 && err == hipSuccess; ++i) {
     const int bq = kTuneCandidates[i];
-    err = fa::launch_fwd_mfma(q, k, v, o, lse, B, H, N, d, scale, mask, bq, f16, s);  // warm-up
-    if (err == hipSuccess) err = hipEventRecord(ev[0], s);
-    for (int r = 0; r < reps && err == hipSuccess; ++r)
-      err = fa::launch_fwd_mfma(q, k, v, o, lse, B, H, N, d, scale, mask, bq, f16, s);
-    if (err == hipSuccess) err = hipEventRecord(ev[1], s);
-    if (err == hipSuccess) err = hipEventSynchronize(ev[1]);
-    float ms = 0.f;
-    if (err == hipSuccess) err = hipEventElapsedTime(&ms, ev[0], ev[1]);
-    ms /= (float)reps;
+    const float ms = time_launches(evs.ev[0], evs.ev[1], s, reps, err, [&] {
+      return fa::launch_fwd_mfma(q, k, v, o, lse, B, H, N, d, scale, mask, bq, f16, s);
+    });
     if (times_ms) times_ms[i] = ms;
     if (err == hipSuccess && (best == 0 || ms < best_ms)) {
       best = bq;
       best_ms = ms;
     }
   }
-  (void)hipEventDestroy(ev[0]);
-  (void)hipEventDestroy(ev[1]);
   if (err != hipSuccess) return done(err, "fa_fwd_tune");
-  {
-    std::lock_guard<std::mutex> lock(g_tune_mu);
-    g_tuned[tune_key(dtype, d, causal, window, B, H, N)] = best;
-  }
+  remember(tune_key(kTuneFwd, dtype, d, causal, window, (long long)B * H, N), best);
   if (best_block_q) *best_block_q = best;
   // Leave o and lse holding the chosen tile's result.
   return done(fa::launch_fwd_mfma(q, k, v, o, lse, B, H, N, d, scale, mask, best, f16, s),
@@ -236,12 +305,73 @@ int fa_fwd_auto_block_q(int B, int H, int N, int d, int causal, int window, fa_d
   if (tuned) *tuned = 0;
   if (check_dense(B, H, N, d, 0.f, causal, window, dtype) != FA_OK) return 0;
   if (dtype == FA_FP32) return 64;
-  const int t = tuned_block_q(tune_key(dtype, d, causal, window, B, H, N));
+  const int t = tuned_block_q(dtype, d, causal, window, B, H, N);
   if (t != 0) {
     if (tuned) *tuned = 1;
     return t;
   }
   return auto_block_q(B, H, N, window);
+}
+
+fa_status fa_decode_tune(const void* q, const void* kcache, const void* vcache, const int32_t* seqlens,
+                         void* o, float* lse, int S, int H, int Lmax, int d, float scale, int window,
+                         void* workspace, size_t workspace_bytes, fa_dtype dtype, void* stream, int reps,
+                         int* best_chunk, float* times_ms) {
+  int chunk0 = 0;  // (validates everything; chunk0 becomes the automatic choice)
+  fa_status st = check_decode(q, kcache, vcache, seqlens, o, S, H, Lmax, d, scale, window, chunk0,
+                              (int)dtype);
+  if (st != FA_OK) return st;
+  if (reps < 1 || reps > 1000) return fail(FA_ERR_INVALID_ARG, "reps must be 1..1000 (got %d)", reps);
+  const int min_chunk = fa::decode_auto_chunk(S, H, Lmax, 0);
+  const size_t need = fa::decode_workspace_bytes(S, H, Lmax, d, min_chunk);
+  if (!workspace || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "decode tuning needs %zu workspace bytes, as for an automatic call "
+                "(got %zu%s)", need, workspace_bytes, workspace ? "" : ", null pointer");
+  const hipStream_t s = (hipStream_t)stream;
+  EventPair evs;
+  if (evs.err != hipSuccess) return done(evs.err, "fa_decode_tune (event)");
+  hipError_t err = hipSuccess;
+  float best_ms = 0.f;
+  int best = 0;
+  for (int i = 0; i < kDecodeTuneCount && err == hipSuccess; ++i) {
+    const int c = kDecodeTuneChunks[i];
+    // Splits shorter than the shortest automatic one would outgrow the
+    // workspace an automatic call is promised; splits past the longest
+    // cache repeat the one-split case.
+    const bool ok = c >= min_chunk && (i == 0 || kDecodeTuneChunks[i - 1] < Lmax);
+    if (!ok) {
+      if (times_ms) times_ms[i] = -1.f;
+      continue;
+    }
+    const float ms = time_launches(evs.ev[0], evs.ev[1], s, reps, err, [&] {
+      return fa::launch_decode(q, kcache, vcache, seqlens, o, lse, S, H, Lmax, d, scale, window, c,
+                               workspace, elem_of(dtype), s);
+    });
+    if (times_ms) times_ms[i] = ms;
+    if (err == hipSuccess && (best == 0 || ms < best_ms)) {
+      best = c;
+      best_ms = ms;
+    }
+  }
+  if (err != hipSuccess) return done(err, "fa_decode_tune");
+  if (best == 0) best = min_chunk;  // (every candidate skipped: cannot happen, min_chunk <= 1024)
+  remember(tune_key(kTuneDecode, dtype, d, 0, window, (long long)S * H, Lmax), best);
+  if (best_chunk) *best_chunk = best;
+  return done(fa::launch_decode(q, kcache, vcache, seqlens, o, lse, S, H, Lmax, d, scale, window, best,
+                                workspace, elem_of(dtype), s),
+              "fa_decode_tune");
+}
+
+int fa_decode_auto_chunk(int S, int H, int Lmax, int d, int window, fa_dtype dtype, int* tuned) {
+  if (tuned) *tuned = 0;
+  if (S <= 0 || H <= 0 || Lmax <= 0 || window < -1 || !valid_dtype(dtype) || (d != 64 && d != 128))
+    return 0;
+  const int t = tuned_value(tune_key(kTuneDecode, dtype, d, 0, window, (long long)S * H, Lmax));
+  if (t != 0) {
+    if (tuned) *tuned = 1;
+    return t;
+  }
+  return fa::decode_auto_chunk(S, H, Lmax, window);
 }
 
 void fa_tune_reset(void) {
@@ -256,14 +386,15 @@ int fa_tune_export(int64_t* rows, int max_rows) {
   int i = 0;
   for (const auto& kv : g_tuned) {
     if (i >= max_rows) break;
-    int64_t* r = rows + 7 * (size_t)i;
-    r[0] = std::get<0>(kv.first);  // dtype
-    r[1] = std::get<1>(kv.first);  // d
-    r[2] = std::get<2>(kv.first);  // causal
-    r[3] = std::get<3>(kv.first);  // window
-    r[4] = std::get<4>(kv.first);  // B * H
-    r[5] = std::get<5>(kv.first);  // N
-    r[6] = kv.second;              // block_q
+    int64_t* r = rows + FA_TUNE_ROW * (size_t)i;
+    r[0] = std::get<0>(kv.first);  // kind
+    r[1] = std::get<1>(kv.first);  // dtype
+    r[2] = std::get<2>(kv.first);  // d
+    r[3] = std::get<3>(kv.first);  // causal
+    r[4] = std::get<4>(kv.first);  // window
+    r[5] = std::get<5>(kv.first);  // B * H or S * H
+    r[6] = std::get<6>(kv.first);  // N or Lmax
+    r[7] = kv.second;              // block_q, chunk or dQ rows
     ++i;
   }
   return n;
@@ -272,18 +403,26 @@ int fa_tune_export(int64_t* rows, int max_rows) {
 fa_status fa_tune_import(const int64_t* rows, int n_rows) {
   if (n_rows < 0 || (n_rows > 0 && !rows)) return fail(FA_ERR_INVALID_ARG, "rows must hold n_rows >= 0 rows");
   for (int i = 0; i < n_rows; ++i) {  // validate everything before changing the table
-    const int64_t* r = rows + 7 * (size_t)i;
-    bool ok_bq = false;
-    for (int bq : kTuneCandidates) ok_bq |= r[6] == bq;
-    if ((r[0] != FA_BF16 && r[0] != FA_FP16) || (r[1] != 64 && r[1] != 128) || (r[2] != 0 && r[2] != 1) ||
-        r[3] < -1 || r[3] > INT_MAX || r[4] <= 0 || r[4] > INT_MAX || r[5] <= 0 || r[5] > INT_MAX || !ok_bq)
-      return fail(FA_ERR_INVALID_ARG, "tuning row %d is not a valid (dtype, d, causal, window, B*H, N, "
-                  "block_q) entry", i);
+    const int64_t* r = rows + FA_TUNE_ROW * (size_t)i;
+    bool ok_value = false;
+    if (r[0] == FA_TUNE_FWD_BLOCK_Q) {
+      for (int bq : kTuneCandidates) ok_value |= r[7] == bq;
+    } else if (r[0] == FA_TUNE_DECODE_CHUNK) {
+      for (int c : kDecodeTuneChunks) ok_value |= r[7] == c;
+      ok_value &= r[3] == 0;
+    } else if (r[0] == FA_TUNE_BWD_DQ_ROWS) {
+      ok_value = r[7] == 128 || r[7] == 256;
+    }
+    if (!ok_value || (r[1] != FA_BF16 && r[1] != FA_FP16) || (r[2] != 64 && r[2] != 128) ||
+        (r[3] != 0 && r[3] != 1) || r[4] < -1 || r[4] > INT_MAX || r[5] <= 0 || r[5] > INT_MAX ||
+        r[6] <= 0 || r[6] > INT_MAX)
+      return fail(FA_ERR_INVALID_ARG, "tuning row %d is not a valid (kind, dtype, d, causal, window, rows, "
+                  "N, value) entry", i);
   }
   std::lock_guard<std::mutex> lock(g_tune_mu);
   for (int i = 0; i < n_rows; ++i) {
-    const int64_t* r = rows + 7 * (size_t)i;
-    g_tuned[TuneKey{(int)r[0], (int)r[1], (int)r[2], (int)r[3], r[4], (int)r[5]}] = (int)r[6];
+    const int64_t* r = rows + FA_TUNE_ROW * (size_t)i;
+    g_tuned[TuneKey{(int)r[0], (int)r[1], (int)r[2], (int)r[3], (int)r[4], r[5], (int)r[6]}] = (int)r[7];
   }
   g_err[0] = '\0';
   return FA_OK;
@@ -355,7 +494,7 @@ fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_page
   if ((long long)page_size * d * (long long)elem_bytes(dtype) > kMaxBufferBytes)
     return fail(FA_ERR_UNSUPPORTED, "one page of one head exceeds 2 GiB");
   const int Lmax = max_pages * page_size;
-  if (chunk == 0) chunk = fa::decode_auto_chunk(S, H, Lmax, window);
+  if (chunk == 0) chunk = auto_decode_chunk(dtype, d, window, S, H, Lmax);
   const long long nchunk = (Lmax + chunk - 1) / chunk;
   if (nchunk * S * H * 256 > kMaxThreadsPerLaunch) return fail(FA_ERR_UNSUPPORTED, "grid too large");
   const size_t need = fa::decode_workspace_bytes(S, H, Lmax, d, chunk);
@@ -377,28 +516,61 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  const float* lse, float* dq, float* dk, float* dv, int B, int H, int N, int d,
                  float scale, int causal, int window, void* workspace, size_t workspace_bytes,
                  fa_dtype dtype, void* stream) {
-  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv)
-    return fail(FA_ERR_INVALID_ARG, "every tensor pointer of fa_bwd must be non-null");
-  fa_status st = check_dense(B, H, N, d, scale, causal, window, dtype);
+  const fa_status st = check_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, window,
+                                 workspace, workspace_bytes, dtype);
   if (st != FA_OK) return st;
-  if (dtype == FA_FP32) return fail(FA_ERR_UNSUPPORTED, "backward supports bf16 and fp16 inputs only");
-  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "backward supports d in {64, 128} (got %d)", d);
-  if ((long long)N * d * 4 > kMaxBufferBytes)
-    return fail(FA_ERR_UNSUPPORTED, "one (batch, head) slice of the float32 gradients exceeds 2 GiB");
-  const long long rows = (long long)B * H * N;
-  const long long pre_rows_per_block = 2048 / d;  // 256 threads, d / 8 per row
-  const long long pre_threads = (rows + pre_rows_per_block - 1) / pre_rows_per_block * 256;
-  const long long main_threads = (long long)((N + 127) / 128) * B * H * 512;  // 128 keys per workgroup
-  if (pre_threads > kMaxThreadsPerLaunch || main_threads > kMaxThreadsPerLaunch)
-    return fail(FA_ERR_UNSUPPORTED, "grid too large");
-  const size_t need = fa::bwd_workspace_bytes(B, H, N, d);
-  if (!workspace || workspace_bytes < need)
-    return fail(FA_ERR_WORKSPACE, "backward needs %zu workspace bytes (got %zu%s)", need, workspace_bytes,
-                workspace ? "" : ", null pointer");
   return done(fa::launch_bwd_mfma(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale,
                                   fa::Mask{causal, window}, workspace, dtype == FA_FP16,
-                                  (hipStream_t)stream),
+                                  auto_dq_rows(dtype, d, causal, window, B, H, N), (hipStream_t)stream),
               "fa_bwd");
+}
+
+fa_status fa_bwd_tune(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                      const float* lse, float* dq, float* dk, float* dv, int B, int H, int N, int d,
+                      float scale, int causal, int window, void* workspace, size_t workspace_bytes,
+                      fa_dtype dtype, void* stream, int reps, int* best_dq_rows, float* times_ms) {
+  const fa_status st = check_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, window,
+                                 workspace, workspace_bytes, dtype);
+  if (st != FA_OK) return st;
+  if (reps < 1 || reps > 1000) return fail(FA_ERR_INVALID_ARG, "reps must be 1..1000 (got %d)", reps);
+  const hipStream_t s = (hipStream_t)stream;
+  const fa::Mask mask{causal, window};
+  EventPair evs;
+  if (evs.err != hipSuccess) return done(evs.err, "fa_bwd_tune (event)");
+  hipError_t err = hipSuccess;
+  const int cand[2] = {128, 256};
+  float best_ms = 0.f;
+  int best = 0;
+  for (int i = 0; i < 2 && err == hipSuccess; ++i) {
+    const float ms = time_launches(evs.ev[0], evs.ev[1], s, reps, err, [&] {
+      return fa::launch_bwd_mfma(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, mask, workspace,
+                                 dtype == FA_FP16, cand[i], s);
+    });
+    if (times_ms) times_ms[i] = ms;
+    if (err == hipSuccess && (best == 0 || ms < best_ms)) {
+      best = cand[i];
+      best_ms = ms;
+    }
+  }
+  if (err != hipSuccess) return done(err, "fa_bwd_tune");
+  remember(tune_key(kTuneBwd, dtype, d, causal, window, (long long)B * H, N), best);
+  if (best_dq_rows) *best_dq_rows = best;
+  return done(fa::launch_bwd_mfma(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, mask, workspace,
+                                  dtype == FA_FP16, best, s),
+              "fa_bwd_tune");
+}
+
+int fa_bwd_auto_dq_rows(int B, int H, int N, int d, int causal, int window, fa_dtype dtype, int* tuned) {
+  if (tuned) *tuned = 0;
+  if (check_dense(B, H, N, d, 0.f, causal, window, dtype) != FA_OK || dtype == FA_FP32 ||
+      (d != 64 && d != 128))
+    return 0;
+  const int t = tuned_value(tune_key(kTuneBwd, dtype, d, causal, window, (long long)B * H, N));
+  if (t != 0) {
+    if (tuned) *tuned = 1;
+    return t;
+  }
+  return fa::bwd_auto_dq_rows(B, H, N);
 }
 
 }  // extern "C"

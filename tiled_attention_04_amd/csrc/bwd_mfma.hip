@@ -823,7 +823,7 @@ void bwd_dq_pp_kernel(const T* __restrict__ q, const T* __restrict__ k,
 template <typename T, int D>
 hipError_t launch_t(const void* q, const void* k, const void* v, const void* o, const void* dO,
                     const float* lse, float* dq, float* dk, float* dv, int B, int H, int N,
-                    float scale, Mask mask, void* ws, hipStream_t stream) {
+                    float scale, Mask mask, void* ws, int dq_rows, hipStream_t stream) {
   const long long rows = (long long)B * H * N;
   float* Dv = (float*)ws;
   float* L2 = Dv + rows;
@@ -839,9 +839,9 @@ hipError_t launch_t(const void* q, const void* k, const void* v, const void* o, 
                      B * H, N, nkt, scale, scale * kLog2e, mask.causal, mask.window);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  // dQ: the ping-pong kernel (256 query rows per workgroup) when its grid
-  // still fills the chip, else the 4-wave kernel (128 rows).
-  if ((long long)B * H * ((N + 255) / 256) >= 256) {
+  // dQ: the ping-pong kernel (256 query rows per workgroup) or the 4-wave
+  // kernel (128 rows).
+  if (dq_rows == 256) {
     const int nqt = (N + 255) / 256;
     hipLaunchKernelGGL((bwd_dq_pp_kernel<T, D>), dim3((unsigned)((long long)nqt * B * H)), dim3(kDqPPThreads),
                        0, stream, (const T*)q, (const T*)k, (const T*)v, (const T*)dO, Dv,
@@ -858,6 +858,12 @@ hipError_t launch_t(const void* q, const void* k, const void* v, const void* o, 
 
 }  // namespace
 
+int bwd_auto_dq_rows(int B, int H, int N) {
+  // The ping-pong dQ kernel while its grid (256 rows per workgroup, one per
+  // CU) still fills the 256 CUs, else the 4-wave kernel.
+  return (long long)B * H * ((N + 255) / 256) >= 256 ? 256 : 128;
+}
+
 size_t bwd_workspace_bytes(int B, int H, int N, int d) {
   (void)d;
   return (size_t)B * H * N * 2 * sizeof(float);
@@ -866,14 +872,16 @@ size_t bwd_workspace_bytes(int B, int H, int N, int d) {
 hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const void* o,
                            const void* dO, const float* lse, float* dq, float* dk, float* dv,
                            int B, int H, int N, int d, float scale, Mask mask, void* ws, bool f16,
-                           hipStream_t stream) {
+                           int dq_rows, hipStream_t stream) {
+  if (dq_rows != 128 && dq_rows != 256) dq_rows = bwd_auto_dq_rows(B, H, N);
   if (f16) {
     if (d == 128)
-      return launch_t<fa::f16, 128>(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, scale, mask, ws, stream);
-    return launch_t<fa::f16, 64>(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, scale, mask, ws, stream);
+      return launch_t<fa::f16, 128>(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, scale, mask, ws, dq_rows, stream);
+    return launch_t<fa::f16, 64>(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, scale, mask, ws, dq_rows, stream);
   }
-  if (d == 128) return launch_t<bf16, 128>(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, scale, mask, ws, stream);
-  return launch_t<bf16, 64>(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, scale, mask, ws, stream);
+  if (d == 128)
+    return launch_t<bf16, 128>(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, scale, mask, ws, dq_rows, stream);
+  return launch_t<bf16, 64>(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, scale, mask, ws, dq_rows, stream);
 }
 
 }  // namespace fa

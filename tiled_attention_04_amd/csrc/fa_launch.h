@@ -52,11 +52,13 @@ hipError_t launch_decode_noalloc(const void* q, const void* kc, const void* vc, 
                                  int window, int chunk, Elem elem, hipStream_t stream);
 
 // 16-bit backward (bf16, or fp16 when f16): preprocess, dK/dV and dQ
-// kernels, d in {64, 128}.
+// kernels, d in {64, 128}.  dq_rows picks the dQ kernel: 256 (8-wave
+// ping-pong) or 128 (4 waves); bwd_auto_dq_rows is the built-in choice.
 size_t bwd_workspace_bytes(int B, int H, int N, int d);
+int bwd_auto_dq_rows(int B, int H, int N);
 hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const void* o,
                            const void* dO, const float* lse, float* dq, float* dk, float* dv,
                            int B, int H, int N, int d, float scale, Mask mask, void* ws, bool f16,
-                           hipStream_t stream);
+                           int dq_rows, hipStream_t stream);
 
 }  // namespace fa

@@ -44,6 +44,11 @@ SIGNATURES = {
                              _I, _P]),
     "fa_bwd_workspace_size": (_Z, [_I, _I, _I, _I]),
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _I, _P]),
+    "fa_decode_tune": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _Z, _I, _P, _I, _P, _P]),
+    "fa_decode_auto_chunk": (_I, [_I, _I, _I, _I, _I, _I, _P]),
+    "fa_bwd_tune": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _I, _P,
+                         _I, _P, _P]),
+    "fa_bwd_auto_dq_rows": (_I, [_I, _I, _I, _I, _I, _I, _I, _P]),
 }
 
 
@@ -175,36 +180,41 @@ def fa_tune_reset() -> None:
     lib().fa_tune_reset()
 
 
-TUNE_FIELDS = ("dtype", "d", "causal", "window", "BH", "N", "block_q")
+# Columns of a remembered tuning choice; "kind" is one of TUNE_KINDS, "rows"
+# is B*H (S*H for decode), "n" is N (Lmax for decode) and "value" the choice:
+# block_q, the decode split length or the dQ kernel's query rows.
+TUNE_FIELDS = ("kind", "dtype", "d", "causal", "window", "rows", "n", "value")
+TUNE_KINDS = {"fwd_block_q": 0, "decode_chunk": 1, "bwd_dq_rows": 2}
+_ROW = len(TUNE_FIELDS)
 
 
 def fa_tune_export() -> list:
-    """The remembered tile choices as dicts with the keys of TUNE_FIELDS."""
+    """The remembered tuning choices as dicts with the keys of TUNE_FIELDS."""
     n = int(lib().fa_tune_export(None, 0))
-    buf = (ctypes.c_int64 * (7 * max(n, 1)))()
+    buf = (ctypes.c_int64 * (_ROW * max(n, 1)))()
     n = min(n, int(lib().fa_tune_export(buf, n)))
-    return [dict(zip(TUNE_FIELDS, buf[7 * i:7 * i + 7])) for i in range(n)]
+    return [dict(zip(TUNE_FIELDS, buf[_ROW * i:_ROW * i + _ROW])) for i in range(n)]
 
 
 def fa_tune_import(entries) -> None:
-    """Add tile choices (dicts as returned by fa_tune_export)."""
+    """Add tuning choices (dicts as returned by fa_tune_export)."""
     entries = list(entries)
-    buf = (ctypes.c_int64 * (7 * max(len(entries), 1)))()
+    buf = (ctypes.c_int64 * (_ROW * max(len(entries), 1)))()
     for i, e in enumerate(entries):
         for j, f in enumerate(TUNE_FIELDS):
-            buf[7 * i + j] = int(e[f])
+            buf[_ROW * i + j] = int(e[f])
     _check(lib().fa_tune_import(buf, len(entries)))
 
 
 def save_tuning(path: str) -> None:
-    """Write the remembered tile choices to a JSON file."""
+    """Write the remembered tuning choices to a JSON file."""
     import json
     with open(path, "w") as f:
         json.dump(fa_tune_export(), f, indent=1)
 
 
 def load_tuning(path: str) -> None:
-    """Load tile choices written by save_tuning."""
+    """Load tuning choices written by save_tuning."""
     import json
     with open(path) as f:
         fa_tune_import(json.load(f))
@@ -241,6 +251,48 @@ def fa_decode(q, kcache, vcache, seqlens, *, scale=None, window: int = -1, chunk
                            int(window), int(chunk), wp, workspace.numel() * workspace.element_size(),
                            _DTYPE[dt], _stream(stream)))
     return o, lse
+
+
+DECODE_TUNE_CANDIDATES = (256, 512, 1024, 2048, 4096)
+
+
+def fa_decode_tune(q, kcache, vcache, seqlens, *, scale=None, window: int = -1, reps: int = 10,
+                   o=None, lse=None, workspace=None, stream=None):
+    """Time the decode's split lengths on these inputs and remember the fastest
+    for later automatic calls (synchronises the stream).  Returns (best chunk,
+    {chunk: mean ms per call, or -1 when skipped}, o, lse)."""
+    S, H, d = q.shape
+    Lmax = kcache.shape[2]
+    dt = q.dtype
+    if dt not in _DTYPE:
+        raise ValueError(f"unsupported dtype {dt}")
+    qp = _dev(q, "q", dt)
+    kp = _dev(kcache, "kcache", dt, (S, H, Lmax, d))
+    vp = _dev(vcache, "vcache", dt, (S, H, Lmax, d))
+    sp = _dev(seqlens, "seqlens", torch.int32, (S,))
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((S, H), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        need = fa_decode_workspace_size(S, H, Lmax, d, 0)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    op = _dev(o, "o", dt, q.shape)
+    lp = _dev(lse, "lse", torch.float32, (S, H))
+    wp = _dev(workspace, "workspace")
+    best = ctypes.c_int(0)
+    times = (ctypes.c_float * len(DECODE_TUNE_CANDIDATES))()
+    _check(lib().fa_decode_tune(qp, kp, vp, sp, op, lp, S, H, Lmax, d, _default_scale(scale, d),
+                                int(window), wp, workspace.numel() * workspace.element_size(), _DTYPE[dt],
+                                _stream(stream), int(reps), ctypes.byref(best), times))
+    return best.value, dict(zip(DECODE_TUNE_CANDIDATES, list(times))), o, lse
+
+
+def fa_decode_auto_chunk(S: int, H: int, Lmax: int, d: int, *, window: int = -1, dtype=torch.bfloat16):
+    """(split length an automatic decode call uses, whether it was tuned)."""
+    tuned = ctypes.c_int(0)
+    c = lib().fa_decode_auto_chunk(S, H, Lmax, d, int(window), _DTYPE[dtype], ctypes.byref(tuned))
+    return int(c), bool(tuned.value)
 
 
 def fa_decode_noalloc(q, kcache, vcache, seqlens, *, scale=None, window: int = -1, chunk: int = 0,
@@ -326,3 +378,41 @@ def fa_bwd(q, k, v, o, dO, lse, *, causal: bool = False, window: int = -1, scale
                         int(window), wp, workspace.numel() * workspace.element_size(), _DTYPE[dt],
                         _stream(stream)))
     return tuple(outs)
+
+
+BWD_TUNE_CANDIDATES = (128, 256)
+
+
+def fa_bwd_tune(q, k, v, o, dO, lse, *, causal: bool = False, window: int = -1, scale=None, reps: int = 10,
+                dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Time the backward with each dQ kernel (128 or 256 query rows per
+    workgroup) and remember the faster for later fa_bwd calls (synchronises
+    the stream).  Returns (best rows, {rows: mean ms per call}, (dq, dk, dv))."""
+    B, H, N, d = q.shape
+    dt = q.dtype
+    if dt not in _DTYPE:
+        raise ValueError(f"unsupported dtype {dt}")
+    ptrs = [_dev(t, n, dt, q.shape) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dO, "dO"))]
+    lp = _dev(lse, "lse", torch.float32, (B, H, N))
+    outs = []
+    for t in (dq, dk, dv):
+        outs.append(torch.empty(q.shape, dtype=torch.float32, device=q.device) if t is None else t)
+    gp = [_dev(t, n, torch.float32, q.shape) for t, n in zip(outs, ("dq", "dk", "dv"))]
+    if workspace is None:
+        workspace = torch.empty(max(fa_bwd_workspace_size(B, H, N, d), 1), dtype=torch.uint8,
+                                device=q.device)
+    wp = _dev(workspace, "workspace")
+    best = ctypes.c_int(0)
+    times = (ctypes.c_float * 2)()
+    _check(lib().fa_bwd_tune(*ptrs, lp, *gp, B, H, N, d, _default_scale(scale, d), int(causal),
+                             int(window), wp, workspace.numel() * workspace.element_size(), _DTYPE[dt],
+                             _stream(stream), int(reps), ctypes.byref(best), times))
+    return best.value, dict(zip(BWD_TUNE_CANDIDATES, list(times))), tuple(outs)
+
+
+def fa_bwd_auto_dq_rows(B: int, H: int, N: int, d: int, *, causal: bool = False, window: int = -1,
+                        dtype=torch.bfloat16):
+    """(dQ kernel rows an fa_bwd call uses, whether it was tuned)."""
+    tuned = ctypes.c_int(0)
+    r = lib().fa_bwd_auto_dq_rows(B, H, N, d, int(causal), int(window), _DTYPE[dtype], ctypes.byref(tuned))
+    return int(r), bool(tuned.value)

@@ -1,13 +1,18 @@
-"""Sweep of the forward's query-tile sizes on the measured workloads.
+"""Sweep of the tuned choices on the measured workloads.
 
     python -m tiled_attention_04_amd.tune [--reps 20] [--save tuning.json]
 
-For each workload, fa_fwd_tune times every tile (32, 64, 128 and 256 query
-rows; 64-key tiles) on the GPU and remembers the fastest; the table printed
-here (markdown) sets those times beside the built-in heuristic's choice.
-With --save the choices are written to a JSON file that a later process
-loads with ``load_tuning`` (no re-measuring).
-Inputs are the seeded synthetic ones the tests and the bench use.
+Three tables (markdown), each setting the measured candidates beside the
+built-in heuristic's choice:
+  * the forward's query tile (fa_fwd_tune: 32, 64, 128 and 256 rows, 64-key
+    tiles);
+  * the decode's split length (fa_decode_tune: 256 to 4096 tokens);
+  * the backward's dQ kernel (fa_bwd_tune: 128 or 256 query rows per
+    workgroup).
+Every tuning call remembers its fastest candidate; with --save the choices
+are written to a JSON file that a later process loads with ``load_tuning``
+(no re-measuring).  Inputs are the seeded synthetic ones the tests and the
+bench use.
 """
 
 from __future__ import annotations
@@ -18,7 +23,7 @@ import numpy as np
 import torch
 
 from . import fa355
-from .inputs import attention_inputs
+from .inputs import attention_inputs, decode_inputs, dense_cache
 
 # name, (B, H, N, d), dtype, causal, window
 WORKLOADS = [
@@ -28,6 +33,23 @@ WORKLOADS = [
     ("causal 2x16x4096x128 bf16", (2, 16, 4096, 128), "bf16", True, -1),
     ("full 1x8x1024x64 bf16", (1, 8, 1024, 64), "bf16", False, -1),
     ("causal 1x8x1024x64 bf16", (1, 8, 1024, 64), "bf16", True, -1),
+]
+
+# name, (S, H, d, shortest, longest cache), dtype, window
+DECODE_WORKLOADS = [
+    ("ragged 64x32 d128 512-8192 bf16", (64, 32, 128, 512, 8192), "bf16", -1),
+    ("ragged 64x32 d128 512-8192 window-1024 bf16", (64, 32, 128, 512, 8192), "bf16", 1024),
+    ("ragged 8x8 d128 512-8192 bf16", (8, 8, 128, 512, 8192), "bf16", -1),
+    ("ragged 64x32 d128 512-8192 fp16", (64, 32, 128, 512, 8192), "fp16", -1),
+]
+
+# name, (B, H, N, d), dtype, causal, window
+BWD_WORKLOADS = [
+    ("causal 2x16x4096x128 bf16", (2, 16, 4096, 128), "bf16", True, -1),
+    ("window-1024 2x16x4096x128 bf16", (2, 16, 4096, 128), "bf16", True, 1024),
+    ("causal 2x16x4096x128 fp16", (2, 16, 4096, 128), "fp16", True, -1),
+    ("causal 1x8x1024x64 bf16", (1, 8, 1024, 64), "bf16", True, -1),
+    ("full 1x8x1024x64 bf16", (1, 8, 1024, 64), "bf16", False, -1),
 ]
 
 
@@ -59,6 +81,53 @@ def main():
         print(f"| {name} | {cells} | {best} | {tf:.1f} | {heur} | {times[heur]:.4f} |", flush=True)
         tuned += fa355.fa_tune_export()
         del q, k, v
+
+    print()
+    print("| decode workload | " + " | ".join(f"{c} tok ms" for c in fa355.DECODE_TUNE_CANDIDATES)
+          + " | fastest | TB/s | heuristic | heuristic ms |")
+    print("|---|" + "---|" * (len(fa355.DECODE_TUNE_CANDIDATES) + 4))
+    for name, (S, H, d, lo, hi), dtype, window in DECODE_WORKLOADS:
+        inp = decode_inputs(S, H, d, lo, hi, dtype=dtype, seed=0)
+        kc, vc = dense_cache(inp, hi, device=dev, fill=0.0)
+        q, sl = inp.q.to(dev), torch.from_numpy(inp.seqlens).to(dev)
+        fa355.fa_tune_reset()
+        heur, _ = fa355.fa_decode_auto_chunk(S, H, hi, d, window=window, dtype=q.dtype)
+        best, times, _, _ = fa355.fa_decode_tune(q, kc, vc, sl, window=window, reps=args.reps)
+        if times.get(heur, -1) < 0:  # the heuristic's split is not a candidate: time it too
+            ws = torch.empty(fa355.fa_decode_workspace_size(S, H, hi, d, 0), dtype=torch.uint8, device=dev)
+            fa355.fa_decode(q, kc, vc, sl, window=window, chunk=heur, workspace=ws)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.reps):
+                fa355.fa_decode(q, kc, vc, sl, window=window, chunk=heur, workspace=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            times[heur] = e0.elapsed_time(e1) / args.reps
+        rows_read = np.minimum(inp.seqlens.astype(np.int64), window + 1 if window >= 0 else 1 << 62)
+        nbytes = int(rows_read.sum()) * H * d * q.element_size() * 2
+        tbs = nbytes / (times[best] * 1e-3) / 1e12
+        cells = " | ".join(f"{times[c]:.4f}" if times[c] >= 0 else "-" for c in fa355.DECODE_TUNE_CANDIDATES)
+        print(f"| {name} | {cells} | {best} | {tbs:.2f} | {heur} | {times[heur]:.4f} |", flush=True)
+        tuned += fa355.fa_tune_export()
+        del kc, vc, q
+
+    print()
+    print("| backward workload | " + " | ".join(f"dQ {r} rows ms" for r in fa355.BWD_TUNE_CANDIDATES)
+          + " | fastest | TFLOP/s | heuristic |")
+    print("|---|" + "---|" * (len(fa355.BWD_TUNE_CANDIDATES) + 3))
+    for name, (B, H, N, d), dtype, causal, window in BWD_WORKLOADS:
+        q, k, v, g = (t.to(dev) for t in attention_inputs(B, H, N, d, dtype, seed=0, with_grad=True))
+        o, lse = fa355.fa_fwd(q, k, v, causal=causal, window=window)
+        fa355.fa_tune_reset()
+        heur, _ = fa355.fa_bwd_auto_dq_rows(B, H, N, d, causal=causal, window=window, dtype=q.dtype)
+        best, times, _ = fa355.fa_bwd_tune(q, k, v, o, g, lse, causal=causal, window=window, reps=args.reps)
+        flops = 10.0 * d * B * H * visible_pairs(N, causal, window)
+        tf = flops / (times[best] * 1e-3) / 1e12
+        cells = " | ".join(f"{times[r]:.4f}" for r in fa355.BWD_TUNE_CANDIDATES)
+        print(f"| {name} | {cells} | {best} | {tf:.1f} | {heur} |", flush=True)
+        tuned += fa355.fa_tune_export()
+        del q, k, v, g, o, lse
+
     if args.save:
         fa355.fa_tune_reset()
         fa355.fa_tune_import(tuned)
