@@ -448,10 +448,11 @@ def main():
         del src, dst
 
     value = flops3 / (ms["fwd"] * 1e-3) / 1e12 if "fwd" in ms else None
-    bq3, tuned3 = fa.fa_fwd_auto_block_q(B3, H3, N3, d3, causal=True)
+    (bq3, bk3), tuned3 = fa.fa_fwd_auto_tile(B3, H3, N3, d3, causal=True)
     kernel3 = (f"fwd_pingpong_kernel<bf16, {d3}>" if bq3 == 256 else
-               f"fwd_mfma_kernel<bf16, {d3}, {bq3 // 32}>")
-    kernel3 += f" ({bq3} query rows per workgroup, {'tuned' if tuned3 else 'heuristic'} choice)"
+               f"fwd_mfma_kernel<bf16, {d3}, {bq3 // 32}, {bk3}>")
+    kernel3 += (f" ({bq3} query rows x {bk3} keys per tile, "
+                f"{'tuned' if tuned3 else 'heuristic'} choice)")
     result = {
         "metric": "causal fwd TFLOP/s & % bf16 MFMA peak (N=4096,d=128); decode % HBM BW",
         "value": round(value, 3) if value is not None else None,

@@ -96,7 +96,14 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
  *            Example", Setting Up the Example), with block_q * d and
  *            block_k * d <= 8192 and block_k * (d + 1) <= 8256; automatic: 64 x 64 for
  *            d <= 128, 32 x 32 above.
- *   FA_BF16, FA_FP16: block_q in {32, 64, 128, 256}, block_k = 64.
+ *   FA_BF16, FA_FP16: block_q in {32, 64, 128} (1, 2 or 4 waves) with
+ *            block_k in {32, 64}, or 128 at d = 64 (at d = 128 two 128-key
+ *            score tiles exceed a wave's registers); or 256 x 64 (8 waves,
+ *            two groups one phase apart, whose three LDS stages leave no
+ *            room for 128-key tiles).  Automatic (block_q = 0): the tile
+ *            fa_fwd_tune remembered for the problem, else the built-in
+ *            choice (see fa_fwd_auto_block_q); a non-zero block_k then
+ *            overrides the automatic key tile.
  * Any other pair: FA_ERR_INVALID_ARG.
  */
 fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -114,14 +121,16 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float*
  * The NumPy page's roadmap (Extending It) asks for tile sizes justified by
  * the on-chip memory: every candidate fits gfx950's 160 KB of LDS.
  *
- * For each block_q in {32, 64, 128, 256} (block_k = 64) the forward runs
- * once to warm up and `reps` more times between two HIP events on
- * `stream`; the mean time per call goes to times_ms[i] (if non-NULL, 4
- * floats, candidate order as above) and the fastest block_q to
- * *best_block_q (if non-NULL).  That choice is remembered for the process
- * under the key (dtype, d, causal, window, B*H, N): fa_fwd (and fa_fwd_ex
- * with block_q = 0) then uses it instead of the built-in heuristic.  On
- * return o and lse hold the chosen tile's result for these inputs.
+ * Candidates: the FA_FWD_TUNE_CANDIDATES tiles (block_q, block_k) = (32,
+ * 32), (32, 64), (32, 128), (64, 32), (64, 64), (64, 128), (128, 32),
+ * (128, 64), (128, 128) and (256, 64), in this order (the 128-key tiles
+ * at d = 64 only).  Each runs once to warm up and `reps` more times
+ * between two HIP events on `stream`; the mean time per call goes to
+ * times_ms[i] (if non-NULL, one float per candidate, -1 for one skipped) and the fastest tile to *best_block_q / *best_block_k (each
+ * if non-NULL).  That choice is remembered for the process under the key
+ * (dtype, d, causal, window, B*H, N): fa_fwd (and fa_fwd_ex with block_q =
+ * 0) then uses it instead of the built-in heuristic.  On return o and lse
+ * hold the chosen tile's result for these inputs.
  *
  * Unlike every other call this one SYNCHRONISES `stream` and creates two
  * HIP events (released before it returns); it is meant for set-up, not the
@@ -129,17 +138,20 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float*
  *
  * Arguments as fa_fwd, plus reps in [1, 1000].  FA_FP32: FA_ERR_UNSUPPORTED.
  */
+#define FA_FWD_TUNE_CANDIDATES 10
 fa_status fa_fwd_tune(const void* q, const void* k, const void* v, void* o, float* lse,
                       int B, int H, int N, int d, float scale, int causal, int window,
-                      fa_dtype dtype, void* stream, int reps, int* best_block_q, float* times_ms);
+                      fa_dtype dtype, void* stream, int reps, int* best_block_q, int* best_block_k,
+                      float* times_ms);
 
 /*
- * The block_q an automatic fa_fwd call uses for this problem: the one
+ * The tile an automatic fa_fwd call uses for this problem: the one
  * fa_fwd_tune remembered (then *tuned = 1, if tuned is non-NULL), else the
- * built-in heuristic's (*tuned = 0).  Returns 0 for invalid arguments.
+ * built-in heuristic's (*tuned = 0).  Returns block_q and writes block_k to
+ * *block_k (if non-NULL); returns 0 for invalid arguments.
  */
 int fa_fwd_auto_block_q(int B, int H, int N, int d, int causal, int window, fa_dtype dtype,
-                        int* tuned);
+                        int* block_k, int* tuned);
 
 /*
  * Remembered tuning choices.  fa_fwd_tune, fa_decode_tune and fa_bwd_tune
@@ -148,7 +160,8 @@ int fa_fwd_auto_block_q(int B, int H, int N, int d, int causal, int window, fa_d
  * FA_TUNE_ROW int64 values:
  *   (kind, dtype, d, causal, window, rows, n, value)
  * with, per kind,
- *   FA_TUNE_FWD_BLOCK_Q : rows = B * H, n = N, value = block_q
+ *   FA_TUNE_FWD_TILE    : rows = B * H, n = N, value = block_q * 1000 +
+ *                         block_k
  *   FA_TUNE_DECODE_CHUNK: causal = 0, rows = S * H, n = Lmax, value = chunk
  *                         (dense, no-allocation and paged decode alike; for
  *                         the paged call Lmax = max_pages * page_size)
@@ -165,7 +178,7 @@ int fa_fwd_auto_block_q(int B, int H, int N, int d, int causal, int window, fa_d
  * positive sizes, value a candidate of its kind) and changes nothing on
  * FA_ERR_INVALID_ARG.
  */
-#define FA_TUNE_FWD_BLOCK_Q 0
+#define FA_TUNE_FWD_TILE 0
 #define FA_TUNE_DECODE_CHUNK 1
 #define FA_TUNE_BWD_DQ_ROWS 2
 #define FA_TUNE_ROW 8

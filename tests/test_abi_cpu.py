@@ -69,7 +69,9 @@ def fwd(lib, q=FAKE, B=1, H=1, N=8, d=64, scale=0.125, causal=0, window=-1, dtyp
     (dict(d=96), 2), (dict(d=257, dtype=0), 2), (dict(d=256, dtype=0, bq=64, bk=32), 1),
     (dict(d=256, dtype=0, bq=32, bk=64), 1), (dict(d=171, dtype=0, bq=32, bk=48), 1), (dict(d=96, dtype=2), 2), (dict(dtype=3), 1),
     (dict(dtype=2, bq=48), 1),
-    (dict(bq=48), 1), (dict(bq=512), 1), (dict(bk=32), 1), (dict(dtype=0, bq=65, bk=4), 1), (dict(dtype=0, bq=0, bk=5), 1),
+    (dict(bq=48), 1), (dict(bq=512), 1), (dict(bq=256, bk=32), 1), (dict(bq=64, bk=96), 1),
+    (dict(d=128, bq=64, bk=128), 1), (dict(bq=256, bk=128), 1),
+    (dict(dtype=0, bq=65, bk=4), 1), (dict(dtype=0, bq=0, bk=5), 1),
     (dict(B=1 << 16, H=1 << 16), 1),
     (dict(N=1 << 23, d=128), 2),          # one slice of N*d bf16 above 2 GiB
     (dict(N=1 << 22, d=128, dtype=0), 2),  # the same in float32
@@ -125,7 +127,7 @@ def test_tune_rejects_bad_arguments_and_starts_empty(lib):
         a = dict(q=FAKE, B=1, H=2, N=64, d=128, scale=0.1, causal=1, window=-1, dtype=1, reps=5)
         a.update(kw)
         return lib.fa_fwd_tune(a["q"], FAKE, FAKE, FAKE, None, a["B"], a["H"], a["N"], a["d"], a["scale"],
-                               a["causal"], a["window"], a["dtype"], None, a["reps"], None, None)
+                               a["causal"], a["window"], a["dtype"], None, a["reps"], None, None, None)
     assert call(q=None) == 1
     assert call(N=0) == 1
     assert call(reps=0) == 1
@@ -139,6 +141,10 @@ def test_tune_rejects_bad_arguments_and_starts_empty(lib):
     assert fa355.fa_fwd_auto_block_q(4, 32, 4096, 128, causal=True) == (256, False)
     assert fa355.fa_fwd_auto_block_q(4, 32, 4096, 128, causal=True, window=1024) == (128, False)
     assert fa355.fa_fwd_auto_block_q(1, 1, 8, 4, dtype=torch.float32) == (64, False)
+    assert fa355.fa_fwd_auto_tile(4, 32, 4096, 128, causal=True) == ((256, 64), False)
+    assert fa355.fa_fwd_auto_tile(4, 32, 4096, 128, causal=True, window=1024) == ((128, 32), False)
+    assert fa355.fa_fwd_auto_tile(1, 2, 64, 128, causal=True) == ((32, 64), False)
+    assert fa355.fa_fwd_auto_tile(1, 1, 8, 4, dtype=torch.float32) == ((64, 64), False)
     assert fa355.fa_fwd_auto_block_q(0, 1, 8, 4)[0] == 0
 
 
@@ -148,14 +154,15 @@ def test_tune_table_export_import_round_trip(tmp_path, lib):
     automatic choice, and a bad row changes nothing."""
     lib.fa_tune_reset()
     K = fa355.TUNE_KINDS
-    rows = [dict(kind=K["fwd_block_q"], dtype=1, d=128, causal=1, window=-1, rows=128, n=4096, value=256),
-            dict(kind=K["fwd_block_q"], dtype=2, d=64, causal=0, window=100, rows=8, n=1024, value=128),
+    rows = [dict(kind=K["fwd_tile"], dtype=1, d=128, causal=1, window=-1, rows=128, n=4096, value=256064),
+            dict(kind=K["fwd_tile"], dtype=2, d=64, causal=0, window=100, rows=8, n=1024, value=128128),
             dict(kind=K["decode_chunk"], dtype=1, d=128, causal=0, window=-1, rows=2048, n=8192, value=2048),
             dict(kind=K["bwd_dq_rows"], dtype=1, d=128, causal=1, window=-1, rows=32, n=4096, value=128)]
     fa355.fa_tune_import(rows)
     assert sorted(fa355.fa_tune_export(), key=str) == sorted(rows, key=str)
     assert fa355.fa_fwd_auto_block_q(1, 8, 1024, 64, window=100, dtype=torch.float16) == (128, True)
-    assert fa355.fa_fwd_auto_block_q(4, 32, 4096, 128, causal=True) == (256, True)
+    assert fa355.fa_fwd_auto_tile(1, 8, 1024, 64, window=100, dtype=torch.float16) == ((128, 128), True)
+    assert fa355.fa_fwd_auto_tile(4, 32, 4096, 128, causal=True) == ((256, 64), True)
     assert fa355.fa_decode_auto_chunk(64, 32, 8192, 128) == (2048, True)
     assert fa355.fa_decode_auto_chunk(64, 32, 8192, 128, window=1024) == (512, False)
     assert fa355.fa_bwd_auto_dq_rows(2, 16, 4096, 128, causal=True) == (128, True)
@@ -167,7 +174,8 @@ def test_tune_table_export_import_round_trip(tmp_path, lib):
     assert fa355.fa_decode_auto_chunk(64, 32, 8192, 128) == (1024, False)
     fa355.load_tuning(path)
     assert sorted(fa355.fa_tune_export(), key=str) == sorted(rows, key=str)
-    for bad in (dict(rows[0], value=96), dict(rows[0], dtype=0), dict(rows[0], d=80),
+    for bad in (dict(rows[0], value=96), dict(rows[0], value=256), dict(rows[0], value=256128),
+                dict(rows[0], value=128128), dict(rows[0], value=64096), dict(rows[0], dtype=0), dict(rows[0], d=80),
                 dict(rows[0], causal=2), dict(rows[0], window=-2), dict(rows[0], n=0), dict(rows[0], kind=3),
                 dict(rows[2], value=300), dict(rows[2], value=8192), dict(rows[2], causal=1),
                 dict(rows[3], value=64), dict(rows[3], value=256 + 128)):

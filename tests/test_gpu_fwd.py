@@ -103,6 +103,36 @@ def test_bf16_ragged_masks_tiles(d, N, causal, window, bq):
     check_lse(lse, L, "L")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 33, 200, 333])
+@pytest.mark.parametrize("causal,window", MASKS)
+@pytest.mark.parametrize("bq,bk", [(32, 32), (64, 32), (128, 32), (32, 128), (64, 128), (128, 128)])
+def test_bf16_key_tiles_32_and_128(d, N, causal, window, bq, bk):
+    """The 32- and 128-key tiles of the 1-4 wave kernels (128 at d = 64 only)
+    over ragged lengths and every mask."""
+    if bk == 128 and d != 64:
+        pytest.skip("128-key tiles are built for d = 64 only")
+    q, k, v = attention_inputs(2, 2, N, d, "bf16", seed=11 * N + d + bk)
+    o, lse = run(q, k, v, causal, window, bq=bq, bk=bk)
+    O, L = oracle.attention_ref(q, k, v, 1 / math.sqrt(d), causal, window)
+    check_bf16(o, O, "O")
+    check_lse(lse, L, "L")
+
+
+@pytest.mark.parametrize("bq,bk", [(128, 32), (64, 128)])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_key_tiles_many_heads_and_fp16(bq, bk, dtype):
+    """A grid of several workgroups per CU in both 16-bit types, the key
+    tiles other than 64, sampled heads against the oracle."""
+    d = 64
+    q, k, v = attention_inputs(2, 48, 900, d, dtype, seed=bq + bk)
+    o, lse = run(q, k, v, True, -1, bq=bq, bk=bk)
+    for b, h in ((0, 3), (1, 47)):
+        O, L = oracle.attention_ref(q[b, h][None], k[b, h][None], v[b, h][None], 1 / math.sqrt(d), True)
+        check_bf16(o[b, h], O[0], "O")
+        check_lse(lse[b, h], L[0], "L")
+
+
 @pytest.mark.parametrize("B,H,N,d", [(1, 160, 700, 128), (2, 96, 1100, 64)])
 @pytest.mark.parametrize("causal,window", [(True, -1), (False, -1), (True, 200), (False, 300)])
 def test_bf16_many_query_tiles_per_workgroup(B, H, N, d, causal, window):

@@ -31,11 +31,15 @@ def test_tune_remembers_the_fastest_tile(dtype, causal, window):
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     best, times, o, lse = fa.fa_fwd_tune(qd, kd, vd, causal=causal, window=window, reps=3)
     assert best in fa.TUNE_CANDIDATES
-    assert all(t > 0 for t in times.values())
-    assert times[best] == min(times.values())
-    assert fa.fa_fwd_auto_block_q(B, H, N, d, causal=causal, window=window, dtype=qd.dtype) == (best, True)
+    ran = {t: ms for t, ms in times.items() if ms >= 0}
+    # every tile ran except the 128-key ones at d = 128
+    assert set(times) - set(ran) == {t for t in fa.TUNE_CANDIDATES if t[1] == 128 and d != 64}
+    assert all(ms > 0 for ms in ran.values())
+    assert times[best] == min(ran.values())
+    assert fa.fa_fwd_auto_tile(B, H, N, d, causal=causal, window=window, dtype=qd.dtype) == (best, True)
+    assert fa.fa_fwd_auto_block_q(B, H, N, d, causal=causal, window=window, dtype=qd.dtype) == (best[0], True)
     # the tuned outputs, an explicit call with that tile and the automatic call agree bit for bit
-    o_ex, l_ex = fa.fa_fwd_ex(qd, kd, vd, best, 64, causal=causal, window=window)
+    o_ex, l_ex = fa.fa_fwd_ex(qd, kd, vd, best[0], best[1], causal=causal, window=window)
     o_auto, l_auto = fa.fa_fwd(qd, kd, vd, causal=causal, window=window)
     torch.cuda.synchronize()
     assert torch.equal(o, o_ex) and torch.equal(lse, l_ex)
@@ -49,8 +53,9 @@ def test_tune_remembers_the_fastest_tile(dtype, causal, window):
 
 def test_tuned_choice_is_per_problem():
     q, k, v = (t.cuda() for t in attention_inputs(1, 4, 300, 64, "bf16", seed=1))
-    best, _, _, _ = fa.fa_fwd_tune(q, k, v, causal=True, reps=2)
-    assert fa.fa_fwd_auto_block_q(1, 4, 300, 64, causal=True) == (best, True)
+    best, times, _, _ = fa.fa_fwd_tune(q, k, v, causal=True, reps=2)
+    assert min(times.values()) > 0  # at d = 64 every tile runs
+    assert fa.fa_fwd_auto_tile(1, 4, 300, 64, causal=True) == (best, True)
     assert not fa.fa_fwd_auto_block_q(1, 4, 301, 64, causal=True)[1]
     assert not fa.fa_fwd_auto_block_q(1, 4, 300, 64, causal=False)[1]
     assert not fa.fa_fwd_auto_block_q(1, 4, 300, 64, causal=True, dtype=torch.float16)[1]

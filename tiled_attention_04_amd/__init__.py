@@ -30,6 +30,7 @@ from .fa355 import (  # noqa: F401
     fa_fwd_ex,
     fa_fwd_tune,
     fa_fwd_auto_block_q,
+    fa_fwd_auto_tile,
     fa_tune_export,
     fa_tune_import,
     fa_tune_reset,

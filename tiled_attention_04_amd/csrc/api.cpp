@@ -60,23 +60,26 @@ fa_status check_dense(int B, int H, int N, int d, float scale, int causal, int w
   return FA_OK;
 }
 
-int auto_block_q(int B, int H, int N, int window) {
+// The built-in forward tile, as block_q * 1000 + block_k.
+int auto_tile(int B, int H, int N, int window) {
   // Prefer the 8-wave ping-pong kernel (256 query rows, one workgroup per
   // CU) while it still fills the 256 CUs of an MI355X -- except under a
-  // sliding window, where the 4-wave kernel measured faster; then 4-wave
-  // workgroups (two per CU); then smaller query tiles.
+  // sliding window, where the 4-wave kernel with 32-key tiles measured
+  // fastest (7% ahead of 64-key tiles, 8% ahead of the ping-pong kernel, on
+  // a 1024-token window over 4 x 32 x 4096 x 128); then 4-wave workgroups
+  // (two per CU); then smaller query tiles.
   const long long bh = (long long)B * H;
-  if (window < 0 && bh * ((N + 255) / 256) >= 256) return 256;
-  if (bh * ((N + 127) / 128) >= 512) return 128;
-  if (bh * ((N + 63) / 64) >= 256) return 64;
-  return 32;
+  if (window < 0 && bh * ((N + 255) / 256) >= 256) return 256064;
+  if (bh * ((N + 127) / 128) >= 512) return window >= 0 ? 128032 : 128064;
+  if (bh * ((N + 63) / 64) >= 256) return 64064;
+  return 32064;
 }
 
 // Choices measured by the tuning calls, by kind and problem: automatic calls
 // with the same key use them instead of the built-in heuristics.  Key:
 // (kind, dtype, d, causal, window, B*H or S*H, N or Lmax).
 enum TuneKind {
-  kTuneFwd = FA_TUNE_FWD_BLOCK_Q,
+  kTuneFwd = FA_TUNE_FWD_TILE,
   kTuneDecode = FA_TUNE_DECODE_CHUNK,
   kTuneBwd = FA_TUNE_BWD_DQ_ROWS
 };
@@ -99,7 +102,8 @@ void remember(const TuneKey& key, int value) {
   g_tuned[key] = value;
 }
 
-int tuned_block_q(fa_dtype dtype, int d, int causal, int window, int B, int H, int N) {
+// A forward tile is remembered as block_q * 1000 + block_k.
+int tuned_tile(fa_dtype dtype, int d, int causal, int window, int B, int H, int N) {
   return tuned_value(tune_key(kTuneFwd, dtype, d, causal, window, (long long)B * H, N));
 }
 
@@ -146,7 +150,20 @@ struct EventPair {
   }
 };
 
-constexpr int kTuneCandidates[4] = {32, 64, 128, 256};
+// Forward tiles (block_q, block_k) fa_fwd_tune measures, as block_q * 1000 +
+// block_k: the 1-4 wave kernels with 32-, 64- and 128-key tiles, and the
+// 8-wave ping-pong kernel (64-key tiles only: its three LDS stages would not
+// fit 128).
+constexpr int kTuneCandidates[FA_FWD_TUNE_CANDIDATES] = {32032,  32064,  32128,  64032,  64064,
+                                                         64128,  128032, 128064, 128128, 256064};
+// (128-key tiles at d = 64 only: at d = 128 they exceed the register file.)
+bool valid_16bit_tile(int block_q, int block_k, int d) {
+  if (block_k == 128 && d != 64) return false;
+  for (int c : kTuneCandidates) {
+    if (c == block_q * 1000 + block_k) return true;
+  }
+  return false;
+}
 constexpr int kDecodeTuneChunks[FA_DECODE_TUNE_CANDIDATES] = {256, 512, 1024, 2048, 4096};
 constexpr int kDecodeTuneCount = FA_DECODE_TUNE_CANDIDATES;
 
@@ -242,14 +259,19 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float*
   }
   if (d != 64 && d != 128)
     return fail(FA_ERR_UNSUPPORTED, "%s forward supports d in {64, 128} (got %d)", dtype_name(dtype), d);
-  if (block_q == 0) block_q = tuned_block_q(dtype, d, causal, window, B, H, N);
-  if (block_q == 0) block_q = auto_block_q(B, H, N, window);
+  if (block_q == 0) {  // the tuned tile, else the heuristic's
+    int t = tuned_tile(dtype, d, causal, window, B, H, N);
+    if (t == 0) t = auto_tile(B, H, N, window);
+    block_q = t / 1000;
+    if (block_k == 0) block_k = t % 1000;
+  }
   if (block_k == 0) block_k = 64;
-  if ((block_q != 32 && block_q != 64 && block_q != 128 && block_q != 256) || block_k != 64)
-    return fail(FA_ERR_INVALID_ARG, "16-bit tiles must be {32,64,128,256} x 64 (got %d x %d)", block_q, block_k);
+  if (!valid_16bit_tile(block_q, block_k, d))
+    return fail(FA_ERR_INVALID_ARG, "16-bit tiles must be {32,64,128} x {32,64} (x 128 too at d = 64) or 256 x 64 "
+                "(got %d x %d at d = %d)", block_q, block_k, d);
   const long long wgs = (long long)B * H * ((N + block_q - 1) / block_q);
   if (wgs * 2 * block_q > kMaxThreadsPerLaunch) return fail(FA_ERR_UNSUPPORTED, "grid too large");
-  return done(fa::launch_fwd_mfma(q, k, v, o, lse, B, H, N, d, scale, mask, block_q,
+  return done(fa::launch_fwd_mfma(q, k, v, o, lse, B, H, N, d, scale, mask, block_q, block_k,
                                   dtype == FA_FP16, (hipStream_t)stream),
               dtype == FA_FP16 ? "fa_fwd (fp16)" : "fa_fwd (bf16)");
 }
@@ -261,7 +283,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 
 fa_status fa_fwd_tune(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                       int N, int d, float scale, int causal, int window, fa_dtype dtype, void* stream,
-                      int reps, int* best_block_q, float* times_ms) {
+                      int reps, int* best_block_q, int* best_block_k, float* times_ms) {
   if (!q || !k || !v || !o) return fail(FA_ERR_INVALID_ARG, "q, k, v and o must be non-null");
   fa_status st = check_dense(B, H, N, d, scale, causal, window, dtype);
   if (st != FA_OK) return st;
@@ -269,7 +291,8 @@ fa_status fa_fwd_tune(const void* q, const void* k, const void* v, void* o, floa
   if (d != 64 && d != 128)
     return fail(FA_ERR_UNSUPPORTED, "%s forward supports d in {64, 128} (got %d)", dtype_name(dtype), d);
   if (reps < 1 || reps > 1000) return fail(FA_ERR_INVALID_ARG, "reps must be 1..1000 (got %d)", reps);
-  for (int bq : kTuneCandidates) {  // every candidate's grid must be launchable
+  for (int c : kTuneCandidates) {  // every candidate's grid must be launchable
+    const int bq = c / 1000;
     const long long wgs = (long long)B * H * ((N + bq - 1) / bq);
     if (wgs * 2 * bq > kMaxThreadsPerLaunch) return fail(FA_ERR_UNSUPPORTED, "grid too large");
   }
@@ -281,36 +304,48 @@ fa_status fa_fwd_tune(const void* q, const void* k, const void* v, void* o, floa
   hipError_t err = hipSuccess;
   float best_ms = 0.f;
   int best = 0;
-  for (int i = 0; i < 4 && err == hipSuccess; ++i) {
-    const int bq = kTuneCandidates[i];
+  for (int i = 0; i < FA_FWD_TUNE_CANDIDATES && err == hipSuccess; ++i) {
+    const int bq = kTuneCandidates[i] / 1000, bk = kTuneCandidates[i] % 1000;
+    if (!valid_16bit_tile(bq, bk, d)) {
+      if (times_ms) times_ms[i] = -1.f;
+      continue;
+    }
     const float ms = time_launches(evs.ev[0], evs.ev[1], s, reps, err, [&] {
-      return fa::launch_fwd_mfma(q, k, v, o, lse, B, H, N, d, scale, mask, bq, f16, s);
+      return fa::launch_fwd_mfma(q, k, v, o, lse, B, H, N, d, scale, mask, bq, bk, f16, s);
     });
     if (times_ms) times_ms[i] = ms;
     if (err == hipSuccess && (best == 0 || ms < best_ms)) {
-      best = bq;
+      best = kTuneCandidates[i];
       best_ms = ms;
     }
   }
   if (err != hipSuccess) return done(err, "fa_fwd_tune");
   remember(tune_key(kTuneFwd, dtype, d, causal, window, (long long)B * H, N), best);
-  if (best_block_q) *best_block_q = best;
+  if (best_block_q) *best_block_q = best / 1000;
+  if (best_block_k) *best_block_k = best % 1000;
   // Leave o and lse holding the chosen tile's result.
-  return done(fa::launch_fwd_mfma(q, k, v, o, lse, B, H, N, d, scale, mask, best, f16, s),
+  return done(fa::launch_fwd_mfma(q, k, v, o, lse, B, H, N, d, scale, mask, best / 1000, best % 1000, f16, s),
               "fa_fwd_tune");
 }
 
 int fa_fwd_auto_block_q(int B, int H, int N, int d, int causal, int window, fa_dtype dtype,
-                        int* tuned) {
+                        int* block_k, int* tuned) {
   if (tuned) *tuned = 0;
+  if (block_k) *block_k = 0;
   if (check_dense(B, H, N, d, 0.f, causal, window, dtype) != FA_OK) return 0;
-  if (dtype == FA_FP32) return 64;
-  const int t = tuned_block_q(dtype, d, causal, window, B, H, N);
+  if (dtype == FA_FP32) {
+    if (block_k) *block_k = d <= 128 ? 64 : 32;
+    return d <= 128 ? 64 : 32;
+  }
+  const int t = tuned_tile(dtype, d, causal, window, B, H, N);
   if (t != 0) {
     if (tuned) *tuned = 1;
-    return t;
+    if (block_k) *block_k = t % 1000;
+    return t / 1000;
   }
-  return auto_block_q(B, H, N, window);
+  const int a = auto_tile(B, H, N, window);
+  if (block_k) *block_k = a % 1000;
+  return a / 1000;
 }
 
 fa_status fa_decode_tune(const void* q, const void* kcache, const void* vcache, const int32_t* seqlens,
@@ -405,8 +440,8 @@ fa_status fa_tune_import(const int64_t* rows, int n_rows) {
   for (int i = 0; i < n_rows; ++i) {  // validate everything before changing the table
     const int64_t* r = rows + FA_TUNE_ROW * (size_t)i;
     bool ok_value = false;
-    if (r[0] == FA_TUNE_FWD_BLOCK_Q) {
-      for (int bq : kTuneCandidates) ok_value |= r[7] == bq;
+    if (r[0] == FA_TUNE_FWD_TILE) {
+      ok_value = r[7] > 0 && r[7] <= INT_MAX && valid_16bit_tile((int)(r[7] / 1000), (int)(r[7] % 1000), (int)r[2]);
     } else if (r[0] == FA_TUNE_DECODE_CHUNK) {
       for (int c : kDecodeTuneChunks) ok_value |= r[7] == c;
       ok_value &= r[3] == 0;

@@ -25,10 +25,11 @@ hipError_t launch_fwd_fp32(const float* q, const float* k, const float* v, float
                            int block_k, hipStream_t stream);
 
 // 16-bit MFMA forward (bf16, or fp16 when f16), d in {64, 128}, block_q in
-// {32, 64, 128, 256}, block_k = 64.
+// {32, 64, 128} with block_k in {32, 64, 128}, or block_q = 256 with
+// block_k = 64.
 hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int H, int N, int d, float scale, Mask mask, int block_q,
-                           bool f16, hipStream_t stream);
+                           int block_k, bool f16, hipStream_t stream);
 
 // Split-K decode (+ merge), any Elem, d in {64, 128}.
 size_t decode_workspace_bytes(int S, int H, int Lmax, int d, int chunk);

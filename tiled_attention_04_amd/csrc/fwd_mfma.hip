@@ -13,7 +13,9 @@
 //
 // Mapping onto CDNA4:
 //  * A workgroup of NW waves owns BQ = 32*NW query rows; each wave owns 32.
-//    Key/value tiles are 64 rows.  They go from HBM straight into LDS
+//    Key/value tiles are BK = 64 rows (32, or at d = 64 also 128, on
+//    request for the 1-4 wave kernels; the 8-wave ping-pong kernel's three
+//    LDS stages leave room for 64 only).  They go from HBM straight into LDS
 //    (buffer_load ... lds, 16 bytes per lane): no register staging and no
 //    ALU work to place them.  K and V are double-buffered.
 //  * Scores are computed transposed, S^T = K Q^T: K (from LDS) is the A
@@ -53,19 +55,26 @@ namespace {
 
 constexpr int kBK = 64;
 
-template <int D>
+// LDS layout of one K and one V tile of BK key rows (BK = 32, 64 or 128),
+// each rounded up to whole 1 KB direct-load blocks (a block's bytes past the
+// tile's rows land in that padding and are never read).
+template <int D, int BK = kBK>
 struct Tile {
   static constexpr int kRowBytes = D * 2;
   static constexpr int kKPitch = kRowBytes + 16;  // bytes per K row in LDS
   static constexpr int kVPitch = kRowBytes + 64;  // bytes per V row in LDS
-  static constexpr int kKBytes = kBK * kKPitch;
-  static constexpr int kVBytes = kBK * kVPitch;
+  static constexpr int kKBytes = (BK * kKPitch + 1023) / 1024 * 1024;
+  static constexpr int kVBytes = (BK * kVPitch + 1023) / 1024 * 1024;
   static constexpr int kKBlocks = kKBytes / 1024;  // 1 KB per wave-wide direct load
   static constexpr int kVBlocks = kVBytes / 1024;
-  static_assert(kKBytes % 1024 == 0 && kVBytes % 1024 == 0, "tiles must be whole 1 KB blocks");
   static constexpr int kSmem = 2 * (kKBytes + kVBytes);
-  // Two waves' O blocks (32 rows of 2 D + 16 bytes each) fit a K tile.
-  static_assert(2 * 32 * (2 * D + 16) <= kKBytes && 2 * 32 * (2 * D + 16) <= kVBytes, "O staging");
+  static constexpr int kNB = BK / 32;  // 32-key blocks per tile
+  static_assert(BK == 32 || BK == 64 || BK == 128, "key tiles of 32, 64 or 128 rows");
+  // O staging: one wave's 32 rows of 2 D + 16 bytes fit each of the four
+  // buffers, two waves' fit a K tile from 64 keys up.
+  static_assert(32 * (2 * D + 16) <= kKBytes && 32 * (2 * D + 16) <= kVBytes, "O staging");
+  static_assert(BK < 64 || (2 * 32 * (2 * D + 16) <= kKBytes && 2 * 32 * (2 * D + 16) <= kVBytes),
+                "O staging");
 };
 
 // Issue this wave's share of the direct loads of one tile (rows k0.. of a
@@ -93,9 +102,10 @@ constexpr float kTau = 8.f;
 // to -inf ("Build a FlashAttention-2 Inference Kernel from Scratch in Pure
 // Python", Step 2).  Only tiles that straddle a mask boundary or the end of
 // the sequence need this.
-__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int lo, int hi, int h) {
+template <int NB>
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[NB], int lo, int hi, int h) {
 #pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2) {
+  for (int kb2 = 0; kb2 < NB; ++kb2) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int rel = kb2 * 32 + c_row(r, h);
@@ -149,27 +159,28 @@ constexpr float kLaneSumFloorF16 = 0.5f;
 // sum at a time.  The batched order measured 2-4% faster in the kernels that
 // run two workgroups per CU and 1-4% slower in the ping-pong kernel, whose
 // softmax shares each SIMD with the other group's matrix work.
-template <typename T, int CB, bool kBatched>
-__device__ __forceinline__ void softmax_tile(const f32x16 (&s)[2], uint32_t (&pk)[2][8],
+template <typename T, int CB, bool kBatched, int NB = 2>
+__device__ __forceinline__ void softmax_tile(const f32x16 (&s)[NB], uint32_t (&pk)[NB][8],
                                              f32x16 (&oacc)[CB], float& m_ref, float& l_run,
                                              float c) {
   auto exps = [&](float ref) {
     if constexpr (kBatched) {
-      float x[32];
+      constexpr int E = 16 * NB;  // scores per lane
+      float x[E];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) x[i] = __builtin_fmaf(s[i >> 4][i & 15], c, -ref);
+      for (int i = 0; i < E; ++i) x[i] = __builtin_fmaf(s[i >> 4][i & 15], c, -ref);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) x[i] = __builtin_amdgcn_exp2f(x[i]);
+      for (int i = 0; i < E; ++i) x[i] = __builtin_amdgcn_exp2f(x[i]);
       float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 32; ++i) part[i & 3] += x[i];
+      for (int i = 0; i < E; ++i) part[i & 3] += x[i];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) pk[i >> 3][i & 7] = pack2<T>(x[2 * i], x[2 * i + 1]);
+      for (int i = 0; i < E / 2; ++i) pk[i >> 3][i & 7] = pack2<T>(x[2 * i], x[2 * i + 1]);
       return (part[0] + part[1]) + (part[2] + part[3]);
     } else {
       float sum = 0.f;
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
+      for (int kb2 = 0; kb2 < NB; ++kb2) {
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
           const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][r], c, -ref));
@@ -194,7 +205,7 @@ __device__ __forceinline__ void softmax_tile(const f32x16 (&s)[2], uint32_t (&pk
   }
   float mx = kNegInf;
 #pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2) {
+  for (int kb2 = 0; kb2 < NB; ++kb2) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb2][r]);
   }
@@ -273,12 +284,13 @@ __device__ __forceinline__ void schedule_pipeline() {
   }
 }
 
-template <typename T, int D, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1)))
+template <typename T, int D, int NW, int BK>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 4 && BK < 128 ? 2 : 1)))
 void fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k,
                      const T* __restrict__ v, T* __restrict__ o, float* __restrict__ lse,
                      int BH, int N, int nqt, float c_log2, int negate_q, int causal, int window) {
-  using TL = Tile<D>;
+  using TL = Tile<D, BK>;
+  constexpr int NB = TL::kNB;  // 32-key blocks per key tile
   constexpr int NT = 64 * NW;  // threads
   constexpr int BQ = 32 * NW;
   constexpr int KS = D / 16;  // MFMA steps over the head dimension
@@ -344,7 +356,7 @@ void fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k,
   const int q_hi = q0 + BQ - 1;
   const int kmin = window >= 0 ? max(0, q0 - window) : 0;
   const int kmax = causal ? min(N - 1, q_hi) : N - 1;
-  const int kt0 = kmin / kBK, kt1 = kmax / kBK + 1;
+  const int kt0 = kmin / BK, kt1 = kmax / BK + 1;
   // Keys this lane's query row may see (the tail of the sequence included).
   const int key_lo = window >= 0 ? qi - window : 0;
   const int key_hi = causal ? min(qi, N - 1) : N - 1;
@@ -364,20 +376,20 @@ void fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k,
   float m_ref = kNegInf, l_run = 0.f;  // log2 units
 
   __syncthreads();  // LDS zeroed before any direct load lands
-  load_tile<D, NW, TL::kKBlocks, TL::kKPitch, PRE>(kg, kt0 * kBK, N, Kb0, kpre, w, lane);
-  load_tile<D, NW, TL::kVBlocks, TL::kVPitch, PRE>(vg, kt0 * kBK, N, Vb0, vpre, w, lane);
+  load_tile<D, NW, TL::kKBlocks, TL::kKPitch, PRE>(kg, kt0 * BK, N, Kb0, kpre, w, lane);
+  load_tile<D, NW, TL::kVBlocks, TL::kVPitch, PRE>(vg, kt0 * BK, N, Vb0, vpre, w, lane);
   if (kt0 + 1 < kt1)
-    load_tile<D, NW, TL::kKBlocks, TL::kKPitch, PRE>(kg, (kt0 + 1) * kBK, N, Kb1, kpre, w, lane);
+    load_tile<D, NW, TL::kKBlocks, TL::kKPitch, PRE>(kg, (kt0 + 1) * BK, N, Kb1, kpre, w, lane);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 #pragma unroll
   for (int s = 0; s < KS; ++s)
     qf[s] = as_vec8<T>(uint4{q_raw[s].x ^ q_neg, q_raw[s].y ^ q_neg, q_raw[s].z ^ q_neg, q_raw[s].w ^ q_neg});
 
-  // S^T = K Q^T of the first tile for its two 32-key blocks.
-  f32x16 s_a[2];
+  // S^T = K Q^T of the first tile for its 32-key blocks.
+  f32x16 s_a[NB];
 #pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2) {
+  for (int kb2 = 0; kb2 < NB; ++kb2) {
     s_a[kb2] = f32x16{};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -390,25 +402,25 @@ void fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k,
   // One pipeline step for tile kt, whose parity selects the buffers at
   // compile time: K_{kt+1} is in the "next" K buffer, V_kt in the "current"
   // V buffer; S_kt is in s_cur and S_{kt+1} is written to s_next.
-  auto step = [&](auto parity, f32x16 (&s_cur)[2], f32x16 (&s_next)[2], int kt) {
+  auto step = [&](auto parity, f32x16 (&s_cur)[NB], f32x16 (&s_next)[NB], int kt) {
     constexpr int P = decltype(parity)::value;
     char* const k_next = P ? Kb0 : Kb1;
     char* const k_refill = P ? Kb1 : Kb0;
     char* const v_cur = P ? Vb1 : Vb0;
     char* const v_next = P ? Vb0 : Vb1;
     const bool has_next = kt + 1 < kt1;
-    if (has_next) load_tile<D, NW, TL::kVBlocks, TL::kVPitch, PRE>(vg, (kt + 1) * kBK, N, v_next, vpre, w, lane);
-    if (kt + 2 < kt1) load_tile<D, NW, TL::kKBlocks, TL::kKPitch, PRE>(kg, (kt + 2) * kBK, N, k_refill, kpre, w, lane);
+    if (has_next) load_tile<D, NW, TL::kVBlocks, TL::kVPitch, PRE>(vg, (kt + 1) * BK, N, v_next, vpre, w, lane);
+    if (kt + 2 < kt1) load_tile<D, NW, TL::kKBlocks, TL::kKPitch, PRE>(kg, (kt + 2) * BK, N, k_refill, kpre, w, lane);
 
-    const int k0 = kt * kBK;
-    const bool need_mask = (k0 + kBK > N) || (causal && k0 + kBK - 1 > q0) ||
+    const int k0 = kt * BK;
+    const bool need_mask = (k0 + BK > N) || (causal && k0 + BK - 1 > q0) ||
                            (window >= 0 && k0 < q_hi - window);
     if (need_mask) mask_tile(s_cur, key_lo - k0, key_hi - k0, h);
 
     // Scores of the next tile on the matrix cores (on the last tile they are
     // computed from whatever the buffer holds and discarded) ...
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
+    for (int kb2 = 0; kb2 < NB; ++kb2) {
       s_next[kb2] = mfma32(*(const vec8<T>*)(k_next + k_rd + kb2 * 32 * TL::kKPitch), qf[0], f32x16{});
 #pragma unroll
       for (int s = 1; s < KS; ++s) {
@@ -418,13 +430,16 @@ void fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k,
     }
 
     // ... while the vector ALUs run the softmax of this one.
-    uint32_t pk[2][8];
-    softmax_tile<T, CB, true>(s_cur, pk, oacc, m_ref, l_run, c_log2);
+    uint32_t pk[NB][8];
+    // (Batched exponentials hold all of a lane's scores at once: with
+    // 128-key tiles that is 64 more live registers than the kernel has room
+    // for.)
+    softmax_tile<T, CB, (NB <= 2), NB>(s_cur, pk, oacc, m_ref, l_run, c_log2);
 
     // O^T += V^T P^T, 16 keys per step.
     const char* vt = v_cur + v_rd;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < 2 * NB; ++s) {
       const uint4 pw = {pk[s >> 1][4 * (s & 1) + 0], pk[s >> 1][4 * (s & 1) + 1],
                         pk[s >> 1][4 * (s & 1) + 2], pk[s >> 1][4 * (s & 1) + 3]};
       const vec8<T> pb = as_vec8<T>(pw);
@@ -443,12 +458,12 @@ void fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k,
     // MFMAs ahead, and each score MFMA is followed by a slice of the softmax
     // so that the matrix cores and the vector ALUs work at the same time; the
     // V^T reads likewise run ahead of the PV MFMAs.
-    schedule_pipeline<2 * KS, 4 * CB>();
+    schedule_pipeline<NB * KS, 2 * NB * CB>();
     __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
     __syncthreads();
   };
 
-  f32x16 s_b[2];
+  f32x16 s_b[NB];
   for (int kt = kt0; kt < kt1; kt += 2) {  // two tiles per trip: s_a and s_b swap roles
     step(std::integral_constant<int, 0>{}, s_a, s_b, kt);
     if (kt + 1 < kt1) step(std::integral_constant<int, 1>{}, s_b, s_a, kt + 1);
@@ -457,10 +472,11 @@ void fwd_mfma_kernel(const T* __restrict__ q, const T* __restrict__ k,
   // Epilogue: O = O / l, L = m ln2 + ln l.
   const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  // O through LDS (the loop's last barrier freed the K buffers): two waves
-  // per buffer.
-  store_o_rows<T, D, CB>(oacc, inv, (w < 2 ? Kb0 : Kb1) + (w & 1) * 32 * (2 * D + 16), o + base,
-                         q0 + 32 * w, N, lane);
+  // O through LDS (the loop's last barrier freed the buffers): two waves per
+  // K buffer, or with 32-key tiles one wave per buffer.
+  char* const stage = BK >= 64 ? (w < 2 ? Kb0 : Kb1) + (w & 1) * 32 * (2 * D + 16)
+                               : (w == 0 ? Kb0 : w == 1 ? Kb1 : w == 2 ? Vb0 : Vb1);
+  store_o_rows<T, D, CB>(oacc, inv, stage, o + base, q0 + 32 * w, N, lane);
   if (qi < N && h == 0 && lse != nullptr)
     lse[(size_t)bh * N + qi] = l_tot > 0.f ? m_ref * kLn2 + logf(l_tot) : kNegInf;
 }
@@ -799,17 +815,30 @@ void fwd_pingpong_kernel(const T* __restrict__ q, const T* __restrict__ k,
 }
 
 
-template <typename T, int D, int NW>
+template <typename T, int D, int NW, int BK>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                   int N, float scale, Mask mask, hipStream_t stream) {
   constexpr int BQ = 32 * NW;
   const int nqt = (N + BQ - 1) / BQ;
   const long long grid = (long long)nqt * B * H;
-  hipLaunchKernelGGL((fwd_mfma_kernel<T, D, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, stream,
+  hipLaunchKernelGGL((fwd_mfma_kernel<T, D, NW, BK>), dim3((unsigned)grid), dim3(64 * NW), 0, stream,
                      (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, B * H, N, nqt,
                      fmaxf(fabsf(scale) * kLog2e, 1e-30f), scale < 0.f ? 1 : 0, mask.causal,
                      mask.window);
   return hipGetLastError();
+}
+
+// 128-key tiles for d = 64 only: at d = 128 two 128-key score tiles, O and Q
+// take more registers than a wave has, and the spills would put scratch
+// memory (and its allocation) on the path.
+template <typename T, int D, int NW>
+hipError_t launch_bk(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                     int N, float scale, Mask mask, int block_k, hipStream_t stream) {
+  if (block_k == 32) return launch<T, D, NW, 32>(q, k, v, o, lse, B, H, N, scale, mask, stream);
+  if constexpr (D == 64) {
+    if (block_k == 128) return launch<T, D, NW, 128>(q, k, v, o, lse, B, H, N, scale, mask, stream);
+  }
+  return launch<T, D, NW, 64>(q, k, v, o, lse, B, H, N, scale, mask, stream);
 }
 
 template <typename T, int D>
@@ -826,26 +855,26 @@ hipError_t launch_pingpong(const void* q, const void* k, const void* v, void* o,
 
 template <typename T>
 hipError_t dispatch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                    int N, int d, float scale, Mask mask, int block_q, hipStream_t stream) {
+                    int N, int d, float scale, Mask mask, int block_q, int block_k, hipStream_t stream) {
   if (d == 128) {
     if (block_q == 256) return launch_pingpong<T, 128>(q, k, v, o, lse, B, H, N, scale, mask, stream);
-    if (block_q == 128) return launch<T, 128, 4>(q, k, v, o, lse, B, H, N, scale, mask, stream);
-    if (block_q == 64) return launch<T, 128, 2>(q, k, v, o, lse, B, H, N, scale, mask, stream);
-    return launch<T, 128, 1>(q, k, v, o, lse, B, H, N, scale, mask, stream);
+    if (block_q == 128) return launch_bk<T, 128, 4>(q, k, v, o, lse, B, H, N, scale, mask, block_k, stream);
+    if (block_q == 64) return launch_bk<T, 128, 2>(q, k, v, o, lse, B, H, N, scale, mask, block_k, stream);
+    return launch_bk<T, 128, 1>(q, k, v, o, lse, B, H, N, scale, mask, block_k, stream);
   }
   if (block_q == 256) return launch_pingpong<T, 64>(q, k, v, o, lse, B, H, N, scale, mask, stream);
-  if (block_q == 128) return launch<T, 64, 4>(q, k, v, o, lse, B, H, N, scale, mask, stream);
-  if (block_q == 64) return launch<T, 64, 2>(q, k, v, o, lse, B, H, N, scale, mask, stream);
-  return launch<T, 64, 1>(q, k, v, o, lse, B, H, N, scale, mask, stream);
+  if (block_q == 128) return launch_bk<T, 64, 4>(q, k, v, o, lse, B, H, N, scale, mask, block_k, stream);
+  if (block_q == 64) return launch_bk<T, 64, 2>(q, k, v, o, lse, B, H, N, scale, mask, block_k, stream);
+  return launch_bk<T, 64, 1>(q, k, v, o, lse, B, H, N, scale, mask, block_k, stream);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int H, int N, int d, float scale, Mask mask, int block_q,
-                           bool f16, hipStream_t stream) {
-  if (f16) return dispatch<fa::f16>(q, k, v, o, lse, B, H, N, d, scale, mask, block_q, stream);
-  return dispatch<bf16>(q, k, v, o, lse, B, H, N, d, scale, mask, block_q, stream);
+                           int block_k, bool f16, hipStream_t stream) {
+  if (f16) return dispatch<fa::f16>(q, k, v, o, lse, B, H, N, d, scale, mask, block_q, block_k, stream);
+  return dispatch<bf16>(q, k, v, o, lse, B, H, N, d, scale, mask, block_q, block_k, stream);
 }
 
 }  // namespace fa

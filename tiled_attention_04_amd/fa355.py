@@ -32,8 +32,8 @@ SIGNATURES = {
     "fa_last_error": (ctypes.c_char_p, []),
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
     "fa_fwd_ex": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P, _I, _I]),
-    "fa_fwd_tune": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P, _I, _P, _P]),
-    "fa_fwd_auto_block_q": (_I, [_I, _I, _I, _I, _I, _I, _I, _P]),
+    "fa_fwd_tune": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P, _I, _P, _P, _P]),
+    "fa_fwd_auto_block_q": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, _P]),
     "fa_tune_reset": (None, []),
     "fa_tune_export": (_I, [_P, _I]),
     "fa_tune_import": (_I, [_P, _I]),
@@ -138,14 +138,16 @@ def fa_fwd(q, k, v, *, causal: bool = False, window: int = -1, scale=None, o=Non
                      stream=stream)
 
 
-TUNE_CANDIDATES = (32, 64, 128, 256)
+# (block_q, block_k) tiles fa_fwd_tune measures, in its order.
+TUNE_CANDIDATES = ((32, 32), (32, 64), (32, 128), (64, 32), (64, 64), (64, 128), (128, 32), (128, 64),
+                   (128, 128), (256, 64))
 
 
 def fa_fwd_tune(q, k, v, *, causal: bool = False, window: int = -1, scale=None, reps: int = 10,
                 o=None, lse=None, stream=None):
-    """Time every query-tile size of the 16-bit forward on these inputs and
-    remember the fastest for later automatic calls (synchronises the stream).
-    Returns (best block_q, {block_q: mean ms per call}, o, lse)."""
+    """Time every tile (block_q, block_k) of the 16-bit forward on these inputs
+    and remember the fastest for later automatic calls (synchronises the
+    stream).  Returns (best (block_q, block_k), {tile: mean ms per call}, o, lse)."""
     B, H, N, d = q.shape
     dt = q.dtype
     if dt not in _DTYPE:
@@ -159,21 +161,28 @@ def fa_fwd_tune(q, k, v, *, causal: bool = False, window: int = -1, scale=None, 
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     op = _dev(o, "o", dt, q.shape)
     lp = _dev(lse, "lse", torch.float32, (B, H, N))
-    best = ctypes.c_int(0)
-    times = (ctypes.c_float * 4)()
+    best_q, best_k = ctypes.c_int(0), ctypes.c_int(0)
+    times = (ctypes.c_float * len(TUNE_CANDIDATES))()
     _check(lib().fa_fwd_tune(qp, kp, vp, op, lp, B, H, N, d, _default_scale(scale, d), int(causal),
-                             int(window), _DTYPE[dt], _stream(stream), int(reps), ctypes.byref(best),
-                             times))
-    return best.value, dict(zip(TUNE_CANDIDATES, list(times))), o, lse
+                             int(window), _DTYPE[dt], _stream(stream), int(reps), ctypes.byref(best_q),
+                             ctypes.byref(best_k), times))
+    return (best_q.value, best_k.value), dict(zip(TUNE_CANDIDATES, list(times))), o, lse
+
+
+def fa_fwd_auto_tile(B: int, H: int, N: int, d: int, *, causal: bool = False, window: int = -1,
+                     dtype=torch.bfloat16):
+    """((block_q, block_k) an automatic fa_fwd call uses, whether it was tuned)."""
+    tuned, bk = ctypes.c_int(0), ctypes.c_int(0)
+    bq = lib().fa_fwd_auto_block_q(B, H, N, d, int(causal), int(window), _DTYPE[dtype], ctypes.byref(bk),
+                                   ctypes.byref(tuned))
+    return (int(bq), int(bk.value)), bool(tuned.value)
 
 
 def fa_fwd_auto_block_q(B: int, H: int, N: int, d: int, *, causal: bool = False, window: int = -1,
                         dtype=torch.bfloat16):
     """(block_q an automatic fa_fwd call uses, whether it was tuned)."""
-    tuned = ctypes.c_int(0)
-    bq = lib().fa_fwd_auto_block_q(B, H, N, d, int(causal), int(window), _DTYPE[dtype],
-                                   ctypes.byref(tuned))
-    return int(bq), bool(tuned.value)
+    (bq, _), tuned = fa_fwd_auto_tile(B, H, N, d, causal=causal, window=window, dtype=dtype)
+    return bq, tuned
 
 
 def fa_tune_reset() -> None:
@@ -182,9 +191,10 @@ def fa_tune_reset() -> None:
 
 # Columns of a remembered tuning choice; "kind" is one of TUNE_KINDS, "rows"
 # is B*H (S*H for decode), "n" is N (Lmax for decode) and "value" the choice:
-# block_q, the decode split length or the dQ kernel's query rows.
+# block_q * 1000 + block_k, the decode split length or the dQ kernel's query
+# rows.
 TUNE_FIELDS = ("kind", "dtype", "d", "causal", "window", "rows", "n", "value")
-TUNE_KINDS = {"fwd_block_q": 0, "decode_chunk": 1, "bwd_dq_rows": 2}
+TUNE_KINDS = {"fwd_tile": 0, "decode_chunk": 1, "bwd_dq_rows": 2}
 _ROW = len(TUNE_FIELDS)
 
 

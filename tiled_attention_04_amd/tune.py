@@ -4,8 +4,8 @@
 
 Three tables (markdown), each setting the measured candidates beside the
 built-in heuristic's choice:
-  * the forward's query tile (fa_fwd_tune: 32, 64, 128 and 256 rows, 64-key
-    tiles);
+  * the forward's tile (fa_fwd_tune: 32, 64 or 128 query rows with 32-, 64-
+    or (at d = 64) 128-key tiles, and 256 x 64);
   * the decode's split length (fa_decode_tune: 256 to 4096 tokens);
   * the backward's dQ kernel (fa_bwd_tune: 128 or 256 query rows per
     workgroup).
@@ -66,19 +66,20 @@ def main():
     ap.add_argument("--save", default=None, help="write the tuned choices to this JSON file")
     args = ap.parse_args()
     dev = torch.device("cuda:0")
-    print("| workload | " + " | ".join(f"{b} rows ms" for b in fa355.TUNE_CANDIDATES)
+    print("| workload | " + " | ".join(f"{bq}x{bk} ms" for bq, bk in fa355.TUNE_CANDIDATES)
           + " | fastest | TFLOP/s | heuristic | heuristic ms |")
     print("|---|" + "---|" * (len(fa355.TUNE_CANDIDATES) + 4))
     tuned = []
     for name, (B, H, N, d), dtype, causal, window in WORKLOADS:
         q, k, v = (t.to(dev) for t in attention_inputs(B, H, N, d, dtype, seed=0))
         fa355.fa_tune_reset()
-        heur, _ = fa355.fa_fwd_auto_block_q(B, H, N, d, causal=causal, window=window, dtype=q.dtype)
+        heur, _ = fa355.fa_fwd_auto_tile(B, H, N, d, causal=causal, window=window, dtype=q.dtype)
         best, times, _, _ = fa355.fa_fwd_tune(q, k, v, causal=causal, window=window, reps=args.reps)
         flops = 4.0 * d * B * H * visible_pairs(N, causal, window)
         tf = flops / (times[best] * 1e-3) / 1e12
-        cells = " | ".join(f"{times[b]:.4f}" for b in fa355.TUNE_CANDIDATES)
-        print(f"| {name} | {cells} | {best} | {tf:.1f} | {heur} | {times[heur]:.4f} |", flush=True)
+        cells = " | ".join(f"{times[t]:.4f}" if times[t] >= 0 else "-" for t in fa355.TUNE_CANDIDATES)
+        print(f"| {name} | {cells} | {best[0]}x{best[1]} | {tf:.1f} | {heur[0]}x{heur[1]} | {times[heur]:.4f} |",
+              flush=True)
         tuned += fa355.fa_tune_export()
         del q, k, v
 
