@@ -9,304 +9,245 @@
 //   P = exp(S - L),  dV += P^T dO,  dP = dO V^T,  dS = P * (dP - D),
 //   dK += scale * dS^T Q,  dQ += scale * dS K.
 //
-// Mapping onto CDNA4 (v_mfma_f32_32x32x16_bf16 / _f16, fp32 accumulation), three
+// Mapping onto CDNA4 (v_mfma_f32_32x32x16_bf16 / _f16, fp32 accumulation), two
 // kernels on one stream:
-//  * bwd_pre: one 16-byte slice per lane, D reduced with DPP; it also stores
-//    L in log2 units so the other kernels need one exp2 per score.
-//  * bwd_main: dK and dV, in the page's loop order (key/value tiles outer):
-//    a workgroup of 8 waves owns a 128-key tile and walks the query tiles.
-//  * bwd_dq: dQ, with the loops the other way round (a workgroup owns 128
-//    query rows and walks the key tiles, as the forward does), recomputing
-//    S, P, dP and dS; no atomics, so dQ is deterministic.
+//  * bwd_dq (or bwd_dq_pp for grids that fill the chip): dQ, with the loops
+//    the other way round (a workgroup owns 128 or 256 query rows and walks
+//    the key tiles, as the forward does), recomputing S, P, dP and dS; no
+//    atomics, so dQ is deterministic.  Owning every query row once, it also
+//    forms the page's first step, D = rowsum(dO * O), and L in log2 units
+//    for the next kernel.
+//  * bwd_kv4: dK and dV, in the page's loop order (key/value tiles outer):
+//    a workgroup of 4 waves owns a 128-key tile and walks the query tiles.
 #include "fa_common.h"
 #include "fa_launch.h"
 
 namespace fa {
 namespace {
 
-constexpr int kThreads = 512;     // main kernel: 8 waves
-constexpr int kPreThreads = 256;  // preprocessing kernel
-constexpr int kBKV = 128;  // keys per workgroup
-constexpr int kBQ = 64;    // queries per step
+constexpr int kBKV = 128;  // keys per dK / dV workgroup
 
-constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedDSRead = 0x100;
+// dK / dV kernel with four waves and two workgroups per CU.  A workgroup owns
+// 128 keys, 32 per wave, and walks the query tiles that see them 32 queries
+// at a time.  Each wave forms S = Q K^T and dP = dO V^T for its own 32 keys
+// and all 32 queries of the step, so P and dS never leave the wave: in the
+// 32x32 accumulator layout a lane holds one key and 16 queries, which is
+// already the A operand (keys x queries) of dV += P^T dO and dK += dS^T Q
+// once the queries run in the accumulator's row order -- the order in which
+// the transpose reads deliver the rows of the dO and Q tiles.  Without the
+// exchange of P and dS there is one workgroup barrier per step (the query
+// tile's stage recycling), and the two workgroups that share a CU (one wave
+// of each per SIMD) run independently, so one's vector work, barriers and
+// start-up overlap the other's matrix work.
+//  * K: a 128-row tile in LDS (B operands of S, 16-byte reads), loaded once;
+//    V: this wave's 32 rows in registers (B operands of dP);
+//  * Q, dO, L2 and D of the next query tile stream into LDS by direct loads
+//    while the current one is processed (two stages);
+//  * a wave skips the steps in which every key it owns is hidden from every
+//    query of the tile (the causal diagonal, a window's far edge).
+constexpr int kKv4Threads = 256;
+constexpr int kKv4BQ = 32;  // queries per step
 
-// Scheduling pattern for a block of M MFMAs fed by R LDS reads, with V
-// vector-ALU instructions of independent work placed after each MFMA: the
-// first A reads go ahead, the rest are spread evenly over the MFMAs.  Keeps
-// the compiler from hoisting every operand read (which runs out of registers
-// at one wave per SIMD) while the reads still run ahead of their MFMAs.
-template <int I, int M, int R, int A, int V, int SYNC>
-__device__ __forceinline__ void interleave_step() {
-  if constexpr (I < M) {
-    constexpr int n = (I + 1) * (R - A) / M - I * (R - A) / M;
-    __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, SYNC);
-    if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, n, SYNC);
-    if constexpr (V > 0) __builtin_amdgcn_sched_group_barrier(kSchedVALU, V, SYNC);
-    interleave_step<I + 1, M, R, A, V, SYNC>();
-  }
-}
-template <int M, int R, int A, int V, int SYNC>
-__device__ __forceinline__ void interleave() {
-  __builtin_amdgcn_sched_group_barrier(kSchedDSRead, A, SYNC);
-  interleave_step<0, M, R, A, V, SYNC>();
-}
-
-template <typename T, int D>
-__global__ __launch_bounds__(kPreThreads) void bwd_pre_kernel(
-    const T* __restrict__ o, const T* __restrict__ dO, const float* __restrict__ lse,
-    float* __restrict__ Dv, float* __restrict__ L2, long long rows) {
-  constexpr int LPR = D / 8;
-  constexpr int RPB = kPreThreads / LPR;
-  const int t = threadIdx.x;
-  const long long row = (long long)blockIdx.x * RPB + t / LPR;
-  const int e = t % LPR;
-  float p = 0.f;
-  if (row < rows) {
-    const size_t off = (size_t)row * D + e * 8;
-    const uint4 a = *(const uint4*)(o + off);
-    const uint4 b = *(const uint4*)(dO + off);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p = __builtin_fmaf(lo16<T>(word(a, i)), lo16<T>(word(b, i)), p);
-      p = __builtin_fmaf(hi16<T>(word(a, i)), hi16<T>(word(b, i)), p);
-    }
-  }
-  p = group_sum<LPR>(p);
-  if (row < rows && e == 0) {
-    Dv[row] = p;
-    const float L = lse[row];
-    L2[row] = L == kNegInf ? __builtin_inff() : L * kLog2e;  // row without keys: P = 0
-  }
-}
-
-// Main backward kernel: dK and dV.  A workgroup of 8 waves (two per SIMD)
-// owns 128 keys and walks the 64-row query tiles that see them.  Wave
-// w = (kb, qb), kb = w % 4 and qb = w / 4:
-//  * scores: S = Q K^T and dP = dO V^T for its 32 keys (block kb) and the
-//    tile's query rows 32 qb .. 32 qb + 31; Q and dO come from LDS as MFMA A
-//    operands, the wave's K and V rows stay in registers as B operands;
-//  * P = exp2(S c - L2) and dS = P (dP - D) on the vector ALUs, written to LDS
-//    (keys as rows) in the order of the MFMA A operand, so every wave reads
-//    P^T and dS^T of a key block for all 64 queries with 16-byte reads;
-//  * gradients: dV += P^T dO and dK += dS^T Q for the wave's key block and
-//    half of the columns, over all 64 queries (B operands by transpose reads
-//    of the row-major dO and Q tiles).
-// Q, dO, L2 and D of the next query tile stream into LDS by direct loads
-// while the current one is processed (two stages); K and V are read once.
-// dQ is formed by its own kernel (below): accumulated here it would take one
-// float atomic per query row, column and key tile, and those atomics cost
-// about as much as all the rest of this kernel.
 template <int D>
-struct BwdTile {
-  static constexpr int kQPitch = D == 128 ? 304 : 144;  // bytes per Q / dO row in LDS
-  static constexpr int kSPitch = 144;                    // bytes per P^T / dS^T row (64 queries)
-  static constexpr int kQBytes = kBQ * kQPitch;
-  static constexpr int kSBytes = kBKV * kSPitch;
-  static constexpr int kQBlocks = kQBytes / 1024;  // 1 KB per wave-wide direct load
-  static_assert(kQBytes % 1024 == 0, "tiles must be whole 1 KB blocks");
+struct Kv4Tile {
+  static constexpr int kKPitch = 2 * D + 16;                 // K rows: 16-byte reads
+  static constexpr int kQPitch = D == 128 ? 304 : 144;       // Q / dO rows: 16-byte and transpose reads
+  static constexpr int kKBytes = kBKV * kKPitch;
+  static constexpr int kQBytes = (kKv4BQ * kQPitch + 1023) / 1024 * 1024;
+  static constexpr int kKBlocks = kKBytes / 1024;
+  static constexpr int kQBlocks = kQBytes / 1024;
+  static_assert(kKBytes % 1024 == 0, "K tile must be whole 1 KB blocks");
 };
 
+// block_src for a tile of `rows` rows: lanes past the last row or on row
+// padding read zero.
+template <int D>
+__device__ __forceinline__ uint32_t block_src_rows(int blk, int lane, int pitch, int rows) {
+  const int pos = blk * 1024 + lane * 16;
+  const int row = pos / pitch, col = pos - row * pitch;
+  return row < rows && col < D * 2 ? (uint32_t)(row * D * 2 + col) : 0x80000000u;
+}
+
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void bwd_main_kernel(const T* __restrict__ q, const T* __restrict__ k,
-                     const T* __restrict__ v, const T* __restrict__ dO,
-                     const float* __restrict__ Dv, const float* __restrict__ L2,
-                     float* __restrict__ dk, float* __restrict__ dv,
-                     int BH, int N, int nkt, float scale, float scale_log2, int causal, int window) {
-  using TL = BwdTile<D>;
-  constexpr int NW = kThreads / 64;  // 8
-  constexpr int KS = D / 16;         // 16-wide steps over the head dimension
-  constexpr int CB = D / 32;         // 32-column blocks of the head dimension
-  constexpr int NCB = CB / 2;        // column blocks of dK / dV per wave
+__global__ __launch_bounds__(kKv4Threads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_kv4_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                    const T* __restrict__ v, const T* __restrict__ dO,
+                    const float* __restrict__ Dv, const float* __restrict__ L2,
+                    float* __restrict__ dk, float* __restrict__ dv,
+                    int BH, int N, int nkt, float scale, float scale_log2, int causal, int window) {
+  using TL = Kv4Tile<D>;
+  constexpr int NW = kKv4Threads / 64;  // 4
+  constexpr int KS = D / 16;            // 16-wide steps over the head dimension
+  constexpr int CB = D / 32;            // 32-column blocks of dK / dV
+  constexpr int KPER = (TL::kKBlocks + NW - 1) / NW;
   constexpr int QPER = (TL::kQBlocks + NW - 1) / NW;
-  constexpr int QP = TL::kQPitch, SP = TL::kSPitch;
-  // One LDS object per stage and matrix (the compiler then knows that direct
-  // loads into one stage do not alias reads of the other).
+  constexpr int KP = TL::kKPitch, QP = TL::kQPitch;
+  __shared__ __attribute__((aligned(1024))) char Kt[TL::kKBytes];
   __shared__ __attribute__((aligned(1024))) char Q0[TL::kQBytes];
   __shared__ __attribute__((aligned(1024))) char Q1[TL::kQBytes];
   __shared__ __attribute__((aligned(1024))) char O0[TL::kQBytes];
   __shared__ __attribute__((aligned(1024))) char O1[TL::kQBytes];
-  __shared__ __attribute__((aligned(1024))) char Pt[TL::kSBytes];
-  __shared__ __attribute__((aligned(1024))) char dSt[TL::kSBytes];
-  __shared__ __attribute__((aligned(256))) float LD0[2 * kBQ];  // L2 then D of a query tile
-  __shared__ __attribute__((aligned(256))) float LD1[2 * kBQ];
+  __shared__ __attribute__((aligned(256))) float LD0[128];  // L2 in [0, 64), D in [64, 128)
+  __shared__ __attribute__((aligned(256))) float LD1[128];
 
   const int t = threadIdx.x;
   const int lane = t & 63, h = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform: keeps per-wave branches scalar
   __builtin_assume(w >= 0 && w < NW);
-  const int kb = w & 3, qb = w >> 2;
 
   int bh, kt;
   tile_order(blockIdx.x, BH, nkt, causal && window < 0, bh, kt);  // heaviest key tile (kt = 0) first
   const int k0 = kt * kBKV;
   const size_t base = (size_t)bh * (size_t)N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2u;
+  const int wk0 = k0 + 32 * w;           // this wave's keys: wk0 .. wk0 + 31
+  const int wk1 = min(wk0 + 31, N - 1);  // the last of them that exists
+  const int my_key = wk0 + l32;
 
-  // This wave's 32 key and value rows as B operands of S and dP:
-  // K[key][16 s + 8 h + 0..7] and V[key][16 s + 8 h + 0..7].
-  const int my_key = k0 + 32 * kb + l32;
-  vec8<T> kf[KS], vf[KS];
+  // K tile (rows past N read as zero) and this wave's V rows.
   {
-    const rsrc_t k_src = make_rsrc(k + base, head_bytes);
-    const rsrc_t v_src = make_rsrc(v + base, head_bytes);
+    const rsrc_t k_src = make_rsrc(k + base + (size_t)k0 * D, (uint32_t)max(0, N - k0) * D * 2u);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      kf[s] = as_vec8<T>(load16(k_src, (uint32_t)(my_key * D + 16 * s + 8 * h) * 2u));
-      vf[s] = as_vec8<T>(load16(v_src, (uint32_t)(my_key * D + 16 * s + 8 * h) * 2u));
+    for (int i = 0; i < KPER; ++i) {
+      const int blk = w + i * NW;
+      if (blk < TL::kKBlocks) load_lds16(k_src, Kt + blk * 1024, block_src_rows<D>(blk, lane, KP, kBKV));
     }
+  }
+  vec8<T> vf[KS];
+  {
+    const rsrc_t v_src = make_rsrc(v + base, (uint32_t)N * D * 2u);
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      vf[s] = as_vec8<T>(load16(v_src, (uint32_t)(my_key * D + 16 * s + 8 * h) * 2u));
   }
 
   // Query tiles that see at least one of this workgroup's keys.
   const int k_hi = k0 + kBKV - 1;
   const int qmin = causal ? k0 : 0;
   const int qmax = window >= 0 ? min(N - 1, k_hi + window) : N - 1;
-  const int qt0 = qmin / kBQ, qt1 = qmax / kBQ + 1;
+  const int qt0 = qmin / kKv4BQ, qt1 = qmax / kKv4BQ + 1;
 
-  // Direct-load source offsets of this lane (padding lanes read nothing).
   uint32_t qpre[QPER];
 #pragma unroll
-  for (int i = 0; i < QPER; ++i) qpre[i] = block_src<D>(w + i * NW, lane, QP);
-
+  for (int i = 0; i < QPER; ++i) qpre[i] = block_src_rows<D>(w + i * NW, lane, QP, kKv4BQ);
   auto stage_q = [&] __device__ (auto st) -> char* { return decltype(st)::value == 0 ? Q0 : Q1; };
   auto stage_o = [&] __device__ (auto st) -> char* { return decltype(st)::value == 0 ? O0 : O1; };
   auto stage_ld = [&] __device__ (auto st) -> float* { return decltype(st)::value == 0 ? LD0 : LD1; };
   const float* Lrow = L2 + (size_t)bh * N;
   const float* Drow = Dv + (size_t)bh * N;
-  // This wave's share of the direct loads of query tile qt into stage st:
-  // Q and dO blocks, and (waves 0 and 1) the tile's 64 values of L2 / D.
+  // This wave's share of the direct loads of query tile qt into stage st.
   auto load_qtile = [&] __device__ (int qt, auto st) {
-    const int q0 = qt * kBQ;
+    const int q0 = qt * kKv4BQ;
     const uint32_t bytes = (uint32_t)max(0, N - q0) * D * 2u;
     const rsrc_t qs = make_rsrc(q + base + (size_t)q0 * D, bytes);
     const rsrc_t os = make_rsrc(dO + base + (size_t)q0 * D, bytes);
-    char* qd = stage_q(st);
-    char* od = stage_o(st);
 #pragma unroll
     for (int i = 0; i < QPER; ++i) {
       const int blk = w + i * NW;
       if (blk < TL::kQBlocks) {
-        load_lds16(qs, qd + blk * 1024, qpre[i]);
-        load_lds16(os, od + blk * 1024, qpre[i]);
+        load_lds16(qs, stage_q(st) + blk * 1024, qpre[i]);
+        load_lds16(os, stage_o(st) + blk * 1024, qpre[i]);
       }
     }
     if (w < 2) {
       const rsrc_t ls = make_rsrc((w == 0 ? Lrow : Drow) + q0, (uint32_t)max(0, N - q0) * 4u);
-      load_lds4(ls, stage_ld(st) + w * kBQ, (uint32_t)lane * 4u);
+      load_lds4(ls, stage_ld(st) + w * 64, (uint32_t)lane * 4u);
     }
   };
 
   using std::integral_constant;
-  // Prologue: the first query tile resident.
   if (qt0 < qt1) load_qtile(qt0, integral_constant<int, 0>{});
-  // The K and V rows above must be in flight together with this tile's
-  // loads: left to itself the compiler issued them only after the wait
-  // below, so the two round trips to memory ran one after the other.  An
-  // empty asm that reads them here keeps them ahead of the wait.
+  // The V rows above must be in flight together with the tile's loads:
+  // left to itself the compiler issued them only after the wait below, so
+  // the two round trips to memory ran one after the other.  An empty asm
+  // that reads them here keeps them ahead of the wait.
 #if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
-  for (int s = 0; s < KS; ++s) asm volatile("" : "+v"(kf[s]), "+v"(vf[s]));
+  for (int s = 0; s < KS; ++s) asm volatile("" : "+v"(vf[s]));
 #endif
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  f32x16 dk_acc[NCB], dv_acc[NCB];
+  f32x16 dk_acc[CB], dv_acc[CB];
 #pragma unroll
-  for (int c = 0; c < NCB; ++c) {
+  for (int c = 0; c < CB; ++c) {
     dk_acc[c] = f32x16{};
     dv_acc[c] = f32x16{};
   }
-  const int q_rd = (32 * qb + l32) * QP + 16 * h;       // A operands of S and dP
-  const int s_wr = (32 * kb + l32) * SP + (32 * qb + 8 * h) * 2;  // this lane's P / dS pieces
-  const int s_rd = (32 * kb + l32) * SP + 16 * h;       // A operands of dV / dK
-  const int tr_q = tr_addr<QP>(lane);                   // B operands of dV / dK
+  const int q_rd = l32 * QP + 16 * h;              // A operands of S and dP (Q, dO rows)
+  const int k_rd = (32 * w + l32) * KP + 16 * h;   // B operands of S (K rows)
+  const int tr_q = tr_addr<QP>(lane);              // B operands of dV / dK
 
-  // One query tile in stage ST.
   auto tile = [&] __device__ (auto stage, int qt) {
     constexpr int ST = decltype(stage)::value;
     const char* Qs = stage_q(stage);
     const char* Os = stage_o(stage);
     const float* LD = stage_ld(stage);
-    const int q0 = qt * kBQ;
+    const int q0 = qt * kKv4BQ;
     if (qt + 1 < qt1) load_qtile(qt + 1, integral_constant<int, ST ^ 1>{});
-    const bool need_mask = (causal && q0 < k_hi) || (window >= 0 && q0 + kBQ - 1 - k0 > window) ||
-                           (k_hi >= N) || (q0 + kBQ > N);
-
-    // 1) S = Q K^T, then dP = dO V^T while P = exp2(S * scale * log2e - L2)
-    //    (masked) is formed on the vector ALUs.
-    f32x16 sacc = f32x16{}, dpacc = f32x16{};
+    const bool act = wk0 <= wk1 && !(causal && wk0 > q0 + kKv4BQ - 1) && !(window >= 0 && wk1 < q0 - window);
+    if (act) {
+      const bool need_mask = (causal && wk0 + 31 > q0) || (window >= 0 && q0 + kKv4BQ - 1 - wk0 > window) ||
+                             (wk0 + 31 >= N) || (q0 + kKv4BQ > N);
+      // S = Q K^T and dP = dO V^T, then P = exp2(S c - L2) and dS = P (dP - D)
+      // on the vector ALUs, then dV += P^T dO and dK += dS^T Q, 16 queries
+      // per MFMA step.  (The compiler's own instruction order measured
+      // fastest here: with every register of the lane in use, explicit
+      // interleaving patterns only delayed the operand reads.)
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-      sacc = mfma32(*(const vec8<T>*)(Qs + q_rd + 32 * s), kf[s], sacc);
-    interleave<KS, KS, 4, 0, 1>();
-    __builtin_amdgcn_sched_barrier(0);
+      for (int s = 0; s < KS; ++s)
+        sacc = mfma32(*(const vec8<T>*)(Qs + q_rd + 32 * s), *(const vec8<T>*)(Kt + k_rd + 32 * s), sacc);
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-      dpacc = mfma32(*(const vec8<T>*)(Os + q_rd + 32 * s), vf[s], dpacc);
-    float pv[16];
+      for (int s = 0; s < KS; ++s)
+        dpacc = mfma32(*(const vec8<T>*)(Os + q_rd + 32 * s), vf[s], dpacc);
+      float pv[16];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const float4 L4 = *(const float4*)(LD + 32 * qb + 8 * g + 4 * h);
-      pv[4 * g + 0] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * g + 0], scale_log2, -L4.x));
-      pv[4 * g + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * g + 1], scale_log2, -L4.y));
-      pv[4 * g + 2] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * g + 2], scale_log2, -L4.z));
-      pv[4 * g + 3] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * g + 3], scale_log2, -L4.w));
-    }
-    // Hidden pairs get P = 0 (one branch around the whole tile: inside the
-    // element loop the test would be evaluated on every tile).
-    if (need_mask) {
+      for (int g = 0; g < 4; ++g) {
+        const float4 L4 = *(const float4*)(LD + 8 * g + 4 * h);
+        pv[4 * g + 0] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * g + 0], scale_log2, -L4.x));
+        pv[4 * g + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * g + 1], scale_log2, -L4.y));
+        pv[4 * g + 2] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * g + 2], scale_log2, -L4.z));
+        pv[4 * g + 3] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * g + 3], scale_log2, -L4.w));
+      }
+      // Hidden pairs get P = 0 (one branch around the whole step).
+      if (need_mask) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qrow = q0 + 32 * qb + c_row(r, h);
-        const int lo = window >= 0 ? qrow - window : 0;
-        const int hi = min(causal ? qrow : N - 1, N - 1);
-        const bool vis = (qrow < N) & ((uint32_t)(my_key - lo) <= (uint32_t)(hi - lo));
-        pv[r] = vis ? pv[r] : 0.f;
+        for (int r = 0; r < 16; ++r) {
+          const int qrow = q0 + c_row(r, h);
+          const int lo = window >= 0 ? qrow - window : 0;
+          const int hi = min(causal ? qrow : N - 1, N - 1);
+          const bool vis = (qrow < N) & ((uint32_t)(my_key - lo) <= (uint32_t)(hi - lo));
+          pv[r] = vis ? pv[r] : 0.f;
+        }
+      }
+      uint32_t ppk[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ppk[j] = pack2<T>(pv[2 * j], pv[2 * j + 1]);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const vec8<T> pa = as_vec8<T>(uint4{ppk[4 * s], ppk[4 * s + 1], ppk[4 * s + 2], ppk[4 * s + 3]});
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+          dv_acc[c] = mfma32(pa, read_tr8<QP, T>(Os + tr_q + 16 * s * QP + 64 * c), dv_acc[c]);
+      }
+      uint32_t dspk[8];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 D4 = *(const float4*)(LD + 64 + 8 * g + 4 * h);
+        dspk[2 * g] = pack2<T>(pv[4 * g] * (dpacc[4 * g] - D4.x), pv[4 * g + 1] * (dpacc[4 * g + 1] - D4.y));
+        dspk[2 * g + 1] = pack2<T>(pv[4 * g + 2] * (dpacc[4 * g + 2] - D4.z),
+                                    pv[4 * g + 3] * (dpacc[4 * g + 3] - D4.w));
+      }
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const vec8<T> da = as_vec8<T>(uint4{dspk[4 * s], dspk[4 * s + 1], dspk[4 * s + 2], dspk[4 * s + 3]});
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+          dk_acc[c] = mfma32(da, read_tr8<QP, T>(Qs + tr_q + 16 * s * QP + 64 * c), dk_acc[c]);
       }
     }
-    uint32_t ppk[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) ppk[j] = pack2<T>(pv[2 * j], pv[2 * j + 1]);
-    interleave<KS, KS, 4, 6, 2>();
-    __builtin_amdgcn_sched_barrier(0);
-    uint32_t dspk[8];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const float4 D4 = *(const float4*)(LD + kBQ + 32 * qb + 8 * g + 4 * h);
-      dspk[2 * g] = pack2<T>(pv[4 * g] * (dpacc[4 * g] - D4.x), pv[4 * g + 1] * (dpacc[4 * g + 1] - D4.y));
-      dspk[2 * g + 1] = pack2<T>(pv[4 * g + 2] * (dpacc[4 * g + 2] - D4.z),
-                                  pv[4 * g + 3] * (dpacc[4 * g + 3] - D4.w));
-    }
-    // P^T and dS^T rows: this lane's key, its 16 queries in A-operand order.
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      *(uint4*)(Pt + s_wr + 32 * j) = uint4{ppk[4 * j], ppk[4 * j + 1], ppk[4 * j + 2], ppk[4 * j + 3]};
-      *(uint4*)(dSt + s_wr + 32 * j) = uint4{dspk[4 * j], dspk[4 * j + 1], dspk[4 * j + 2], dspk[4 * j + 3]};
-    }
-    // LDS writes done, then the barrier; direct loads stay in flight.
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-
-    // 2) dV += P^T dO and dK += dS^T Q over the tile's 64 queries (16 per
-    //    step) for this wave's column blocks.
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const vec8<T> pa = *(const vec8<T>*)(Pt + s_rd + 32 * s);
-      const vec8<T> da = *(const vec8<T>*)(dSt + s_rd + 32 * s);
-#pragma unroll
-      for (int c = 0; c < NCB; ++c) {
-        const int off = tr_q + 16 * s * QP + 64 * (NCB * qb + c);
-        dv_acc[c] = mfma32(pa, read_tr8<QP, T>(Os + off), dv_acc[c]);
-        dk_acc[c] = mfma32(da, read_tr8<QP, T>(Qs + off), dk_acc[c]);
-      }
-    }
-    interleave<8 * NCB, 8 + 16 * NCB, 4, 0, 3>();
-    __builtin_amdgcn_sched_barrier(0);
-
     // The next tile's direct loads have landed; after the barrier no wave
-    // reads this stage, P^T or dS^T any more.
+    // reads this stage any more.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
@@ -317,16 +258,15 @@ void bwd_main_kernel(const T* __restrict__ q, const T* __restrict__ k,
     tile(integral_constant<int, 1>{}, qt + 1);
   }
 
-  // dK = scale * dS^T Q, dV = P^T dO for key block kb and this wave's column
-  // blocks; rows past N fall outside the buffers and are dropped.
+  // dK = scale * dS^T Q, dV = P^T dO for this wave's keys; rows past N fall
+  // outside the buffers and are dropped.
   const rsrc_t dk_dst = make_rsrc(dk + base, (uint32_t)N * D * 4u);
   const rsrc_t dv_dst = make_rsrc(dv + base, (uint32_t)N * D * 4u);
 #pragma unroll
-  for (int c = 0; c < NCB; ++c) {
+  for (int c = 0; c < CB; ++c) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const uint32_t off =
-          ((uint32_t)(k0 + 32 * kb + c_row(r, h)) * D + 32 * (NCB * qb + c) + l32) * 4u;
+      const uint32_t off = ((uint32_t)(wk0 + c_row(r, h)) * D + 32 * c + l32) * 4u;
       store_f32(dk_dst, off, scale * dk_acc[c][r]);
       store_f32(dv_dst, off, dv_acc[c][r]);
     }
@@ -368,6 +308,36 @@ __device__ __forceinline__ void store_dq_rows(const f32x16 (&dqa)[CB], float sca
   }
 }
 
+// Per-row constants of the backward for this lane's query row qi, formed by
+// the dQ kernels (which own every query row once and hold its dO already):
+// D = rowsum(dO * O) (the two lanes of a row each sum half of the columns)
+// and L2 = L * log2(e) (+inf for a row without visible keys, so that every P
+// of it is 0).  Stored for the dK / dV kernel, which runs after them.
+template <typename T, int KS>
+__device__ __forceinline__ void row_constants(const vec8<T> (&of)[KS], rsrc_t o_src, uint32_t row_off,
+                                              const float* __restrict__ lse, float* __restrict__ Dv,
+                                              float* __restrict__ L2, size_t row, bool row_ok, int h,
+                                              float& Di, float& Li) {
+  float p = 0.f;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const uint4 a = load16(o_src, row_off + 32u * s);
+    const uint4 b = __builtin_bit_cast(uint4, of[s]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p = __builtin_fmaf(lo16<T>(word(a, i)), lo16<T>(word(b, i)), p);
+      p = __builtin_fmaf(hi16<T>(word(a, i)), hi16<T>(word(b, i)), p);
+    }
+  }
+  Di = pair_sum(p);
+  const float L = row_ok ? lse[row] : 0.f;
+  Li = L == kNegInf ? __builtin_inff() : L * kLog2e;
+  if (row_ok && h == 0) {
+    Dv[row] = Di;
+    L2[row] = Li;
+  }
+}
+
 // dQ kernel: dQ = scale * dS K without atomics.  A workgroup of 4 waves owns
 // 128 query rows (32 per wave, one per lane pair as in the forward kernels)
 // and walks the 64-key tiles they see, recomputing per tile
@@ -403,7 +373,8 @@ template <typename T, int D>
 __global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : 2, 2)))
 void bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k,
                    const T* __restrict__ v, const T* __restrict__ dO,
-                   const float* __restrict__ Dv, const float* __restrict__ L2,
+                   const T* __restrict__ o, const float* __restrict__ lse,
+                   float* __restrict__ Dv, float* __restrict__ L2,
                    float* __restrict__ dq, int BH, int N, int nqt, float scale, float scale_log2,
                    int causal, int window) {
   using TL = DqTile<D>;
@@ -445,8 +416,9 @@ void bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k,
     }
   }
   const bool row_ok = qi < N;
-  const float Li = row_ok ? L2[(size_t)bh * N + qi] : 0.f;
-  const float Di = row_ok ? Dv[(size_t)bh * N + qi] : 0.f;
+  float Li, Di;
+  row_constants<T, KS>(of, make_rsrc(o + base, (uint32_t)N * D * 2u), (uint32_t)(qi * D + 8 * h) * 2u, lse, Dv,
+                       L2, (size_t)bh * N + qi, row_ok, h, Di, Li);
 
   // Key tiles holding at least one key visible to this query tile, and the
   // keys this lane's row sees.
@@ -604,7 +576,8 @@ template <typename T, int D>
 __global__ __launch_bounds__(kDqPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_pp_kernel(const T* __restrict__ q, const T* __restrict__ k,
                       const T* __restrict__ v, const T* __restrict__ dO,
-                      const float* __restrict__ Dv, const float* __restrict__ L2,
+                      const T* __restrict__ o, const float* __restrict__ lse,
+                      float* __restrict__ Dv, float* __restrict__ L2,
                       float* __restrict__ dq, int BH, int N, int nqt, float scale, float scale_log2,
                       int causal, int window) {
   using TL = DqPPTile<D>;
@@ -653,8 +626,9 @@ void bwd_dq_pp_kernel(const T* __restrict__ q, const T* __restrict__ k,
     }
   }
   const bool row_ok = qi < N;
-  const float Li = row_ok ? L2[(size_t)bh * N + qi] : 0.f;
-  const float Di = row_ok ? Dv[(size_t)bh * N + qi] : 0.f;
+  float Li, Di;
+  row_constants<T, KS>(of, make_rsrc(o + base, (uint32_t)N * D * 2u), (uint32_t)(qi * D + 8 * h) * 2u, lse, Dv,
+                       L2, (size_t)bh * N + qi, row_ok, h, Di, Li);
 
   // Key tiles holding at least one key visible to this query tile, the keys
   // this lane's row sees, and the tiles that hold any key visible to this
@@ -827,32 +801,28 @@ hipError_t launch_t(const void* q, const void* k, const void* v, const void* o, 
   const long long rows = (long long)B * H * N;
   float* Dv = (float*)ws;
   float* L2 = Dv + rows;
-  constexpr int RPB = kPreThreads / (D / 8);
-  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(kPreThreads),
-                     0, stream, (const T*)o, (const T*)dO, lse, Dv, L2, rows);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  const int nkt = (N + kBKV - 1) / kBKV;
-  const long long grid = (long long)nkt * B * H;
-  hipLaunchKernelGGL((bwd_main_kernel<T, D>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                     (const T*)q, (const T*)k, (const T*)v, (const T*)dO, Dv, L2, dk, dv,
-                     B * H, N, nkt, scale, scale * kLog2e, mask.causal, mask.window);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  // dQ: the ping-pong kernel (256 query rows per workgroup) or the 4-wave
-  // kernel (128 rows).
+  // dQ first: it also stores D and L2 of every query row, which the dK / dV
+  // kernel reads.  dQ: the ping-pong kernel (256 query rows per workgroup) or
+  // the 4-wave kernel (128 rows).
   if (dq_rows == 256) {
     const int nqt = (N + 255) / 256;
     hipLaunchKernelGGL((bwd_dq_pp_kernel<T, D>), dim3((unsigned)((long long)nqt * B * H)), dim3(kDqPPThreads),
-                       0, stream, (const T*)q, (const T*)k, (const T*)v, (const T*)dO, Dv,
-                       L2, dq, B * H, N, nqt, scale, scale * kLog2e, mask.causal, mask.window);
+                       0, stream, (const T*)q, (const T*)k, (const T*)v, (const T*)dO, (const T*)o, lse,
+                       Dv, L2, dq, B * H, N, nqt, scale, scale * kLog2e, mask.causal, mask.window);
   } else {
     constexpr int BQ = kDqThreads / 2;  // 32 query rows per wave
     const int nqt = (N + BQ - 1) / BQ;
     hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3((unsigned)((long long)nqt * B * H)), dim3(kDqThreads), 0,
-                       stream, (const T*)q, (const T*)k, (const T*)v, (const T*)dO, Dv, L2,
-                       dq, B * H, N, nqt, scale, scale * kLog2e, mask.causal, mask.window);
+                       stream, (const T*)q, (const T*)k, (const T*)v, (const T*)dO, (const T*)o, lse,
+                       Dv, L2, dq, B * H, N, nqt, scale, scale * kLog2e, mask.causal, mask.window);
   }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int nkt = (N + kBKV - 1) / kBKV;
+  const long long grid = (long long)nkt * B * H;
+  hipLaunchKernelGGL((bwd_kv4_kernel<T, D>), dim3((unsigned)grid), dim3(kKv4Threads), 0, stream,
+                     (const T*)q, (const T*)k, (const T*)v, (const T*)dO, Dv, L2, dk, dv,
+                     B * H, N, nkt, scale, scale * kLog2e, mask.causal, mask.window);
   return hipGetLastError();
 }
 
