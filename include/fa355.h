@@ -363,7 +363,8 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
  *
  * dQ is formed by its own kernel, in the forward's loop order (a workgroup
  * owns query rows and walks the key tiles); it comes with 256 query rows per
- * workgroup (8 waves, two groups one phase apart) or 128 (4 waves).  Which
+ * workgroup (8 waves, two groups one phase apart, one workgroup per CU) or
+ * 128 (4 waves, two workgroups per CU).  Which
  * is faster depends on how well each grid fills the chip, so the choice is
  * measured: the "profiling-driven auto-tuning" upgrade of "Build a
  * FlashAttention-2 Inference Kernel from Scratch in Pure Python", Extending
@@ -372,7 +373,8 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
  * non-NULL) get the mean ms per call with 128 / 256 rows and *best_dq_rows
  * (if non-NULL) the faster, remembered under (dtype, d, causal, window,
  * B * H, N).  On return dq, dk and dv hold the chosen kernel's result
- * (both give identical dk and dv; dq agrees to rounding order).
+ * (both give identical dk and dv, and form dq from the same terms in
+ * the same order).
  *
  * Arguments as fa_bwd, plus reps in [1, 1000].  Like fa_fwd_tune it
  * SYNCHRONISES `stream` and creates two HIP events.

@@ -11,10 +11,11 @@
 //
 // Mapping onto CDNA4 (v_mfma_f32_32x32x16_bf16 / _f16, fp32 accumulation), two
 // kernels on one stream:
-//  * bwd_dq (or bwd_dq_pp for grids that fill the chip): dQ, with the loops
-//    the other way round (a workgroup owns 128 or 256 query rows and walks
-//    the key tiles, as the forward does), recomputing S, P, dP and dS; no
-//    atomics, so dQ is deterministic.  Owning every query row once, it also
+//  * bwd_dq4 (4 waves, two workgroups per CU) or bwd_dq_pp (8 waves in two
+//    groups one phase apart, for grids that fill the chip): dQ, with the
+//    loops the other way round (a workgroup owns 128 or 256 query rows and
+//    walks the key tiles, as the forward does), recomputing S, P, dP and dS;
+//    no atomics, so dQ is deterministic.  Owning every query row once, it also
 //    forms the page's first step, D = rowsum(dO * O), and L in log2 units
 //    for the next kernel.
 //  * bwd_kv4: dK and dV, in the page's loop order (key/value tiles outer):
@@ -26,6 +27,7 @@ namespace fa {
 namespace {
 
 constexpr int kBKV = 128;  // keys per dK / dV workgroup
+
 
 // dK / dV kernel with four waves and two workgroups per CU.  A workgroup owns
 // 128 keys, 32 per wave, and walks the query tiles that see them 32 queries
@@ -338,57 +340,56 @@ __device__ __forceinline__ void row_constants(const vec8<T> (&of)[KS], rsrc_t o_
   }
 }
 
-// dQ kernel: dQ = scale * dS K without atomics.  A workgroup of 4 waves owns
-// 128 query rows (32 per wave, one per lane pair as in the forward kernels)
-// and walks the 64-key tiles they see, recomputing per tile
-//   S^T = K Q^T,  dP^T = V dO^T   (Q and dO rows in registers as B operands,
-//                                  K and V rows from LDS as A operands),
-//   P^T = exp2(S^T * scale * log2e - L2),  dS^T = P^T (dP^T - D)
-//                                 (L2 and D: one value per lane),
-//   dQ^T += K^T dS^T              (K^T by transpose reads of the K tile, dS^T
-//                                  packed to T straight from the
-//                                  accumulators, as P in the forward).
-// K and V tiles are double-buffered in LDS and filled by direct loads.
-constexpr int kDqBK = 64;   // keys per tile
-constexpr int kDqThreads = 256;
+constexpr int kDqBK = 64;  // keys per tile of the ping-pong dQ kernel
 
-template <int D>
-struct DqTile {
+// dQ kernel with four waves and two workgroups per CU (the counterpart of
+// bwd_kv4_kernel): a workgroup owns 128 query rows, 32 per wave (one per lane
+// pair, Q and dO rows in registers as B operands, L2 and D one value per
+// lane), and walks the keys that see them KB * 32 at a time (KB = 1 at
+// d = 128, where two 32-key blocks would not fit two waves per SIMD; 2 at
+// d = 64), recomputing
+//   S^T = K Q^T,  dP^T = V dO^T        (K and V rows from LDS),
+//   P^T = exp2(S^T c - L2),  dS^T = P^T (dP^T - D),
+//   dQ^T += K^T dS^T                    (K^T by transpose reads, dS^T packed
+//                                        straight from the accumulator).
+// One workgroup barrier per step (the K / V stage recycling); a wave skips
+// the steps whose keys are all hidden from its 32 rows.
+constexpr int kDq4Threads = 256;
+
+template <int D, int KB>
+struct Dq4Tile {
+  static constexpr int kBK = 32 * KB;                    // keys per step
   static constexpr int kKPitch = D == 128 ? 304 : 144;  // K rows: 16-byte and transpose reads
   static constexpr int kVPitch = 2 * D + 16;             // V rows: 16-byte reads
-  static constexpr int kKBytes = kDqBK * kKPitch;
-  static constexpr int kVBytes = kDqBK * kVPitch;
+  static constexpr int kKBytes = (kBK * kKPitch + 1023) / 1024 * 1024;
+  static constexpr int kVBytes = (kBK * kVPitch + 1023) / 1024 * 1024;
   static constexpr int kKBlocks = kKBytes / 1024;
   static constexpr int kVBlocks = kVBytes / 1024;
-  static_assert(kKBytes % 1024 == 0 && kVBytes % 1024 == 0, "tiles must be whole 1 KB blocks");
-  // Two waves' dQ half-blocks (32 rows of 2 D + 16 bytes each) fit a tile.
-  static_assert(2 * 32 * (2 * D + 16) <= kKBytes && 2 * 32 * (2 * D + 16) <= kVBytes, "dQ staging");
+  // Each wave stages its dQ rows (32 rows of 2 D + 16 bytes) in one buffer.
+  static_assert(32 * (2 * D + 16) <= kKBytes && 32 * (2 * D + 16) <= kVBytes, "dQ staging");
 };
 
-// (d = 128 may run one wave per SIMD: this kernel serves grids too small for
-// the ping-pong kernel below, under two workgroups per CU anyway, and held to
-// two waves per SIMD its registers spilled to scratch -- 21-27% slower.
-// d = 64 fits two waves per SIMD and is faster so.)
-template <typename T, int D>
-__global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : 2, 2)))
-void bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k,
-                   const T* __restrict__ v, const T* __restrict__ dO,
-                   const T* __restrict__ o, const float* __restrict__ lse,
-                   float* __restrict__ Dv, float* __restrict__ L2,
-                   float* __restrict__ dq, int BH, int N, int nqt, float scale, float scale_log2,
-                   int causal, int window) {
-  using TL = DqTile<D>;
-  constexpr int NW = kDqThreads / 64;
+template <typename T, int D, int KB>
+__global__ __launch_bounds__(kDq4Threads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq4_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                    const T* __restrict__ v, const T* __restrict__ dO,
+                    const T* __restrict__ o, const float* __restrict__ lse,
+                    float* __restrict__ Dv, float* __restrict__ L2,
+                    float* __restrict__ dq, int BH, int N, int nqt, float scale, float scale_log2,
+                    int causal, int window) {
+  using TL = Dq4Tile<D, KB>;
+  constexpr int BK = TL::kBK;
+  constexpr int NW = kDq4Threads / 64;
   constexpr int BQ = 32 * NW;
   constexpr int KS = D / 16;
   constexpr int CB = D / 32;
   constexpr int KPER = (TL::kKBlocks + NW - 1) / NW;
   constexpr int VPER = (TL::kVBlocks + NW - 1) / NW;
   constexpr int KP = TL::kKPitch, VP = TL::kVPitch;
-  __shared__ __attribute__((aligned(1024))) char Kb0[TL::kKBytes];
-  __shared__ __attribute__((aligned(1024))) char Kb1[TL::kKBytes];
-  __shared__ __attribute__((aligned(1024))) char Vb0[TL::kVBytes];
-  __shared__ __attribute__((aligned(1024))) char Vb1[TL::kVBytes];
+  __shared__ __attribute__((aligned(1024))) char K0[TL::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char K1[TL::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char V0[TL::kVBytes];
+  __shared__ __attribute__((aligned(1024))) char V1[TL::kVBytes];
 
   const int t = threadIdx.x;
   const int lane = t & 63, h = lane >> 5, l32 = lane & 31;
@@ -403,7 +404,7 @@ void bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k,
   const int qi = q0 + 32 * w + l32;  // this lane's query row
 
   // Q and dO rows of this lane as B fragments: [qi][16 s + 8 h + 0..7]
-  // (rows past N read as zero), and the row's L2 and D.
+  // (rows past N read as zero), and the row's D and L2.
   vec8<T> qf[KS], of[KS];
   {
     const rsrc_t q_src = make_rsrc(q + base, (uint32_t)N * D * 2u);
@@ -420,22 +421,25 @@ void bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k,
   row_constants<T, KS>(of, make_rsrc(o + base, (uint32_t)N * D * 2u), (uint32_t)(qi * D + 8 * h) * 2u, lse, Dv,
                        L2, (size_t)bh * N + qi, row_ok, h, Di, Li);
 
-  // Key tiles holding at least one key visible to this query tile, and the
-  // keys this lane's row sees.
+  // Key steps holding a key visible to any row of the workgroup, the keys
+  // this lane's row sees, and those any row of this wave sees.
   const int q_hi = q0 + BQ - 1;
   const int kmin = window >= 0 ? max(0, q0 - window) : 0;
   const int kmax = causal ? min(N - 1, q_hi) : N - 1;
-  const int kt0 = kmin / kDqBK, kt1 = kmax / kDqBK + 1;
+  const int kt0 = kmin / BK, kt1 = kmax / BK + 1;
   const int key_lo = window >= 0 ? qi - window : 0;
   const int key_hi = causal ? min(qi, N - 1) : N - 1;
+  const int wq0 = q0 + 32 * w, wq1 = wq0 + 31;
+  const int wk_lo = window >= 0 ? max(0, wq0 - window) : 0;
+  const int wk_hi = wq0 < N ? (causal ? min(N - 1, wq1) : N - 1) : -1;
 
   uint32_t kpre[KPER], vpre[VPER];
 #pragma unroll
-  for (int i = 0; i < KPER; ++i) kpre[i] = block_src<D>(w + i * NW, lane, KP);
+  for (int i = 0; i < KPER; ++i) kpre[i] = block_src_rows<D>(w + i * NW, lane, KP, BK);
 #pragma unroll
-  for (int i = 0; i < VPER; ++i) vpre[i] = block_src<D>(w + i * NW, lane, VP);
+  for (int i = 0; i < VPER; ++i) vpre[i] = block_src_rows<D>(w + i * NW, lane, VP, BK);
   auto load_kv = [&] __device__ (int kt, char* kd, char* vd) {
-    const int k0 = kt * kDqBK;
+    const int k0 = kt * BK;
     const uint32_t bytes = (uint32_t)max(0, N - k0) * D * 2u;
     const rsrc_t ks = make_rsrc(k + base + (size_t)k0 * D, bytes);
     const rsrc_t vs = make_rsrc(v + base + (size_t)k0 * D, bytes);
@@ -455,64 +459,59 @@ void bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k,
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) dqa[cb] = f32x16{};
 
-  if (kt0 < kt1) load_kv(kt0, Kb0, Vb0);
+  if (kt0 < kt1) load_kv(kt0, K0, V0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   auto tile = [&] __device__ (auto parity, int kt) {
     constexpr int P = decltype(parity)::value;
-    const char* Kc = P ? Kb1 : Kb0;
-    const char* Vc = P ? Vb1 : Vb0;
-    if (kt + 1 < kt1) load_kv(kt + 1, P ? Kb0 : Kb1, P ? Vb0 : Vb1);
-    const int k0 = kt * kDqBK;
-    const bool need_mask = (k0 + kDqBK > N) || (causal && k0 + kDqBK - 1 > q0) ||
-                           (window >= 0 && k0 < q_hi - window);
-
-    // S^T and dP^T for the tile's two 32-key blocks.
-    f32x16 sacc[2], dpacc[2];
+    const char* Kc = P ? K1 : K0;
+    const char* Vc = P ? V1 : V0;
+    if (kt + 1 < kt1) load_kv(kt + 1, P ? K0 : K1, P ? V0 : V1);
+    const int k0 = kt * BK;
+    if (k0 <= wk_hi && k0 + BK - 1 >= wk_lo) {
+      const bool need_mask = (k0 + BK > N) || (causal && k0 + BK - 1 > wq0) || (window >= 0 && k0 < wq1 - window);
+      f32x16 sc[KB], dpc[KB];
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      sacc[kb2] = f32x16{};
-      dpacc[kb2] = f32x16{};
+      for (int kb = 0; kb < KB; ++kb) {
+        sc[kb] = f32x16{};
+        dpc[kb] = f32x16{};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        sacc[kb2] = mfma32(*(const vec8<T>*)(Kc + k_rd + kb2 * 32 * KP + 32 * s), qf[s], sacc[kb2]);
-        dpacc[kb2] = mfma32(*(const vec8<T>*)(Vc + v_rd + kb2 * 32 * VP + 32 * s), of[s], dpacc[kb2]);
-      }
-    }
-    // dS^T = P^T (dP^T - D), P^T = exp2(S^T c - L2) with hidden keys at 0
-    // (the mask is one branch around the whole tile: inside the element
-    // loop it would be evaluated on every tile).
-    // (P^T overwrites S^T in place.)
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        sacc[kb2][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb2][r], scale_log2, -Li));
-    if (need_mask) {
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + kb2 * 32 + c_row(r, h);
-          sacc[kb2][r] = (uint32_t)(key - key_lo) <= (uint32_t)(key_hi - key_lo) ? sacc[kb2][r] : 0.f;
+        for (int s = 0; s < KS; ++s) {
+          sc[kb] = mfma32(*(const vec8<T>*)(Kc + k_rd + kb * 32 * KP + 32 * s), qf[s], sc[kb]);
+          dpc[kb] = mfma32(*(const vec8<T>*)(Vc + v_rd + kb * 32 * VP + 32 * s), of[s], dpc[kb]);
         }
-    }
-    uint32_t dspk[2][8];
+      }
+      // P^T = exp2(S^T c - L2) (overwriting S^T), hidden keys at 0.
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2)
-        dspk[kb2][r >> 1] = pack2<T>(sacc[kb2][r] * (dpacc[kb2][r] - Di),
-                                      sacc[kb2][r + 1] * (dpacc[kb2][r + 1] - Di));
-    // dQ^T += K^T dS^T, 16 keys per step.
+        for (int r = 0; r < 16; ++r)
+          sc[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], scale_log2, -Li));
+      if (need_mask) {
 #pragma unroll
-    for (int s = 0; s < kDqBK / 16; ++s) {
-      const uint4 dw = {dspk[s >> 1][4 * (s & 1)], dspk[s >> 1][4 * (s & 1) + 1],
-                        dspk[s >> 1][4 * (s & 1) + 2], dspk[s >> 1][4 * (s & 1) + 3]};
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-        dqa[cb] = mfma32(read_tr8<KP, T>(Kc + k_tr + 16 * s * KP + 64 * cb), as_vec8<T>(dw), dqa[cb]);
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kb * 32 + c_row(r, h);
+            sc[kb][r] = (uint32_t)(key - key_lo) <= (uint32_t)(key_hi - key_lo) ? sc[kb][r] : 0.f;
+          }
+      }
+      uint32_t dspk[KB][8];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2)
+          dspk[kb][r >> 1] = pack2<T>(sc[kb][r] * (dpc[kb][r] - Di), sc[kb][r + 1] * (dpc[kb][r + 1] - Di));
+      // dQ^T += K^T dS^T, 16 keys per step.
+#pragma unroll
+      for (int s = 0; s < BK / 16; ++s) {
+        const uint4 dw = {dspk[s >> 1][4 * (s & 1)], dspk[s >> 1][4 * (s & 1) + 1], dspk[s >> 1][4 * (s & 1) + 2],
+                          dspk[s >> 1][4 * (s & 1) + 3]};
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          dqa[cb] = mfma32(read_tr8<KP, T>(Kc + k_tr + 16 * s * KP + 64 * cb), as_vec8<T>(dw), dqa[cb]);
+      }
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads of the next tile have landed
     __syncthreads();
@@ -524,16 +523,14 @@ void bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k,
     tile(std::integral_constant<int, 1>{}, kt + 1);
   }
 
-  // dQ row qi: element r of block cb is column 32 cb + c_row(r, h); four
-  // consecutive columns per 16-byte store.
-  // dQ through LDS (the loop's last barrier freed the K tiles): two waves
-  // per tile.
-  store_dq_rows<D, CB>(dqa, scale, (w < 2 ? Kb0 : Kb1) + (w & 1) * 32 * (2 * D + 16), dq + base,
-                       q0 + 32 * w, N, lane);
+  // dQ through LDS (the loop's last barrier freed the stages): one buffer per
+  // wave.
+  store_dq_rows<D, CB>(dqa, scale, w == 0 ? K0 : w == 1 ? K1 : w == 2 ? V0 : V1, dq + base, q0 + 32 * w, N,
+                       lane);
 }
 
 // Ping-pong dQ kernel for long sequences: 8 waves, 256 query rows per
-// workgroup, the same computation as bwd_dq_kernel.  The waves form two groups
+// workgroup, the same computation as bwd_dq4_kernel.  The waves form two groups
 // (by their order of arrival on a SIMD, one wave of each group per SIMD) that
 // run the tile loop one phase apart with workgroup barriers between phases:
 // while one group's waves form P and dS of tile j on the vector ALUs, the
@@ -810,11 +807,12 @@ hipError_t launch_t(const void* q, const void* k, const void* v, const void* o, 
                        0, stream, (const T*)q, (const T*)k, (const T*)v, (const T*)dO, (const T*)o, lse,
                        Dv, L2, dq, B * H, N, nqt, scale, scale * kLog2e, mask.causal, mask.window);
   } else {
-    constexpr int BQ = kDqThreads / 2;  // 32 query rows per wave
+    constexpr int BQ = kDq4Threads / 2;  // 32 query rows per wave
     const int nqt = (N + BQ - 1) / BQ;
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3((unsigned)((long long)nqt * B * H)), dim3(kDqThreads), 0,
-                       stream, (const T*)q, (const T*)k, (const T*)v, (const T*)dO, (const T*)o, lse,
-                       Dv, L2, dq, B * H, N, nqt, scale, scale * kLog2e, mask.causal, mask.window);
+    hipLaunchKernelGGL((bwd_dq4_kernel<T, D, D == 64 ? 2 : 1>), dim3((unsigned)((long long)nqt * B * H)),
+                       dim3(kDq4Threads), 0, stream, (const T*)q, (const T*)k, (const T*)v, (const T*)dO,
+                       (const T*)o, lse, Dv, L2, dq, B * H, N, nqt, scale, scale * kLog2e, mask.causal,
+                       mask.window);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
