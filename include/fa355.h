@@ -147,8 +147,13 @@ fa_status fa_fwd_tune(const void* q, const void* k, const void* v, void* o, floa
 /*
  * The tile an automatic fa_fwd call uses for this problem: the one
  * fa_fwd_tune remembered (then *tuned = 1, if tuned is non-NULL), else the
- * built-in heuristic's (*tuned = 0).  Returns block_q and writes block_k to
- * *block_k (if non-NULL); returns 0 for invalid arguments.
+ * built-in heuristic's (*tuned = 0): 32 x 32 under a window of at most 256
+ * keys; 256 x 64 at d = 128 without a window when B * H * ceil(N / 256) >=
+ * 256; otherwise 128 x 32 at d = 128 and 128 x 64 at d = 64 (FA_FP32: 64 x 64
+ * for d <= 128, 32 x 32 above).  Returns block_q and writes block_k to
+ * *block_k (if non-NULL); returns 0 for invalid arguments.  (fa_fwd_ex with
+ * block_q = 0 and a block_k other than 64 uses 128 rows where this would give
+ * 256.)
  */
 int fa_fwd_auto_block_q(int B, int H, int N, int d, int causal, int window, fa_dtype dtype,
                         int* block_k, int* tuned);

@@ -137,13 +137,18 @@ def test_tune_rejects_bad_arguments_and_starts_empty(lib):
     assert call(d=96) == 2
     lib.fa_tune_reset()
     # nothing tuned: the heuristic (256 rows only when the grid fills 256 CUs)
-    assert fa355.fa_fwd_auto_block_q(1, 2, 64, 128, causal=True) == (32, False)
+    assert fa355.fa_fwd_auto_block_q(1, 2, 64, 128, causal=True) == (128, False)
     assert fa355.fa_fwd_auto_block_q(4, 32, 4096, 128, causal=True) == (256, False)
     assert fa355.fa_fwd_auto_block_q(4, 32, 4096, 128, causal=True, window=1024) == (128, False)
     assert fa355.fa_fwd_auto_block_q(1, 1, 8, 4, dtype=torch.float32) == (64, False)
     assert fa355.fa_fwd_auto_tile(4, 32, 4096, 128, causal=True) == ((256, 64), False)
     assert fa355.fa_fwd_auto_tile(4, 32, 4096, 128, causal=True, window=1024) == ((128, 32), False)
-    assert fa355.fa_fwd_auto_tile(1, 2, 64, 128, causal=True) == ((32, 64), False)
+    assert fa355.fa_fwd_auto_tile(1, 2, 64, 128, causal=True) == ((128, 32), False)
+    assert fa355.fa_fwd_auto_tile(1, 2, 64, 64, causal=True) == ((128, 64), False)
+    assert fa355.fa_fwd_auto_tile(4, 32, 4096, 64, causal=True) == ((128, 64), False)
+    assert fa355.fa_fwd_auto_tile(4, 32, 4096, 128, causal=True, window=256) == ((32, 32), False)
+    assert fa355.fa_fwd_auto_tile(4, 32, 4096, 128, causal=True, window=257) == ((128, 32), False)
+    assert fa355.fa_fwd_auto_tile(1, 8, 1024, 128) == ((128, 32), False)
     assert fa355.fa_fwd_auto_tile(1, 1, 8, 4, dtype=torch.float32) == ((64, 64), False)
     assert fa355.fa_fwd_auto_block_q(0, 1, 8, 4)[0] == 0
 

@@ -60,19 +60,25 @@ fa_status check_dense(int B, int H, int N, int d, float scale, int causal, int w
   return FA_OK;
 }
 
-// The built-in forward tile, as block_q * 1000 + block_k.
-int auto_tile(int B, int H, int N, int window) {
-  // Prefer the 8-wave ping-pong kernel (256 query rows, one workgroup per
-  // CU) while it still fills the 256 CUs of an MI355X -- except under a
-  // sliding window, where the 4-wave kernel with 32-key tiles measured
-  // fastest (7% ahead of 64-key tiles, 8% ahead of the ping-pong kernel, on
-  // a 1024-token window over 4 x 32 x 4096 x 128); then 4-wave workgroups
-  // (two per CU); then smaller query tiles.
+// The built-in forward tile, as block_q * 1000 + block_k, from sweeps of
+// every tile over shapes from 1 x 8 x 64 to 4 x 32 x 4096, d = 64 and 128,
+// with and without windows (one MI355X):
+//  * a window of at most 256 keys: 32 x 32 -- a tile of bq rows touches about
+//    bq + W keys for W + 1 useful ones, and short tiles waste the least
+//    (15-25% ahead of 128-row tiles at W = 128);
+//  * d = 128 without a window, while the 8-wave ping-pong kernel (256 query
+//    rows, one workgroup per CU) still fills the 256 CUs: 256 x 64;
+//  * otherwise the 4-wave kernel (two workgroups per CU) with 128 query rows
+//    and 32-key tiles at d = 128, 64-key tiles at d = 64 -- ahead of 32- and
+//    64-row tiles even when its grid leaves CUs idle (up to 4.7x at
+//    1 x 8 x 1024 x 64, where one-wave workgroups each load every K/V tile
+//    alone), and at d = 64 ahead of the ping-pong kernel too.
+// Every choice measured within 10% of the fastest tile of its shape.
+int auto_tile(int B, int H, int N, int d, int window) {
   const long long bh = (long long)B * H;
-  if (window < 0 && bh * ((N + 255) / 256) >= 256) return 256064;
-  if (bh * ((N + 127) / 128) >= 512) return window >= 0 ? 128032 : 128064;
-  if (bh * ((N + 63) / 64) >= 256) return 64064;
-  return 32064;
+  if (window >= 0 && window <= 256) return 32032;
+  if (d == 128 && window < 0 && bh * ((N + 255) / 256) >= 256) return 256064;
+  return d == 128 ? 128032 : 128064;
 }
 
 // Choices measured by the tuning calls, by kind and problem: automatic calls
@@ -261,9 +267,10 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float*
     return fail(FA_ERR_UNSUPPORTED, "%s forward supports d in {64, 128} (got %d)", dtype_name(dtype), d);
   if (block_q == 0) {  // the tuned tile, else the heuristic's
     int t = tuned_tile(dtype, d, causal, window, B, H, N);
-    if (t == 0) t = auto_tile(B, H, N, window);
+    if (t == 0) t = auto_tile(B, H, N, d, window);
     block_q = t / 1000;
     if (block_k == 0) block_k = t % 1000;
+    if (block_q == 256 && block_k != 64) block_q = 128;  // the ping-pong kernel has 64-key tiles only
   }
   if (block_k == 0) block_k = 64;
   if (!valid_16bit_tile(block_q, block_k, d))
@@ -343,7 +350,7 @@ int fa_fwd_auto_block_q(int B, int H, int N, int d, int causal, int window, fa_d
     if (block_k) *block_k = t % 1000;
     return t / 1000;
   }
-  const int a = auto_tile(B, H, N, window);
+  const int a = auto_tile(B, H, N, d, window);
   if (block_k) *block_k = a % 1000;
   return a / 1000;
 }
