@@ -147,7 +147,7 @@ fa_status fa_fwd_tune(const void* q, const void* k, const void* v, void* o, floa
 /*
  * The tile an automatic fa_fwd call uses for this problem: the one
  * fa_fwd_tune remembered (then *tuned = 1, if tuned is non-NULL), else the
- * built-in heuristic's (*tuned = 0): 32 x 32 under a window of at most 256
+ * built-in heuristic's (*tuned = 0): 32 x 32 under a window of at most 128
  * keys; 256 x 64 at d = 128 without a window when B * H * ceil(N / 256) >=
  * 256; otherwise 128 x 32 at d = 128 and 128 x 64 at d = 64 (FA_FP32: 64 x 64
  * for d <= 128, 32 x 32 above).  Returns block_q and writes block_k to

@@ -146,8 +146,8 @@ def test_tune_rejects_bad_arguments_and_starts_empty(lib):
     assert fa355.fa_fwd_auto_tile(1, 2, 64, 128, causal=True) == ((128, 32), False)
     assert fa355.fa_fwd_auto_tile(1, 2, 64, 64, causal=True) == ((128, 64), False)
     assert fa355.fa_fwd_auto_tile(4, 32, 4096, 64, causal=True) == ((128, 64), False)
-    assert fa355.fa_fwd_auto_tile(4, 32, 4096, 128, causal=True, window=256) == ((32, 32), False)
-    assert fa355.fa_fwd_auto_tile(4, 32, 4096, 128, causal=True, window=257) == ((128, 32), False)
+    assert fa355.fa_fwd_auto_tile(4, 32, 4096, 128, causal=True, window=128) == ((32, 32), False)
+    assert fa355.fa_fwd_auto_tile(4, 32, 4096, 128, causal=True, window=129) == ((128, 32), False)
     assert fa355.fa_fwd_auto_tile(1, 8, 1024, 128) == ((128, 32), False)
     assert fa355.fa_fwd_auto_tile(1, 1, 8, 4, dtype=torch.float32) == ((64, 64), False)
     assert fa355.fa_fwd_auto_block_q(0, 1, 8, 4)[0] == 0

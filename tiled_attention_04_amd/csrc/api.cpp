@@ -63,9 +63,10 @@ fa_status check_dense(int B, int H, int N, int d, float scale, int causal, int w
 // The built-in forward tile, as block_q * 1000 + block_k, from sweeps of
 // every tile over shapes from 1 x 8 x 64 to 4 x 32 x 4096, d = 64 and 128,
 // with and without windows (one MI355X):
-//  * a window of at most 256 keys: 32 x 32 -- a tile of bq rows touches about
+//  * a window of at most 128 keys: 32 x 32 -- a tile of bq rows touches about
 //    bq + W keys for W + 1 useful ones, and short tiles waste the least
-//    (15-25% ahead of 128-row tiles at W = 128);
+//    (15-25% ahead of 128-row tiles at W = 128; from W = 256 on, 128-row
+//    tiles lead again, by 25-44% at 2 x 16 x 4096);
 //  * d = 128 without a window, while the 8-wave ping-pong kernel (256 query
 //    rows, one workgroup per CU) still fills the 256 CUs: 256 x 64;
 //  * otherwise the 4-wave kernel (two workgroups per CU) with 128 query rows
@@ -73,10 +74,10 @@ fa_status check_dense(int B, int H, int N, int d, float scale, int causal, int w
 //    64-row tiles even when its grid leaves CUs idle (up to 4.7x at
 //    1 x 8 x 1024 x 64, where one-wave workgroups each load every K/V tile
 //    alone), and at d = 64 ahead of the ping-pong kernel too.
-// Every choice measured within 10% of the fastest tile of its shape.
+// Every choice measured within 15% of the fastest tile of its shape.
 int auto_tile(int B, int H, int N, int d, int window) {
   const long long bh = (long long)B * H;
-  if (window >= 0 && window <= 256) return 32032;
+  if (window >= 0 && window <= 128) return 32032;
   if (d == 128 && window < 0 && bh * ((N + 255) / 256) >= 256) return 256064;
   return d == 128 ? 128032 : 128064;
 }

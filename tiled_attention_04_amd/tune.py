@@ -1,6 +1,7 @@
 """Sweep of the tuned choices on the measured workloads.
 
     python -m tiled_attention_04_amd.tune [--reps 20] [--save tuning.json]
+    python -m tiled_attention_04_amd.tune --tile-grid [--reps 20]
 
 Three tables (markdown), each setting the measured candidates beside the
 built-in heuristic's choice:
@@ -9,6 +10,9 @@ built-in heuristic's choice:
   * the decode's split length (fa_decode_tune: 256 to 4096 tokens);
   * the backward's dQ kernel (fa_bwd_tune: 128 or 256 query rows per
     workgroup).
+With --tile-grid only the forward table is printed, over a grid of shapes
+(d = 64 and 128, 1 x 8 x 64 to 4 x 32 x 4096, with and without windows):
+the measurements the built-in tile choice rests on.
 Every tuning call remembers its fastest candidate; with --save the choices
 are written to a JSON file that a later process loads with ``load_tuning``
 (no re-measuring).  Inputs are the seeded synthetic ones the tests and the
@@ -53,6 +57,26 @@ BWD_WORKLOADS = [
 ]
 
 
+# The grid of --tile-grid: (B, H, N) for d = 64 and 128, causal and full,
+# and causal with windows on a subset.
+TILE_GRID_SHAPES = [(1, 8, 64), (1, 8, 256), (1, 8, 1024), (2, 8, 512), (1, 4, 4096), (1, 16, 2048),
+                    (2, 16, 1024), (4, 16, 1024), (1, 32, 2048), (1, 64, 2048), (2, 16, 4096), (4, 32, 4096)]
+TILE_GRID_WINDOWS = [((1, 8, 1024), (128, 512)), ((2, 16, 1024), (128, 512)), ((1, 4, 4096), (128, 512)),
+                     ((2, 16, 4096), (256, 1024)), ((4, 32, 4096), (1024,))]
+
+
+def tile_grid_workloads():
+    out = []
+    for d in (64, 128):
+        for B, H, N in TILE_GRID_SHAPES:
+            for causal in (False, True):
+                out.append((f"{'causal' if causal else 'full'} {B}x{H}x{N}x{d} bf16", (B, H, N, d), "bf16", causal, -1))
+        for (B, H, N), windows in TILE_GRID_WINDOWS:
+            for w in windows:
+                out.append((f"window-{w} {B}x{H}x{N}x{d} bf16", (B, H, N, d), "bf16", True, w))
+    return out
+
+
 def visible_pairs(N: int, causal: bool, window: int) -> int:
     i = np.arange(N, dtype=np.int64)
     hi = i + 1 if causal else np.full(N, N, dtype=np.int64)
@@ -64,13 +88,14 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--reps", type=int, default=20)
     ap.add_argument("--save", default=None, help="write the tuned choices to this JSON file")
+    ap.add_argument("--tile-grid", action="store_true", help="only the forward table, over a grid of shapes")
     args = ap.parse_args()
     dev = torch.device("cuda:0")
     print("| workload | " + " | ".join(f"{bq}x{bk} ms" for bq, bk in fa355.TUNE_CANDIDATES)
-          + " | fastest | TFLOP/s | heuristic | heuristic ms |")
-    print("|---|" + "---|" * (len(fa355.TUNE_CANDIDATES) + 4))
+          + " | fastest | TFLOP/s | heuristic | heuristic ms | heuristic / fastest |")
+    print("|---|" + "---|" * (len(fa355.TUNE_CANDIDATES) + 5))
     tuned = []
-    for name, (B, H, N, d), dtype, causal, window in WORKLOADS:
+    for name, (B, H, N, d), dtype, causal, window in (tile_grid_workloads() if args.tile_grid else WORKLOADS):
         q, k, v = (t.to(dev) for t in attention_inputs(B, H, N, d, dtype, seed=0))
         fa355.fa_tune_reset()
         heur, _ = fa355.fa_fwd_auto_tile(B, H, N, d, causal=causal, window=window, dtype=q.dtype)
@@ -78,10 +103,12 @@ def main():
         flops = 4.0 * d * B * H * visible_pairs(N, causal, window)
         tf = flops / (times[best] * 1e-3) / 1e12
         cells = " | ".join(f"{times[t]:.4f}" if times[t] >= 0 else "-" for t in fa355.TUNE_CANDIDATES)
-        print(f"| {name} | {cells} | {best[0]}x{best[1]} | {tf:.1f} | {heur[0]}x{heur[1]} | {times[heur]:.4f} |",
-              flush=True)
+        print(f"| {name} | {cells} | {best[0]}x{best[1]} | {tf:.1f} | {heur[0]}x{heur[1]} | {times[heur]:.4f} | "
+              f"{times[heur] / times[best]:.2f} |", flush=True)
         tuned += fa355.fa_tune_export()
         del q, k, v
+    if args.tile_grid:
+        return
 
     print()
     print("| decode workload | " + " | ".join(f"{c} tok ms" for c in fa355.DECODE_TUNE_CANDIDATES)
