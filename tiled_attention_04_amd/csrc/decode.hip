@@ -35,6 +35,15 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kUnroll = 8;
 
+// A 16-byte load of a cache row, marked non-temporal: every row is read once
+// per call, so keeping it in the caches only evicts other data.  (Measured on
+// the 64 x 32 ragged batch: 5.86 -> 6.61 TB/s dense, 5.47 -> 6.05 TB/s with a
+// 1024-token window, 5.93 -> 6.52 TB/s paged; same values.)
+constexpr int kCacheStream = 2;  // buffer-load cache policy: nt
+__device__ __forceinline__ uint4 load_row16(rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCacheStream));
+}
+
 template <typename T>
 __device__ __forceinline__ void widen(const uint4& u, float (&x)[16 / sizeof(T)]);
 
@@ -151,8 +160,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const uint32_t off = (uint32_t)((row0 + u * RPW + g) * D + e * VEC) * (uint32_t)sizeof(T);
-      kr[u] = load16(k_src, off);
-      vr[u] = load16(v_src, off);
+      kr[u] = load_row16(k_src, off);
+      vr[u] = load_row16(v_src, off);
     }
     // Every load of the trip is issued before any of them is used (left
     // alone, the compiler interleaves fp16 loads with their mixed-precision
