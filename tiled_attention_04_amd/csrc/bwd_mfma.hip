@@ -566,6 +566,8 @@ __device__ __forceinline__ void pin_dq_phase(uint32_t (&ds)[2][8], f32x16 (&acc)
     for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(ds[i][j]));
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) asm volatile("" : "+v"(acc[cb]));
+#else
+  (void)ds; (void)acc;
 #endif
 }
 

@@ -536,6 +536,8 @@ __device__ __forceinline__ void pin_softmax_results(uint32_t (&pk)[2][8], f32x16
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) asm volatile("" : "+v"(oacc[cb]));
   asm volatile("" : "+v"(l_run), "+v"(m_ref));
+#else
+  (void)pk; (void)oacc; (void)l_run; (void)m_ref;
 #endif
 }
 
