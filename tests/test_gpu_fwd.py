@@ -267,3 +267,21 @@ def test_heads_not_multiple_of_eight_use_plain_order():
         O, L = oracle.attention_ref(q, k, v, 1 / 8, True)
         check_bf16(o, O, "O")
         check_lse(lse, L, "L")
+
+
+@pytest.mark.parametrize("bk", [32, 64])
+def test_automatic_tile_with_explicit_key_tile(bk):
+    """fa_fwd_ex(block_q = 0, block_k) where the built-in choice is the 256-row
+    kernel (64-key tiles only): a 32-key request runs 128 query rows instead,
+    and the result is the explicit tile's, bit for bit."""
+    B, H, N, d = 1, 64, 1024, 128
+    fa.fa_tune_reset()
+    assert fa.fa_fwd_auto_tile(B, H, N, d, causal=True) == ((256, 64), False)
+    q, k, v = (t.cuda() for t in attention_inputs(B, H, N, d, "bf16", seed=12))
+    o, lse = fa.fa_fwd_ex(q, k, v, 0, bk, causal=True)
+    o_ref, lse_ref = fa.fa_fwd_ex(q, k, v, 256 if bk == 64 else 128, bk, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref)
+    O, L = oracle.attention_ref(q[0, 5][None].cpu(), k[0, 5][None].cpu(), v[0, 5][None].cpu(), 1 / math.sqrt(d), True)
+    check_bf16(o[0, 5].cpu(), O[0], "O")
+    check_lse(lse[0, 5].cpu(), L[0], "L")
