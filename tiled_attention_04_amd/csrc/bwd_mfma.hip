@@ -315,25 +315,40 @@ __device__ __forceinline__ void store_dq_rows(const f32x16 (&dqa)[CB], float sca
 // D = rowsum(dO * O) (the two lanes of a row each sum half of the columns)
 // and L2 = L * log2(e) (+inf for a row without visible keys, so that every P
 // of it is 0).  Stored for the dK / dV kernel, which runs after them.
+// In three parts, so that the loads of O and L travel with the kernel's first
+// K/V tile instead of taking a memory round trip of their own: issue the
+// loads, form D and L2 once the first tile's wait has passed, store them at
+// the end.
+template <int KS>
+struct RowConstants {
+  uint4 o[KS];  // this lane's half of the O row, as the dO fragments
+  float L;
+};
+template <int KS>
+__device__ __forceinline__ void row_constants_load(RowConstants<KS>& rc, rsrc_t o_src, uint32_t row_off,
+                                                   const float* __restrict__ lse, size_t row, bool row_ok) {
+#pragma unroll
+  for (int s = 0; s < KS; ++s) rc.o[s] = load16(o_src, row_off + 32u * s);
+  rc.L = row_ok ? lse[row] : 0.f;
+}
 template <typename T, int KS>
-__device__ __forceinline__ void row_constants(const vec8<T> (&of)[KS], rsrc_t o_src, uint32_t row_off,
-                                              const float* __restrict__ lse, float* __restrict__ Dv,
-                                              float* __restrict__ L2, size_t row, bool row_ok, int h,
-                                              float& Di, float& Li) {
+__device__ __forceinline__ void row_constants_form(const RowConstants<KS>& rc, const vec8<T> (&of)[KS], float& Di,
+                                                   float& Li) {
   float p = 0.f;
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
-    const uint4 a = load16(o_src, row_off + 32u * s);
     const uint4 b = __builtin_bit_cast(uint4, of[s]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p = __builtin_fmaf(lo16<T>(word(a, i)), lo16<T>(word(b, i)), p);
-      p = __builtin_fmaf(hi16<T>(word(a, i)), hi16<T>(word(b, i)), p);
+      p = __builtin_fmaf(lo16<T>(word(rc.o[s], i)), lo16<T>(word(b, i)), p);
+      p = __builtin_fmaf(hi16<T>(word(rc.o[s], i)), hi16<T>(word(b, i)), p);
     }
   }
   Di = pair_sum(p);
-  const float L = row_ok ? lse[row] : 0.f;
-  Li = L == kNegInf ? __builtin_inff() : L * kLog2e;
+  Li = rc.L == kNegInf ? __builtin_inff() : rc.L * kLog2e;
+}
+__device__ __forceinline__ void row_constants_store(float* __restrict__ Dv, float* __restrict__ L2, size_t row,
+                                                    bool row_ok, int h, float Di, float Li) {
   if (row_ok && h == 0) {
     Dv[row] = Di;
     L2[row] = Li;
@@ -417,9 +432,10 @@ void bwd_dq4_kernel(const T* __restrict__ q, const T* __restrict__ k,
     }
   }
   const bool row_ok = qi < N;
-  float Li, Di;
-  row_constants<T, KS>(of, make_rsrc(o + base, (uint32_t)N * D * 2u), (uint32_t)(qi * D + 8 * h) * 2u, lse, Dv,
-                       L2, (size_t)bh * N + qi, row_ok, h, Di, Li);
+  RowConstants<KS> rc;
+  row_constants_load<KS>(rc, make_rsrc(o + base, (uint32_t)N * D * 2u), (uint32_t)(qi * D + 8 * h) * 2u, lse,
+                         (size_t)bh * N + qi, row_ok);
+  float Li, Di;  // formed once the first tile's wait has passed
 
   // Key steps holding a key visible to any row of the workgroup, the keys
   // this lane's row sees, and those any row of this wave sees.
@@ -462,6 +478,7 @@ void bwd_dq4_kernel(const T* __restrict__ q, const T* __restrict__ k,
   if (kt0 < kt1) load_kv(kt0, K0, V0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  row_constants_form<T, KS>(rc, of, Di, Li);
 
   auto tile = [&] __device__ (auto parity, int kt) {
     constexpr int P = decltype(parity)::value;
@@ -527,6 +544,7 @@ void bwd_dq4_kernel(const T* __restrict__ q, const T* __restrict__ k,
   // wave.
   store_dq_rows<D, CB>(dqa, scale, w == 0 ? K0 : w == 1 ? K1 : w == 2 ? V0 : V1, dq + base, q0 + 32 * w, N,
                        lane);
+  row_constants_store(Dv, L2, (size_t)bh * N + qi, row_ok, h, Di, Li);
 }
 
 // Ping-pong dQ kernel for long sequences: 8 waves, 256 query rows per
@@ -625,9 +643,10 @@ void bwd_dq_pp_kernel(const T* __restrict__ q, const T* __restrict__ k,
     }
   }
   const bool row_ok = qi < N;
-  float Li, Di;
-  row_constants<T, KS>(of, make_rsrc(o + base, (uint32_t)N * D * 2u), (uint32_t)(qi * D + 8 * h) * 2u, lse, Dv,
-                       L2, (size_t)bh * N + qi, row_ok, h, Di, Li);
+  RowConstants<KS> rc;
+  row_constants_load<KS>(rc, make_rsrc(o + base, (uint32_t)N * D * 2u), (uint32_t)(qi * D + 8 * h) * 2u, lse,
+                         (size_t)bh * N + qi, row_ok);
+  float Li, Di;  // formed once the first tile's wait has passed
 
   // Key tiles holding at least one key visible to this query tile, the keys
   // this lane's row sees, and the tiles that hold any key visible to this
@@ -703,7 +722,8 @@ void bwd_dq_pp_kernel(const T* __restrict__ q, const T* __restrict__ k,
   const int nblk = (TL::kKBlocks - w + NW - 1) / NW + (TL::kVBlocks - w + NW - 1) / NW;
   load_share(kt0, integral_constant<int, 0>{});
   if (kt0 + 1 < kt1) load_share(kt0 + 1, integral_constant<int, 1>{});
-  wait_vm(kt0 + 1 < kt1 ? nblk : 0);  // tile kt0 only; tile kt0+1 may still land
+  wait_vm(kt0 + 1 < kt1 ? nblk : 0);  // tile kt0 only (and O and L, issued before it); tile kt0+1 may still land
+  row_constants_form<T, KS>(rc, of, Di, Li);
   barrier_keep_loads();
   if (active(kt0)) scores(integral_constant<int, 0>{});
   if (grp == 1) {  // group 1 runs one phase behind
@@ -791,6 +811,7 @@ void bwd_dq_pp_kernel(const T* __restrict__ q, const T* __restrict__ k,
   // waves per K stage, the last two in V stage 0.
   store_dq_rows<D, CB>(dqa, scale, (w < 2 ? K0 : w < 4 ? K1 : w < 6 ? K2 : V0) + (w & 1) * 32 * (2 * D + 16),
                        dq + base, q0 + 32 * w, N, lane);
+  row_constants_store(Dv, L2, (size_t)bh * N + qi, row_ok, h, Di, Li);
 }
 
 template <typename T, int D>
