@@ -331,6 +331,44 @@ fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_page
                           void* workspace, size_t workspace_bytes, fa_dtype dtype, void* stream);
 
 /*
+ * fa_decode_check -- find the arguments that fa_decode, fa_decode_noalloc
+ * and fa_decode_paged repair on the device instead of rejecting.  Those
+ * calls read seqlens (and the page table) only on the device, so they cannot
+ * return an error for them without synchronising: a length outside [1,
+ * capacity] is clamped into it, and a table entry outside [0, num_pages)
+ * leaves its page's tokens out (the argument readings of "Build a
+ * FlashAttention Kernel with Online Softmax and KV Cache in Pure Python",
+ * Step 4, and of the paged cache of "Build a FlashAttention-2 Inference
+ * Kernel from Scratch in Pure Python", Extending It, extended to such input).
+ * This call reports them, one int32 per sequence, so that a caller can check
+ * its inputs on the stream before or after the decode:
+ *   flags[s] = 0, or the OR of
+ *     FA_CHECK_LENGTH (1): seqlens[s] < 1 or > capacity (capacity = Lmax
+ *                          for a dense cache, max_pages * page_size for a
+ *                          paged one);
+ *     FA_CHECK_PAGE   (2): paged only -- an entry of block_table[s] outside
+ *                          [0, num_pages) among the pages holding the tokens
+ *                          the decode reads (with the window, if any, of the
+ *                          decode call: pages before its first token are
+ *                          never read).
+ *
+ *   seqlens     : [S] int32, device memory
+ *   block_table : [S, max_pages] int32, device memory; NULL for a dense cache
+ *                 (page_size, max_pages and num_pages are then ignored)
+ *   Lmax        : dense cache length (ignored for a paged cache)
+ *   window      : as in the decode call (-1 off)
+ *   flags       : [S] int32, device memory, written
+ *
+ * Asynchronous on `stream`; allocates nothing.  S = 0 is a no-op.  Errors:
+ * FA_ERR_INVALID_ARG for null pointers, S < 0, window < -1, non-positive
+ * sizes, or max_pages * page_size above 2^31-1; FA_ERR_HIP if the launch fails.
+ */
+#define FA_CHECK_LENGTH 1
+#define FA_CHECK_PAGE 2
+fa_status fa_decode_check(const int32_t* seqlens, const int32_t* block_table, int S, int Lmax, int page_size,
+                          int max_pages, int num_pages, int window, int32_t* flags, void* stream);
+
+/*
  * fa_bwd_workspace_size -- bytes of workspace fa_bwd needs (0 if invalid).
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);

@@ -33,7 +33,7 @@ def test_header_declares_the_expected_calls():
     for must in ("fa_fwd", "fa_fwd_ex", "fa_fwd_tune", "fa_tune_export", "fa_tune_import", "fa_decode_tune",
                  "fa_decode_auto_chunk", "fa_bwd_tune", "fa_bwd_auto_dq_rows", "fa_decode", "fa_decode_paged",
                  "fa_bwd", "fa_decode_workspace_size", "fa_bwd_workspace_size", "fa_status_str", "fa_last_error",
-                 "fa_version"):
+                 "fa_version", "fa_decode_check"):
         assert must in names
 
 
@@ -79,6 +79,26 @@ def fwd(lib, q=FAKE, B=1, H=1, N=8, d=64, scale=0.125, causal=0, window=-1, dtyp
 def test_fwd_rejects_bad_arguments(lib, kw, status):
     assert fwd(lib, **kw) == status
     assert fa355.last_error() != ""
+
+
+def test_decode_check_rejects_bad_arguments(lib):
+    def call(**kw):
+        a = dict(sl=FAKE, table=None, S=4, L=128, ps=64, mp=4, npg=10, window=-1, flags=FAKE)
+        a.update(kw)
+        return lib.fa_decode_check(a["sl"], a["table"], a["S"], a["L"], a["ps"], a["mp"], a["npg"], a["window"],
+                                   a["flags"], None)
+    assert call(sl=None) == 1
+    assert call(flags=None) == 1
+    assert call(S=-1) == 1
+    assert call(window=-2) == 1
+    assert call(L=0) == 1                       # dense cache needs a length
+    assert call(table=FAKE, L=0, ps=0) == 1     # paged: sizes must be positive
+    assert call(table=FAKE, mp=0) == 1
+    assert call(table=FAKE, npg=0) == 1
+    assert call(table=FAKE, ps=1 << 20, mp=1 << 12) == 1
+    assert "2^31" in fa355.last_error()
+    assert call(S=0) == 0                       # nothing to check: no launch
+    assert call(S=0, table=FAKE, L=0) == 0
 
 
 def test_decode_rejects_bad_arguments(lib):

@@ -226,3 +226,30 @@ def test_outputs_written_only_in_bounds(paged, window):
     O, L = oracle_decode(inp, window)
     check_bf16(o.cpu(), O, "o")
     check_lse(lse.cpu(), L, "lse")
+
+
+def test_decode_check_flags_what_the_decode_repairs():
+    """fa_decode_check reports the lengths the decode clamps and the absent
+    pages it leaves out -- only among the pages the call reads."""
+    Lmax = 100
+    lens = torch.tensor([0, 5, 100, 101, -3], dtype=torch.int32, device="cuda")
+    f = fa.fa_decode_check(lens, Lmax=Lmax)
+    assert f.cpu().tolist() == [fa.FA_CHECK_LENGTH, 0, 0, fa.FA_CHECK_LENGTH, fa.FA_CHECK_LENGTH]
+    # Paged: 64-token pages, 4 table columns, a pool of 10 pages.
+    lens = torch.tensor([130, 300, 64, 200, 1], dtype=torch.int32, device="cuda")
+    table = torch.tensor([[1, 2, -1, 99],     # token 128-129 on an absent page
+                          [0, 1, 2, 3],       # 300 > 4 * 64: clamped to 256, every page present
+                          [3, 99, 99, 99],    # only page 0 is read
+                          [99, 99, 4, 5],     # pages 0 and 1 absent
+                          [10, 0, 0, 0]],     # entry == num_pages: absent
+                         dtype=torch.int32, device="cuda")
+    f = fa.fa_decode_check(lens, table, page_size=64, num_pages=10).cpu().tolist()
+    assert f == [fa.FA_CHECK_PAGE, fa.FA_CHECK_LENGTH, 0, fa.FA_CHECK_PAGE, fa.FA_CHECK_PAGE]
+    # With a 50-token window sequence 3 reads tokens 149..199 (pages 2 and 3):
+    # the absent pages 0 and 1 are never read.
+    f = fa.fa_decode_check(lens, table, page_size=64, num_pages=10, window=50).cpu().tolist()
+    assert f == [fa.FA_CHECK_PAGE, fa.FA_CHECK_LENGTH, 0, 0, fa.FA_CHECK_PAGE]
+    # A batch the decode tests use is clean.
+    inp = decode_inputs(3, 2, 128, 1, 300, seed=6, seqlens=[300, 260, 129])
+    sl = torch.from_numpy(inp.seqlens).cuda()
+    assert not fa.fa_decode_check(sl, Lmax=300).any()

@@ -8,6 +8,8 @@ replaced: if it is missing, calls raise.
 
 from .fa355 import (  # noqa: F401
     FA_BF16,
+    FA_CHECK_LENGTH,
+    FA_CHECK_PAGE,
     FA_FP16,
     FA_FP32,
     BWD_TUNE_CANDIDATES,
@@ -22,6 +24,7 @@ from .fa355 import (  # noqa: F401
     fa_bwd_workspace_size,
     fa_decode,
     fa_decode_auto_chunk,
+    fa_decode_check,
     fa_decode_noalloc,
     fa_decode_tune,
     fa_decode_paged,

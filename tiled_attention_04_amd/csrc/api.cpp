@@ -550,6 +550,25 @@ fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_page
               "fa_decode_paged");
 }
 
+fa_status fa_decode_check(const int32_t* seqlens, const int32_t* block_table, int S, int Lmax, int page_size,
+                          int max_pages, int num_pages, int window, int32_t* flags, void* stream) {
+  if (!seqlens || !flags) return fail(FA_ERR_INVALID_ARG, "seqlens and flags must be non-null");
+  if (S < 0) return fail(FA_ERR_INVALID_ARG, "S must be >= 0 (got %d)", S);
+  if (window < -1) return fail(FA_ERR_INVALID_ARG, "window must be -1 (off) or >= 0 (got %d)", window);
+  if (block_table) {
+    if (page_size <= 0 || max_pages <= 0 || num_pages <= 0)
+      return fail(FA_ERR_INVALID_ARG, "page_size, max_pages and num_pages must be positive (got %d, %d, %d)",
+                  page_size, max_pages, num_pages);
+    if ((long long)max_pages * page_size > INT_MAX)
+      return fail(FA_ERR_INVALID_ARG, "max_pages * page_size exceeds 2^31-1");
+  } else if (Lmax <= 0) {
+    return fail(FA_ERR_INVALID_ARG, "Lmax must be positive for a dense cache (got %d)", Lmax);
+  }
+  return done(fa::launch_decode_check(seqlens, block_table, S, Lmax, page_size, max_pages, num_pages, window,
+                                      flags, (hipStream_t)stream),
+              "fa_decode_check");
+}
+
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
   if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 0;
   return fa::bwd_workspace_bytes(B, H, N, d);

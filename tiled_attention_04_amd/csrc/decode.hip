@@ -403,4 +403,41 @@ hipError_t launch_decode_paged(const void* q, const void* k_pages, const void* v
                   chunk, ws, elem, PagedCache{block_table, page_size, max_pages, num_pages}, stream);
 }
 
+namespace {
+
+// One thread per sequence: the arguments the decode kernels repair on the
+// device instead of rejecting (clamp_len above; table entries outside the
+// pool), reported as flag bits.  For a paged cache only the pages that hold
+// the tokens a call reads are examined (with a window, the pages before its
+// first token are never read, so whatever they hold does no harm).
+__global__ __launch_bounds__(256) void decode_check_kernel(const int32_t* __restrict__ seqlens,
+                                                           PagedCache pc, int S, int Lmax, int window,
+                                                           int32_t* __restrict__ flags) {
+  const int s = blockIdx.x * 256 + threadIdx.x;
+  if (s >= S) return;
+  const int cap = pc.table ? pc.max_pages * pc.page_size : Lmax;
+  int n = seqlens[s];
+  int f = (n < 1 || n > cap) ? 1 : 0;
+  if (pc.table) {
+    clamp_len(n, cap);
+    const int lo = window >= 0 ? max(0, n - 1 - window) : 0;
+    const int32_t* row = pc.table + (size_t)s * pc.max_pages;
+    for (int p = lo / pc.page_size; p <= (n - 1) / pc.page_size; ++p)
+      if ((uint32_t)row[p] >= (uint32_t)pc.num_pages) f |= 2;
+  }
+  flags[s] = f;
+}
+
+}  // namespace
+
+hipError_t launch_decode_check(const int32_t* seqlens, const int32_t* block_table, int S, int Lmax,
+                               int page_size, int max_pages, int num_pages, int window, int32_t* flags,
+                               hipStream_t stream) {
+  if (S == 0) return hipSuccess;
+  const PagedCache pc{block_table, page_size, max_pages, num_pages};
+  hipLaunchKernelGGL(decode_check_kernel, dim3((unsigned)((S + 255) / 256)), dim3(256), 0, stream, seqlens, pc, S,
+                     Lmax, window, flags);
+  return hipGetLastError();
+}
+
 }  // namespace fa

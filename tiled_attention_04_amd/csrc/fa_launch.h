@@ -48,6 +48,11 @@ hipError_t launch_decode_paged(const void* q, const void* k_pages, const void* v
 // has checked that decode_workspace_bytes fits).  No allocation; calls that
 // overlap on one device race on the array.
 constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+// Per-sequence flags of the arguments the decode repairs on the device
+// (bit 1: length outside [1, capacity]; bit 2: an absent page among those read).
+hipError_t launch_decode_check(const int32_t* seqlens, const int32_t* block_table, int S, int Lmax,
+                               int page_size, int max_pages, int num_pages, int window, int32_t* flags,
+                               hipStream_t stream);
 hipError_t launch_decode_noalloc(const void* q, const void* kc, const void* vc, const int32_t* seqlens,
                                  void* o, float* lse, int S, int H, int Lmax, int d, float scale,
                                  int window, int chunk, Elem elem, hipStream_t stream);

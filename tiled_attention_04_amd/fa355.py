@@ -49,6 +49,7 @@ SIGNATURES = {
     "fa_bwd_tune": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _I, _P,
                          _I, _P, _P]),
     "fa_bwd_auto_dq_rows": (_I, [_I, _I, _I, _I, _I, _I, _I, _P]),
+    "fa_decode_check": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
 }
 
 
@@ -261,6 +262,33 @@ def fa_decode(q, kcache, vcache, seqlens, *, scale=None, window: int = -1, chunk
                            int(window), int(chunk), wp, workspace.numel() * workspace.element_size(),
                            _DTYPE[dt], _stream(stream)))
     return o, lse
+
+
+FA_CHECK_LENGTH, FA_CHECK_PAGE = 1, 2
+
+
+def fa_decode_check(seqlens, block_table=None, *, Lmax: int = 0, page_size: int = 0, num_pages: int = 0,
+                    window: int = -1, flags=None, stream=None):
+    """Per-sequence flags of the arguments the decode calls repair on the device
+    (0: none; FA_CHECK_LENGTH: length outside [1, capacity]; FA_CHECK_PAGE: an
+    entry outside the pool among the pages the decode reads).  seqlens: int32
+    [S]; block_table: int32 [S, max_pages], or None for a dense cache of length
+    Lmax.  Returns flags, int32 [S] on the GPU, written asynchronously."""
+    S = seqlens.shape[0]
+    if flags is None:
+        flags = torch.empty(S, dtype=torch.int32, device=seqlens.device)
+    if S == 0:
+        return flags
+    sp = _dev(seqlens, "seqlens", torch.int32, (S,))
+    if block_table is None:
+        tp, max_pages = None, 0
+    else:
+        max_pages = block_table.shape[1]
+        tp = _dev(block_table, "block_table", torch.int32, (S, max_pages))
+    fp = _dev(flags, "flags", torch.int32, (S,))
+    _check(lib().fa_decode_check(sp, tp, S, int(Lmax), int(page_size), int(max_pages), int(num_pages),
+                                 int(window), fp, _stream(stream)))
+    return flags
 
 
 DECODE_TUNE_CANDIDATES = (256, 512, 1024, 2048, 4096)
