@@ -389,11 +389,13 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d);
  *   dq, dk, dv     : [B, H, N, d] float32 outputs
  *   workspace      : >= fa_bwd_workspace_size(B, H, N, d) bytes
  *
- * Supported: FA_BF16 and FA_FP16 with d in {64, 128}.  No atomics: dq, dk and dv are
- * each written once, so repeated calls give identical bits.  P and dS are
+ * Supported: FA_BF16 and FA_FP16 with d in {64, 128}, and FA_FP32 with any
+ * 1 <= d <= 256.  No atomics: dq, dk and dv are each written once, so
+ * repeated calls give identical bits.  For the 16-bit types P and dS are
  * rounded to the input type for the products that use them (fp32
- * accumulation): with FA_FP16 a |dP - D| above 65504 overflows, as for
- * any fp16 operand.
+ * accumulation): with FA_FP16 a |dP - D| above 65504 overflows, as for any
+ * fp16 operand.  FA_FP32 keeps every step in float32 (plain FMAs, the
+ * exactness path beside the float32 forward).
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
                  const float* lse, float* dq, float* dk, float* dv,
@@ -419,8 +421,9 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
  * (both give identical dk and dv, and form dq from the same terms in
  * the same order).
  *
- * Arguments as fa_bwd, plus reps in [1, 1000].  Like fa_fwd_tune it
- * SYNCHRONISES `stream` and creates two HIP events.
+ * Arguments as fa_bwd (16-bit types only: the float32 backward has one
+ * kernel and returns FA_ERR_UNSUPPORTED), plus reps in [1, 1000].  Like
+ * fa_fwd_tune it SYNCHRONISES `stream` and creates two HIP events.
  */
 fa_status fa_bwd_tune(const void* q, const void* k, const void* v, const void* o, const void* dO,
                       const float* lse, float* dq, float* dk, float* dv,
@@ -431,7 +434,8 @@ fa_status fa_bwd_tune(const void* q, const void* k, const void* v, const void* o
 /*
  * The dQ kernel (query rows per workgroup, 128 or 256) an fa_bwd call uses
  * for this problem: the one fa_bwd_tune remembered (*tuned = 1), else the
- * built-in choice (*tuned = 0).  Returns 0 for invalid arguments.
+ * built-in choice (*tuned = 0).  Returns 0 for invalid arguments and for
+ * FA_FP32, whose backward has a single kernel.
  */
 int fa_bwd_auto_dq_rows(int B, int H, int N, int d, int causal, int window, fa_dtype dtype,
                         int* tuned);

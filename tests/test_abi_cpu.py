@@ -292,11 +292,14 @@ def test_bwd_rejects_bad_arguments(lib):
                           a["d"], 0.1, 1, a["window"], a["ws"], a["wsb"], a["dtype"], None)
     assert call(ptr=None) == 1
     assert call(N=0) == 1
-    assert call(dtype=0) == 2
     assert call(dtype=3) == 1
     assert call(d=32) == 2
     assert call(d=32, dtype=2) == 2
     assert call(wsb=8) == 3
+    # float32: any d <= 256 passes the checks up to the workspace
+    assert call(dtype=0, d=257) == 2
+    assert call(dtype=0, d=32, wsb=8) == 3
+    assert call(dtype=0, d=256, ws=None) == 3
 
 
 def test_workspace_sizes(lib):

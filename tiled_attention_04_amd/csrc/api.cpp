@@ -207,15 +207,17 @@ fa_status check_bwd(const void* q, const void* k, const void* v, const void* o, 
     return fail(FA_ERR_INVALID_ARG, "every tensor pointer of fa_bwd must be non-null");
   fa_status st = check_dense(B, H, N, d, scale, causal, window, dtype);
   if (st != FA_OK) return st;
-  if (dtype == FA_FP32) return fail(FA_ERR_UNSUPPORTED, "backward supports bf16 and fp16 inputs only");
-  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "backward supports d in {64, 128} (got %d)", d);
+  if (dtype == FA_FP32) {
+    if (d > 256) return fail(FA_ERR_UNSUPPORTED, "float32 backward supports d <= 256 (got %d)", d);
+  } else if (d != 64 && d != 128) {
+    return fail(FA_ERR_UNSUPPORTED, "%s backward supports d in {64, 128} (got %d)", dtype_name(dtype), d);
+  }
   if ((long long)N * d * 4 > kMaxBufferBytes)
     return fail(FA_ERR_UNSUPPORTED, "one (batch, head) slice of the float32 gradients exceeds 2 GiB");
-  const long long rows = (long long)B * H * N;
-  const long long pre_rows_per_block = 2048 / d;  // 256 threads, d / 8 per row
-  const long long pre_threads = (rows + pre_rows_per_block - 1) / pre_rows_per_block * 256;
-  const long long main_threads = (long long)((N + 127) / 128) * B * H * 512;  // 128 keys per workgroup
-  if (pre_threads > kMaxThreadsPerLaunch || main_threads > kMaxThreadsPerLaunch)
+  // The largest grid: 256-thread workgroups over tiles of 128 query rows or
+  // keys (16-bit), or bwd_fp32_tile(d) (float32).
+  const int tile = dtype == FA_FP32 ? fa::bwd_fp32_tile(d) : 128;
+  if ((long long)((N + tile - 1) / tile) * B * H * 256 > kMaxThreadsPerLaunch)
     return fail(FA_ERR_UNSUPPORTED, "grid too large");
   const size_t need = fa::bwd_workspace_bytes(B, H, N, d);
   if (!workspace || workspace_bytes < need)
@@ -581,6 +583,11 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   const fa_status st = check_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, window,
                                  workspace, workspace_bytes, dtype);
   if (st != FA_OK) return st;
+  if (dtype == FA_FP32)
+    return done(fa::launch_bwd_fp32((const float*)q, (const float*)k, (const float*)v, (const float*)o,
+                                    (const float*)dO, lse, dq, dk, dv, B, H, N, d, scale, fa::Mask{causal, window},
+                                    workspace, (hipStream_t)stream),
+                "fa_bwd (float32)");
   return done(fa::launch_bwd_mfma(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale,
                                   fa::Mask{causal, window}, workspace, dtype == FA_FP16,
                                   auto_dq_rows(dtype, d, causal, window, B, H, N), (hipStream_t)stream),
@@ -594,6 +601,7 @@ fa_status fa_bwd_tune(const void* q, const void* k, const void* v, const void* o
   const fa_status st = check_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, window,
                                  workspace, workspace_bytes, dtype);
   if (st != FA_OK) return st;
+  if (dtype == FA_FP32) return fail(FA_ERR_UNSUPPORTED, "the float32 backward has one kernel: nothing to tune");
   if (reps < 1 || reps > 1000) return fail(FA_ERR_INVALID_ARG, "reps must be 1..1000 (got %d)", reps);
   const hipStream_t s = (hipStream_t)stream;
   const fa::Mask mask{causal, window};

@@ -19,7 +19,7 @@ struct Mask {
 // Element type of q, k, v, o (and dO, the caches).
 enum class Elem { kF32, kBF16, kF16 };
 
-// Generic float32 forward, any 1 <= d <= 128, tiles 1..64 x 1..64.
+// Generic float32 forward, any 1 <= d <= 256, tiles 1..64 x 1..64 that fit LDS.
 hipError_t launch_fwd_fp32(const float* q, const float* k, const float* v, float* o, float* lse,
                            int B, int H, int N, int d, float scale, Mask mask, int block_q,
                            int block_k, hipStream_t stream);
@@ -61,6 +61,14 @@ hipError_t launch_decode_noalloc(const void* q, const void* kc, const void* vc, 
 // kernels, d in {64, 128}.  dq_rows picks the dQ kernel: 256 (8-wave
 // ping-pong) or 128 (4 waves); bwd_auto_dq_rows is the built-in choice.
 size_t bwd_workspace_bytes(int B, int H, int N, int d);
+
+// Float32 backward, any 1 <= d <= 256: the dQ kernel (which also leaves D of
+// every query row in ws) then the dK / dV kernel, both over square tiles of
+// bwd_fp32_tile(d) rows.  ws: at least B * H * N floats.
+int bwd_fp32_tile(int d);
+hipError_t launch_bwd_fp32(const float* q, const float* k, const float* v, const float* o, const float* dO,
+                           const float* lse, float* dq, float* dk, float* dv, int B, int H, int N, int d,
+                           float scale, Mask mask, void* ws, hipStream_t stream);
 int bwd_auto_dq_rows(int B, int H, int N);
 hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const void* o,
                            const void* dO, const float* lse, float* dq, float* dk, float* dv,
