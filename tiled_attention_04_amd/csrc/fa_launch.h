@@ -19,7 +19,7 @@ struct Mask {
 // Element type of q, k, v, o (and dO, the caches).
 enum class Elem { kF32, kBF16, kF16 };
 
-// Generic float32 forward, any 1 <= d <= 256, tiles 1..64 x 1..64 that fit LDS.
+// Generic float32 forward, any 1 <= d <= 256, tiles 1..64 x 1..64.
 hipError_t launch_fwd_fp32(const float* q, const float* k, const float* v, float* o, float* lse,
                            int B, int H, int N, int d, float scale, Mask mask, int block_q,
                            int block_k, hipStream_t stream);

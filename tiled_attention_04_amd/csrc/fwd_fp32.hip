@@ -1,54 +1,62 @@
-// Generic float32 forward: any head size d <= 256 and any tile shape up to
-// 64 x 64 whose tiles fit the LDS staging buffers (block_q * d and
-// block_k * d at most 8192 floats: 64 x 64 tiles up to d = 128, 32 x 32 up
-// to d = 256), including the 4 x 4 tiles of the worked example
-// ("FlashAttention Algorithm > Worked Example", Setting Up the Example).
+// Generic float32 forward: any head size 1 <= d <= 256 and any tile shape
+// from 1 x 1 to 64 x 64 (block_q query rows x block_k keys), including the
+// 4 x 4 tiles of the worked example ("FlashAttention Algorithm > Worked
+// Example", Setting Up the Example).
 //
 // One workgroup owns one query tile and walks the key/value tiles the mask
 // leaves visible, keeping the running max m, running sum l and unnormalised
 // output O of the online softmax ("Building Flash Attention from Scratch in
-// Pure NumPy", Architecture Overview and Step 2).  Everything is staged in
-// LDS and computed with plain float32 FMAs; this path is for exactness on
-// small and odd shapes, the bf16 MFMA kernels are the fast path.
-#include "fa_common.h"
+// Pure NumPy", Architecture Overview and Step 2) for each of its rows; the
+// statistics move once per key tile of the caller's size, as the page's loop
+// does, so every tile shape gives the same result up to rounding.  The
+// arithmetic is plain float32 FMAs on LDS-staged tiles (the exactness path;
+// the 16-bit MFMA kernels are the fast path): the tiles sit in 64-row LDS
+// buffers whatever the caller's tile, a 16 x 16 grid of threads holds 4 x 4
+// scores each, a row's max and sum are butterflies over its 16 lanes, and
+// the P V product accumulates one key at a time into registers.  Up to
+// d = 128, K and V have their own buffers; above, V is staged into K's
+// buffer once the scores of the tile are taken, so that 64-row tiles of
+// 256 columns fit the LDS.
 #include "fa_launch.h"
+#include "fp32_tile.h"
 
 namespace fa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kMaxTile = 64;
-constexpr int kTileFloats = 8192;            // Q, V and O tiles: block * d floats at most
-constexpr int kKFloats = kMaxTile * 129;     // K tile, rows padded by one float
-constexpr int kSPitch = kMaxTile + 1;
+using namespace fp32;
 
+constexpr int kTB = 64;
+
+template <int DM, bool kSharedKV>
 __global__ __launch_bounds__(kThreads) void fwd_fp32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, float* __restrict__ lse, int N, int d, int BQ, int BK, int nqt,
     float scale, int causal, int window) {
-  __shared__ float Qs[kTileFloats];
-  __shared__ float Ks[kKFloats];
-  __shared__ float Vs[kTileFloats];
-  __shared__ float Os[kTileFloats];
-  __shared__ float Ss[kMaxTile * kSPitch];
-  __shared__ float m_row[kMaxTile], l_row[kMaxTile], a_row[kMaxTile];
+  using F = Tile<kTB, DM>;
+  constexpr int R = F::R, P = F::kPitch, SP = F::kSPitch;
+  __shared__ __align__(16) float Qs[kTB * P];
+  __shared__ __align__(16) float Ks[kTB * P];
+  __shared__ __align__(16) float Vbuf[kSharedKV ? 4 : kTB * P];
+  __shared__ float Ts[kTB * SP];
+  float* Vs = kSharedKV ? Ks : Vbuf;
 
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, ti = t >> 4, tj = t & 15;
   const int bh = blockIdx.x / nqt;
-  const int q0 = (blockIdx.x % nqt) * BQ;
-  const size_t base = (size_t)bh * (size_t)N * (size_t)d;
+  const int q0 = (blockIdx.x - bh * nqt) * BQ;
+  const size_t base = (size_t)bh * N * d;
+  const int dpad = (d + 3) & ~3;
   const int nq = min(BQ, N - q0);
-  const int kpitch = d + 1;
 
-  for (int i = t; i < BQ * d; i += kThreads) {
-    const int r = i / d, c = i % d;
-    Qs[i] = r < nq ? q[base + (size_t)(q0 + r) * d + c] : 0.f;
-    Os[i] = 0.f;
+  stage<kTB, P>(Qs, q + base, q0, nq, d, dpad);
+
+  float m_run[R], l_run[R];
+  float4 oacc[R][F::kChunks];
+#pragma unroll
+  for (int a = 0; a < R; ++a) {
+    m_run[a] = kNegInf;
+    l_run[a] = 0.f;
   }
-  if (t < BQ) {
-    m_row[t] = kNegInf;
-    l_row[t] = 0.f;
-  }
+  zero<kTB, DM>(oacc);
 
   // Key tiles that hold at least one visible key for this query tile.
   const int kmin = window >= 0 ? max(0, q0 - window) : 0;
@@ -56,61 +64,62 @@ __global__ __launch_bounds__(kThreads) void fwd_fp32_kernel(
   for (int kt = kmin / BK; kt <= kmax / BK; ++kt) {
     const int k0 = kt * BK;
     const int nk = min(BK, N - k0);
-    __syncthreads();  // readers of the previous tile are done
-    for (int i = t; i < BK * d; i += kThreads) {
-      const int r = i / d, c = i % d;
-      const bool in = r < nk;
-      const size_t g = base + (size_t)(k0 + r) * d + c;
-      Ks[r * kpitch + c] = in ? k[g] : 0.f;
-      Vs[i] = in ? v[g] : 0.f;
-    }
+    __syncthreads();  // the previous tile's readers are done
+    stage<kTB, P>(Ks, k + base, k0, nk, d, dpad);
+    if constexpr (!kSharedKV) stage<kTB, P>(Vs, v + base, k0, nk, d, dpad);
     __syncthreads();
-    // Scaled, masked scores of the tile.
-    for (int i = t; i < BQ * BK; i += kThreads) {
-      const int r = i / BK, c = i % BK;
-      float acc = 0.f;
-      for (int e = 0; e < d; ++e) acc = __builtin_fmaf(Qs[r * d + e], Ks[c * kpitch + e], acc);
-      const int qi = q0 + r, kj = k0 + c;
-      const bool vis = kj < N && (!causal || kj <= qi) && (window < 0 || kj >= qi - window);
-      Ss[r * kSPitch + c] = vis ? acc * scale : kNegInf;
-    }
-    __syncthreads();
-    // Online-softmax statistics, one thread per query row.
-    if (t < BQ) {
-      const float m_old = m_row[t];
+    float s[1][R][R];
+    dot_blocks<kTB, DM, 1>(Qs, Ks, nullptr, nullptr, dpad, ti, tj, s);
+#pragma unroll
+    for (int a = 0; a < R; ++a) {
+      const int i = ti + 16 * a;
+      float x[R];
       float mx = kNegInf;
-      for (int c = 0; c < BK; ++c) mx = fmaxf(mx, Ss[t * kSPitch + c]);
-      const float m_new = fmaxf(m_old, mx);
+#pragma unroll
+      for (int b = 0; b < R; ++b) {
+        const int j = tj + 16 * b;
+        const bool vis = i < nq && j < nk && visible(q0 + i, k0 + j, N, causal, window);
+        x[b] = vis ? s[0][a][b] * scale : kNegInf;
+        mx = fmaxf(mx, x[b]);
+      }
+      const float m_new = fmaxf(m_run[a], row_max16(mx));
       const float ref = m_new == kNegInf ? 0.f : m_new;  // no key seen yet: any finite reference
-      const float alpha = expf(m_old - ref);               // exp(-inf) = 0 while m_old is -inf
+      const float alpha = expf(m_run[a] - ref);           // exp(-inf) = 0 while m is -inf
       float sum = 0.f;
-      for (int c = 0; c < BK; ++c) {
-        const float p = expf(Ss[t * kSPitch + c] - ref);
-        Ss[t * kSPitch + c] = p;
+#pragma unroll
+      for (int b = 0; b < R; ++b) {
+        const float p = expf(x[b] - ref);
+        Ts[(tj + 16 * b) * SP + i] = p;  // [key][query]: the P V product walks keys
         sum += p;
       }
-      l_row[t] = alpha * l_row[t] + sum;
-      m_row[t] = m_new;
-      a_row[t] = alpha;
+      l_run[a] = alpha * l_run[a] + row_sum16(sum);
+      m_run[a] = m_new;
+#pragma unroll
+      for (int c = 0; c < F::kChunks; ++c) {
+        oacc[a][c].x *= alpha;
+        oacc[a][c].y *= alpha;
+        oacc[a][c].z *= alpha;
+        oacc[a][c].w *= alpha;
+      }
+    }
+    if constexpr (kSharedKV) {
+      __syncthreads();  // the scores are taken: K's buffer takes V
+      stage<kTB, P>(Vs, v + base, k0, nk, d, dpad);
     }
     __syncthreads();
-    // O <- alpha * O + P V.
-    for (int i = t; i < BQ * d; i += kThreads) {
-      const int r = i / d, c = i % d;
-      float acc = Os[i] * a_row[r];
-      for (int j = 0; j < BK; ++j) acc = __builtin_fmaf(Ss[r * kSPitch + j], Vs[j * d + c], acc);
-      Os[i] = acc;
+    accumulate<kTB, DM>(Ts, Vs, nk, dpad, ti, tj, oacc);
+  }
+
+  float inv[R];
+#pragma unroll
+  for (int a = 0; a < R; ++a) inv[a] = l_run[a] > 0.f ? 1.f / l_run[a] : 0.f;
+  store_rows<kTB, DM>(o + base, oacc, inv, q0, nq, d, ti, tj);
+  if (lse != nullptr && tj == 0) {
+#pragma unroll
+    for (int a = 0; a < R; ++a) {
+      const int i = ti + 16 * a;
+      if (i < nq) lse[(size_t)bh * N + q0 + i] = l_run[a] > 0.f ? m_run[a] + logf(l_run[a]) : kNegInf;
     }
-  }
-  __syncthreads();
-  for (int i = t; i < nq * d; i += kThreads) {
-    const int r = i / d;
-    const float l = l_row[r];
-    o[base + (size_t)q0 * d + i] = l > 0.f ? Os[i] / l : 0.f;
-  }
-  if (t < nq && lse != nullptr) {
-    const float l = l_row[t];
-    lse[(size_t)bh * N + q0 + t] = l > 0.f ? m_row[t] + logf(l) : kNegInf;
   }
 }
 
@@ -120,9 +129,13 @@ hipError_t launch_fwd_fp32(const float* q, const float* k, const float* v, float
                            int B, int H, int N, int d, float scale, Mask mask, int block_q,
                            int block_k, hipStream_t stream) {
   const int nqt = (N + block_q - 1) / block_q;
-  const long long grid = (long long)nqt * B * H;
-  hipLaunchKernelGGL(fwd_fp32_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, q, k, v, o,
-                     lse, N, d, block_q, block_k, nqt, scale, mask.causal, mask.window);
+  const unsigned grid = (unsigned)((long long)nqt * B * H);
+  if (d <= 128)
+    hipLaunchKernelGGL((fwd_fp32_kernel<128, false>), dim3(grid), dim3(kThreads), 0, stream, q, k, v, o, lse, N, d,
+                       block_q, block_k, nqt, scale, mask.causal, mask.window);
+  else
+    hipLaunchKernelGGL((fwd_fp32_kernel<256, true>), dim3(grid), dim3(kThreads), 0, stream, q, k, v, o, lse, N, d,
+                       block_q, block_k, nqt, scale, mask.causal, mask.window);
   return hipGetLastError();
 }
 
