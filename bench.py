@@ -47,6 +47,12 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # Stages of one step, in the order they run.
 STAGES = ("fwd", "window", "decode", "bwd", "paged", "fwd16", "decw", "bwdw", "dec16", "bwd16", "c2", "c2c")
+# The float32 exactness path (plain FMAs), timed only when named in --stages:
+# the causal forward and backward at the backward's shape.
+OPT_STAGES = ("fwd32", "bwd32")
+# Float32 FMA rate of the vector ALUs without packed FP32 (off in this build):
+# 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz.
+PEAK_FP32_ALU_TFLOPS = 78.6
 W_DEC = 1024   # sliding window of the windowed decode stage
 W_BWD = 1024   # sliding window of the windowed backward stage
 
@@ -198,7 +204,9 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=15)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--stages", default=",".join(STAGES))
+    ap.add_argument("--stages", default=",".join(STAGES),
+                    help="comma-separated stages; the default runs every stage of STAGES, the "
+                         "float32 ones (" + ",".join(OPT_STAGES) + ") run only when named")
     ap.add_argument("--page-size", type=int, default=64)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, copy 1 GiB device-to-device three times: the reference "
@@ -294,6 +302,14 @@ def main():
         dq9, dk9, dv9 = (torch.empty(q9.shape, dtype=torch.float32, device=dev) for _ in range(3))
         ws9 = torch.empty(fa.fa_bwd_workspace_size(B5, H5, N5, d5), dtype=torch.uint8, device=dev)
 
+    if "fwd32" in stages or "bwd32" in stages:
+        log("generating float32 inputs")
+        q10, k10, v10, g10 = (t.to(dev) for t in attention_inputs(B5, H5, N5, d5, "fp32", seed=0,
+                                                                  with_grad=True))
+        o10, l10 = fa.fa_fwd(q10, k10, v10, causal=True)
+        dq10, dk10, dv10 = (torch.empty_like(q10) for _ in range(3))
+        ws10 = torch.empty(fa.fa_bwd_workspace_size(B5, H5, N5, d5), dtype=torch.uint8, device=dev)
+
     w2 = WORKLOADS["fwd_b1_h8_n1024_d64_bf16"]
     B2, H2, N2, d2, T2 = w2["B"], w2["H"], w2["N"], w2["d"], w2["block"]
     if "c2" in stages or "c2c" in stages:
@@ -325,8 +341,15 @@ def main():
                                    workspace=ws9),
         "c2": lambda: fa.fa_fwd_ex(q2, k2, v2, T2, T2, o=o2, lse=l2),
         "c2c": lambda: fa.fa_fwd_ex(q2, k2, v2, T2, T2, causal=True, o=o2c, lse=l2c),
+        "fwd32": lambda: fa.fa_fwd(q10, k10, v10, causal=True, o=o10, lse=l10),
+        "bwd32": lambda: fa.fa_bwd(q10, k10, v10, o10, g10, l10, causal=True, dq=dq10, dk=dk10, dv=dv10,
+                                   workspace=ws10),
     }
-    run = [n for n in STAGES if n in stages]
+    unknown = [n for n in stages if n not in calls]
+    if unknown:
+        print(f"unknown stages: {', '.join(unknown)}", file=sys.stderr)
+        sys.exit(2)
+    run = [n for n in STAGES + OPT_STAGES if n in stages]
 
     def step(ev=None):
         for i, n in enumerate(run):
@@ -437,6 +460,16 @@ def main():
         mfma_stage(f"fwd_b1_h8_n1024_d64_tile{T2}", flops2, "c2", None)
     if "c2c" in ms:
         mfma_stage(f"fwd_causal_b1_h8_n1024_d64_tile{T2}", flops2 / 2, "c2c", None)
+
+    # The float32 path runs on the vector ALUs: priced against their FMA rate.
+    for key, name, flops in (("fwd32", "fwd_causal_fp32_b2_h16_n4096_d128", flops5 * 0.4),
+                             ("bwd32", "bwd_causal_fp32_b2_h16_n4096_d128", flops5)):
+        if key in ms:
+            tf = flops / (ms[key] * 1e-3) / 1e12
+            components[name] = {
+                **stage_stats(key), "TFLOP/s": round(tf, 2), "algorithmic_tflop": round(flops / 1e12, 5),
+                "roofline": {"bound": "alu", "achieved": round(tf, 2), "peak": PEAK_FP32_ALU_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(tf / PEAK_FP32_ALU_TFLOPS, 4), "traffic": None}}
 
     if args.copy_calibration:
         log("copy calibration: 3 x 1 GiB device-to-device")
