@@ -93,8 +93,10 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
  * fa_fwd_ex -- fa_fwd with an explicit tile shape (0, 0 = automatic).
  *   FA_FP32: 1 <= block_q <= 64, 1 <= block_k <= 64 (any values, e.g. 4 x 4
  *            for the worked example "FlashAttention Algorithm > Worked
- *            Example", Setting Up the Example) at any d <= 256;
- *            automatic: 64 x 64.
+ *            Example", Setting Up the Example) at any d <= 256, on the
+ *            vector ALUs; or 128 x 32 at d = 64 and 128, on the matrix cores
+ *            (float32 MFMA: float32 products and sums).  Automatic: 128 x 32
+ *            at d = 64 and 128, 64 x 64 otherwise.
  *   FA_BF16, FA_FP16: block_q in {32, 64, 128} (1, 2 or 4 waves) with
  *            block_k in {32, 64}, or 128 at d = 64 (at d = 128 two 128-key
  *            score tiles exceed a wave's registers); or 256 x 64 (8 waves,
@@ -149,7 +151,7 @@ fa_status fa_fwd_tune(const void* q, const void* k, const void* v, void* o, floa
  * built-in heuristic's (*tuned = 0): 32 x 32 under a window of at most 128
  * keys; 256 x 64 at d = 128 without a window when B * H * ceil(N / 256) >=
  * 256; otherwise 128 x 32 at d = 128 and 128 x 64 at d = 64 (FA_FP32:
- * 64 x 64).  Returns block_q and writes block_k to
+ * 128 x 32 at d = 64 and 128, 64 x 64 otherwise).  Returns block_q and writes block_k to
  * *block_k (if non-NULL); returns 0 for invalid arguments.  (fa_fwd_ex with
  * block_q = 0 and a block_k other than 64 uses 128 rows where this would give
  * 256.)

@@ -67,7 +67,8 @@ def fwd(lib, q=FAKE, B=1, H=1, N=8, d=64, scale=0.125, causal=0, window=-1, dtyp
     (dict(causal=2), 1), (dict(window=-2), 1), (dict(scale=float("inf")), 1),
     (dict(scale=float("nan")), 1), (dict(dtype=7), 1),
     (dict(d=96), 2), (dict(d=257, dtype=0), 2), (dict(d=256, dtype=0, bq=64, bk=65), 1),
-    (dict(d=200, dtype=0, bq=0, bk=64), 1), (dict(d=96, dtype=2), 2), (dict(dtype=3), 1),
+    (dict(d=200, dtype=0, bq=0, bk=64), 1), (dict(d=96, dtype=0, bq=128, bk=32), 1),
+    (dict(d=128, dtype=0, bq=128, bk=64), 1), (dict(d=96, dtype=2), 2), (dict(dtype=3), 1),
     (dict(dtype=2, bq=48), 1),
     (dict(bq=48), 1), (dict(bq=512), 1), (dict(bq=256, bk=32), 1), (dict(bq=64, bk=96), 1),
     (dict(d=128, bq=64, bk=128), 1), (dict(bq=256, bk=128), 1),
@@ -170,6 +171,10 @@ def test_tune_rejects_bad_arguments_and_starts_empty(lib):
     assert fa355.fa_fwd_auto_tile(4, 32, 4096, 128, causal=True, window=129) == ((128, 32), False)
     assert fa355.fa_fwd_auto_tile(1, 8, 1024, 128) == ((128, 32), False)
     assert fa355.fa_fwd_auto_tile(1, 1, 8, 4, dtype=torch.float32) == ((64, 64), False)
+    # float32 at d = 64 and 128: the matrix-core kernel's 128 x 32
+    assert fa355.fa_fwd_auto_tile(2, 16, 4096, 128, dtype=torch.float32) == ((128, 32), False)
+    assert fa355.fa_fwd_auto_tile(1, 1, 8, 64, dtype=torch.float32) == ((128, 32), False)
+    assert fa355.fa_fwd_auto_tile(1, 1, 8, 96, dtype=torch.float32) == ((64, 64), False)
     assert fa355.fa_fwd_auto_block_q(0, 1, 8, 4)[0] == 0
 
 

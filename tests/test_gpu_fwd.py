@@ -76,6 +76,53 @@ def test_fp32_large_head_dims(d, bq, bk, causal, window):
     check_fp32(lse, L, "L")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 31, 33, 128, 129, 300, 1000])
+@pytest.mark.parametrize("causal,window", [(False, -1), (True, -1), (True, 45), (False, 30), (True, 0)])
+def test_fp32_matrix_core_tile(N, d, causal, window):
+    """The automatic float32 tile at d = 64 and 128: 128 query rows x 32 keys
+    on float32 MFMA, ragged tails and every mask."""
+    assert fa.fa_fwd_auto_tile(1, 2, N, d, dtype=torch.float32)[0] == (128, 32)
+    q, k, v = attention_inputs(1, 2, N, d, "fp32", seed=N + d + 1)
+    o, lse = run(q, k, v, causal, window)
+    O, L = oracle.attention_ref(q, k, v, 1 / math.sqrt(d), causal, window)
+    check_fp32(o, O, "O")
+    check_fp32(lse, L, "L")
+
+
+@pytest.mark.parametrize("causal,window", [(True, -1), (False, -1), (True, 1024)])
+def test_fp32_matrix_core_many_heads(causal, window):
+    """2 x 16 x 2048 x 128 float32 (a grid over every XCD), sampled heads
+    against the oracle; the explicit 128 x 32 tile gives the same bits."""
+    q, k, v = attention_inputs(2, 16, 2048, 128, "fp32", seed=5)
+    o, lse = run(q, k, v, causal, window)
+    o2, lse2 = run(q, k, v, causal, window, bq=128, bk=32)
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    s = 1 / math.sqrt(128)
+    for b, h in ((0, 0), (1, 11)):
+        O, L = oracle.attention_ref(q[b, h], k[b, h], v[b, h], s, causal, window)
+        check_fp32(o[b, h], O, f"O[{b},{h}]")
+        check_fp32(lse[b, h], L, f"L[{b},{h}]")
+
+
+@pytest.mark.parametrize("offset", [-40.0, 25.0])
+def test_fp32_matrix_core_row_offsets(offset):
+    """Every score of a row shifted far from zero: the softmax is
+    shift-invariant.  A float32 score s is itself held only to 2^-24 |s|, so
+    the bar widens to max(1e-5, 8 * 2^-24 * max|s| * max|O|)."""
+    N, d = 180, 64
+    q, k, v = attention_inputs(1, 2, N, d, "fp32", seed=11)
+    k = k.clone()
+    k[..., 0] = 1.0
+    q = q.clone()
+    q[..., 0] = offset * math.sqrt(d)
+    o, lse = run(q, k, v, True)
+    O, L = oracle.attention_ref(q, k, v, 1 / math.sqrt(d), True)
+    smax = float(np.abs(to64(q)[0] @ to64(k)[0].transpose(0, 2, 1)).max()) / math.sqrt(d)
+    check_fp32(o, O, "O", atol=max(1e-5, 8 * 2.0 ** -24 * smax * float(np.abs(O).max())))
+    check_fp32(lse, L, "L", atol=max(1e-5, 8 * 2.0 ** -24 * smax))
+
+
 # ------------------------------------------------------------------ bf16 ---
 
 @pytest.mark.parametrize("causal", [False, True])

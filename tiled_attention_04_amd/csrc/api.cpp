@@ -254,11 +254,23 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float*
   const fa::Mask mask{causal, window};
   if (dtype == FA_FP32) {
     if (d > 256) return fail(FA_ERR_UNSUPPORTED, "float32 forward supports d <= 256 (got %d)", d);
-    if (block_q == 0 && block_k == 0) block_q = block_k = 64;
-    if (block_q < 1 || block_q > 64 || block_k < 1 || block_k > 64)
-      return fail(FA_ERR_INVALID_ARG, "float32 tiles must be 1..64 x 1..64 (got %d x %d)", block_q, block_k);
+    // 128 x 32 on the matrix cores at d = 64 and 128 (the automatic tile
+    // there), any tile up to 64 x 64 on the vector ALUs.
+    const bool mfma = d == 64 || d == 128;
+    if (block_q == 0 && block_k == 0) {
+      block_q = mfma ? 128 : 64;
+      block_k = mfma ? 32 : 64;
+    }
+    const bool on_mfma = mfma && block_q == 128 && block_k == 32;
+    if (!on_mfma && (block_q < 1 || block_q > 64 || block_k < 1 || block_k > 64))
+      return fail(FA_ERR_INVALID_ARG, "float32 tiles must be 1..64 x 1..64, or 128 x 32 at d = 64 or 128 "
+                  "(got %d x %d at d = %d)", block_q, block_k, d);
     const long long wgs = (long long)B * H * ((N + block_q - 1) / block_q);
     if (wgs * 256 > kMaxThreadsPerLaunch) return fail(FA_ERR_UNSUPPORTED, "grid too large");
+    if (on_mfma)
+      return done(fa::launch_fwd_fp32_mfma((const float*)q, (const float*)k, (const float*)v, (float*)o, lse,
+                                           B, H, N, d, scale, mask, (hipStream_t)stream),
+                  "fa_fwd (float32)");
     return done(fa::launch_fwd_fp32((const float*)q, (const float*)k, (const float*)v, (float*)o, lse,
                                     B, H, N, d, scale, mask, block_q, block_k, (hipStream_t)stream),
                 "fa_fwd (float32)");
@@ -341,8 +353,9 @@ int fa_fwd_auto_block_q(int B, int H, int N, int d, int causal, int window, fa_d
   if (block_k) *block_k = 0;
   if (check_dense(B, H, N, d, 0.f, causal, window, dtype) != FA_OK) return 0;
   if (dtype == FA_FP32) {
-    if (block_k) *block_k = 64;
-    return 64;
+    const bool mfma = d == 64 || d == 128;
+    if (block_k) *block_k = mfma ? 32 : 64;
+    return mfma ? 128 : 64;
   }
   const int t = tuned_tile(dtype, d, causal, window, B, H, N);
   if (t != 0) {

@@ -19,6 +19,11 @@ struct Mask {
 // Element type of q, k, v, o (and dO, the caches).
 enum class Elem { kF32, kBF16, kF16 };
 
+// Float32 forward on the matrix cores, d in {64, 128}: 128 query rows x
+// 32 keys per tile (the automatic float32 tile at those head sizes).
+hipError_t launch_fwd_fp32_mfma(const float* q, const float* k, const float* v, float* o, float* lse, int B,
+                                int H, int N, int d, float scale, Mask mask, hipStream_t stream);
+
 // Generic float32 forward, any 1 <= d <= 256, tiles 1..64 x 1..64.
 hipError_t launch_fwd_fp32(const float* q, const float* k, const float* v, float* o, float* lse,
                            int B, int H, int N, int d, float scale, Mask mask, int block_q,
