@@ -593,11 +593,12 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   const fa_status st = check_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, window,
                                  workspace, workspace_bytes, dtype);
   if (st != FA_OK) return st;
-  if (dtype == FA_FP32)
-    return done(fa::launch_bwd_fp32((const float*)q, (const float*)k, (const float*)v, (const float*)o,
-                                    (const float*)dO, lse, dq, dk, dv, B, H, N, d, scale, fa::Mask{causal, window},
-                                    workspace, (hipStream_t)stream),
+  if (dtype == FA_FP32) {  // matrix cores at d = 64 and 128, vector ALUs otherwise
+    const auto launch = d == 64 || d == 128 ? fa::launch_bwd_fp32_mfma : fa::launch_bwd_fp32;
+    return done(launch((const float*)q, (const float*)k, (const float*)v, (const float*)o, (const float*)dO, lse,
+                       dq, dk, dv, B, H, N, d, scale, fa::Mask{causal, window}, workspace, (hipStream_t)stream),
                 "fa_bwd (float32)");
+  }
   return done(fa::launch_bwd_mfma(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale,
                                   fa::Mask{causal, window}, workspace, dtype == FA_FP16,
                                   auto_dq_rows(dtype, d, causal, window, B, H, N), (hipStream_t)stream),

@@ -71,6 +71,12 @@ size_t bwd_workspace_bytes(int B, int H, int N, int d);
 // every query row in ws) then the dK / dV kernel, both over square tiles of
 // bwd_fp32_tile(d) rows.  ws: at least B * H * N floats.
 int bwd_fp32_tile(int d);
+// Float32 backward on the matrix cores, d in {64, 128}: the dQ kernel (which
+// also stores D and L log2(e) of every query row in ws) then the dK / dV
+// kernel, 128 rows per workgroup.  ws: at least 2 * B * H * N floats.
+hipError_t launch_bwd_fp32_mfma(const float* q, const float* k, const float* v, const float* o, const float* dO,
+                                const float* lse, float* dq, float* dk, float* dv, int B, int H, int N, int d,
+                                float scale, Mask mask, void* ws, hipStream_t stream);
 hipError_t launch_bwd_fp32(const float* q, const float* k, const float* v, const float* o, const float* dO,
                            const float* lse, float* dq, float* dk, float* dv, int B, int H, int N, int d,
                            float scale, Mask mask, void* ws, hipStream_t stream);
