@@ -47,12 +47,10 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # Stages of one step, in the order they run.
 STAGES = ("fwd", "window", "decode", "bwd", "paged", "fwd16", "decw", "bwdw", "dec16", "bwd16", "c2", "c2c")
-# The float32 exactness path (plain FMAs), timed only when named in --stages:
-# the causal forward and backward at the backward's shape.
+# The float32 path, timed only when named in --stages: the causal forward and
+# backward at the backward's shape (d = 128: the float32 MFMA kernels).
 OPT_STAGES = ("fwd32", "bwd32")
-# Float32 FMA rate of the vector ALUs without packed FP32 (off in this build):
-# 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz.
-PEAK_FP32_ALU_TFLOPS = 78.6
+PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense float32 MFMA
 W_DEC = 1024   # sliding window of the windowed decode stage
 W_BWD = 1024   # sliding window of the windowed backward stage
 
@@ -461,15 +459,15 @@ def main():
     if "c2c" in ms:
         mfma_stage(f"fwd_causal_b1_h8_n1024_d64_tile{T2}", flops2 / 2, "c2c", None)
 
-    # The float32 path runs on the vector ALUs: priced against their FMA rate.
+    # The float32 path at d = 128 runs on float32 MFMA: priced against its peak.
     for key, name, flops in (("fwd32", "fwd_causal_fp32_b2_h16_n4096_d128", flops5 * 0.4),
                              ("bwd32", "bwd_causal_fp32_b2_h16_n4096_d128", flops5)):
         if key in ms:
             tf = flops / (ms[key] * 1e-3) / 1e12
             components[name] = {
                 **stage_stats(key), "TFLOP/s": round(tf, 2), "algorithmic_tflop": round(flops / 1e12, 5),
-                "roofline": {"bound": "alu", "achieved": round(tf, 2), "peak": PEAK_FP32_ALU_TFLOPS,
-                             "unit": "TFLOP/s", "frac": round(tf / PEAK_FP32_ALU_TFLOPS, 4), "traffic": None}}
+                "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP32_MFMA_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(tf / PEAK_FP32_MFMA_TFLOPS, 4), "traffic": None}}
 
     if args.copy_calibration:
         log("copy calibration: 3 x 1 GiB device-to-device")

@@ -395,8 +395,8 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d);
  * repeated calls give identical bits.  For the 16-bit types P and dS are
  * rounded to the input type for the products that use them (fp32
  * accumulation): with FA_FP16 a |dP - D| above 65504 overflows, as for any
- * fp16 operand.  FA_FP32 keeps every step in float32 (plain FMAs, the
- * exactness path beside the float32 forward).
+ * fp16 operand.  FA_FP32 keeps every step in float32 (float32 MFMA at
+ * d = 64 and 128, vector-ALU FMAs at other d).
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
                  const float* lse, float* dq, float* dk, float* dv,
