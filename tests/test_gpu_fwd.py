@@ -201,7 +201,7 @@ def test_bf16_scale_values(scale):
     check_lse(lse, L, "L")
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("fp32", 32)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("fp32", 32), ("fp32", 128)])
 @pytest.mark.parametrize("causal,window", [(True, -1), (True, 23), (False, 23)])
 def test_masked_positions_contribute_exactly_zero(dtype, d, causal, window):
     """Perturbing K and V where the mask hides them leaves O and L bitwise equal."""
@@ -232,16 +232,22 @@ def test_forward_is_deterministic():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-def test_output_written_only_in_bounds():
-    """Guard band after o and lse stays untouched."""
-    B, H, N, d = 1, 2, 65, 128
-    q, k, v = (t.cuda() for t in attention_inputs(B, H, N, d, "bf16", seed=1))
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp32", 128), ("fp32", 64), ("fp32", 40)])
+def test_output_written_only_in_bounds(dtype, d):
+    """Guard band after o and lse stays untouched (16-bit, float32 matrix-core
+    and float32 vector-ALU kernels)."""
+    B, H, N = 1, 2, 65
+    q, k, v = (t.cuda() for t in attention_inputs(B, H, N, d, dtype, seed=1))
     n = B * H * N * d
-    obuf = torch.full((n + 4096,), 7.0, dtype=torch.bfloat16, device="cuda")
+    obuf = torch.full((n + 4096,), 7.0, dtype=q.dtype, device="cuda")
     lbuf = torch.full((B * H * N + 1024,), 7.0, dtype=torch.float32, device="cuda")
     fa.fa_fwd(q, k, v, causal=True, o=obuf[:n].view(B, H, N, d), lse=lbuf[: B * H * N].view(B, H, N))
     torch.cuda.synchronize()
     assert torch.all(obuf[n:] == 7.0) and torch.all(lbuf[B * H * N:] == 7.0)
+    O, L = oracle.attention_ref(q.cpu(), k.cpu(), v.cpu(), 1 / math.sqrt(d), True)
+    check = check_fp32 if dtype == "fp32" else check_bf16
+    check(obuf[:n].view(B, H, N, d).cpu(), O, "O")
+    check_lse(lbuf[: B * H * N].view(B, H, N).cpu(), L, "L")
 
 
 # -------------------------------------------- full size: 4 x 32 x 4096 x 128
