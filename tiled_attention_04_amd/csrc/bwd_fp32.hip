@@ -3,16 +3,17 @@
 // Step 4: D = rowsum(dO * O), P = exp(scale * Q K^T - L), dV = P^T dO,
 // dP = dO V^T, dS = P * (dP - D), dQ = scale * dS K, dK = scale * dS^T Q).
 //
-// The float32 companion of the 16-bit MFMA backward, with the same two-kernel
-// shape and no atomics.  The first kernel owns a tile of query rows: it forms
-// D for them (kept in the workspace for the second) and walks the key tiles
-// the mask leaves visible, accumulating dQ in registers.  The second owns a
-// tile of keys and walks the query tiles that see them, accumulating dK and
-// dV.  Everything is plain float32 FMAs on tiles staged in LDS, the head
-// dimension padded to a multiple of 4 with zeros (which add exact zeros):
-// 64 x 64 tiles with a 4 x 4 block of scores per thread for d <= 128,
-// 32 x 32 tiles with 2 x 2 up to d = 256.  Every output is written once, so
-// repeated calls give identical bits.
+// The vector-ALU float32 backward, for the head sizes the float32 MFMA
+// kernels do not take (any d other than 64 and 128), with the 16-bit
+// backward's two-kernel shape and no atomics.  The first kernel owns a tile
+// of query rows: it forms D for them (kept in the workspace for the second)
+// and walks the key tiles the mask leaves visible, accumulating dQ in
+// registers.  The second owns a tile of keys and walks the query tiles that
+// see them, accumulating dK and dV.  Everything is plain float32 FMAs on tiles
+// staged in LDS, the head dimension padded to a multiple of 4 with zeros
+// (which add exact zeros): 64 x 64 tiles with a 4 x 4 block of scores per
+// thread for d <= 128, 32 x 32 tiles with 2 x 2 up to d = 256.  Every output
+// is written once, so repeated calls give identical bits.
 #include "fa_launch.h"
 #include "fp32_tile.h"
 

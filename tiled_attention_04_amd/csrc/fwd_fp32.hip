@@ -1,7 +1,9 @@
-// Generic float32 forward: any head size 1 <= d <= 256 and any tile shape
-// from 1 x 1 to 64 x 64 (block_q query rows x block_k keys), including the
-// 4 x 4 tiles of the worked example ("FlashAttention Algorithm > Worked
-// Example", Setting Up the Example).
+// Generic float32 forward on the vector ALUs: any head size 1 <= d <= 256
+// and any tile shape from 1 x 1 to 64 x 64 (block_q query rows x block_k
+// keys), including the 4 x 4 tiles of the worked example ("FlashAttention
+// Algorithm > Worked Example", Setting Up the Example).  The automatic
+// float32 tile at d = 64 and 128 runs on the matrix cores instead
+// (fwd_fp32_mfma.hip).
 //
 // One workgroup owns one query tile and walks the key/value tiles the mask
 // leaves visible, keeping the running max m, running sum l and unnormalised
@@ -9,8 +11,7 @@
 // Pure NumPy", Architecture Overview and Step 2) for each of its rows; the
 // statistics move once per key tile of the caller's size, as the page's loop
 // does, so every tile shape gives the same result up to rounding.  The
-// arithmetic is plain float32 FMAs on LDS-staged tiles (the exactness path;
-// the 16-bit MFMA kernels are the fast path): the tiles sit in 64-row LDS
+// arithmetic is plain float32 FMAs on LDS-staged tiles: the tiles sit in 64-row LDS
 // buffers whatever the caller's tile, a 16 x 16 grid of threads holds 4 x 4
 // scores each, a row's max and sum are butterflies over its 16 lanes, and
 // the P V product accumulates one key at a time into registers.  Up to
