@@ -49,7 +49,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 STAGES = ("fwd", "window", "decode", "bwd", "paged", "fwd16", "decw", "bwdw", "dec16", "bwd16", "c2", "c2c")
 # The float32 path, timed only when named in --stages: the causal forward and
 # backward at the backward's shape (d = 128: the float32 MFMA kernels).
-OPT_STAGES = ("fwd32", "bwd32")
+OPT_STAGES = ("fwd32", "bwd32", "bwdr")
 PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense float32 MFMA
 W_DEC = 1024   # sliding window of the windowed decode stage
 W_BWD = 1024   # sliding window of the windowed backward stage
@@ -285,20 +285,26 @@ def main():
         q5, k5, v5, g5 = (t.to(dev) for t in attention_inputs(B5, H5, N5, d5, "bf16", seed=0, with_grad=True))
         o5, l5 = fa.fa_fwd(q5, k5, v5, causal=True)
         dq5, dk5, dv5 = (torch.empty(q5.shape, dtype=torch.float32, device=dev) for _ in range(3))
-        ws5 = torch.empty(fa.fa_bwd_workspace_size(B5, H5, N5, d5), dtype=torch.uint8, device=dev)
-
-    if "bwdw" in stages:
+    if "bwdw" in stages or "bwdr" in stages:
         if "bwd" not in stages:
             q5, k5, v5, g5 = (t.to(dev) for t in attention_inputs(B5, H5, N5, d5, "bf16", seed=0,
                                                                   with_grad=True))
+            o5, l5 = fa.fa_fwd(q5, k5, v5, causal=True)
             dq5, dk5, dv5 = (torch.empty(q5.shape, dtype=torch.float32, device=dev) for _ in range(3))
-            ws5 = torch.empty(fa.fa_bwd_workspace_size(B5, H5, N5, d5), dtype=torch.uint8, device=dev)
+    if "bwdw" in stages:
         o5w, l5w = fa.fa_fwd(q5, k5, v5, causal=True, window=W_BWD)
+    if any(s_ in stages for s_ in ("bwd", "bwdw", "bwd16", "bwdr")):
+        # The binding's default: dQ from the stored dS (0.54 GB of dS blocks for the causal
+        # backward, which also covers the windowed one); the opt-in stage bwdr times the
+        # recompute path with the minimum workspace.
+        ws5 = torch.empty(fa.fa_bwd_default_workspace_size(B5, H5, N5, d5, True, -1), dtype=torch.uint8,
+                          device=dev)
+        ws5r = torch.empty(fa.fa_bwd_workspace_size(B5, H5, N5, d5), dtype=torch.uint8, device=dev)
     if "bwd16" in stages:
         q9, k9, v9, g9 = (t.to(dev) for t in attention_inputs(B5, H5, N5, d5, "fp16", seed=0, with_grad=True))
         o9, l9 = fa.fa_fwd(q9, k9, v9, causal=True)
         dq9, dk9, dv9 = (torch.empty(q9.shape, dtype=torch.float32, device=dev) for _ in range(3))
-        ws9 = torch.empty(fa.fa_bwd_workspace_size(B5, H5, N5, d5), dtype=torch.uint8, device=dev)
+        ws9 = ws5
 
     if "fwd32" in stages or "bwd32" in stages:
         log("generating float32 inputs")
@@ -337,6 +343,8 @@ def main():
         "dec16": lambda: fa.fa_decode(q8, kc8, vc8, sl8, o=o8, lse=l8, workspace=ws8),
         "bwd16": lambda: fa.fa_bwd(q9, k9, v9, o9, g9, l9, causal=True, dq=dq9, dk=dk9, dv=dv9,
                                    workspace=ws9),
+        "bwdr": lambda: fa.fa_bwd(q5, k5, v5, o5, g5, l5, causal=True, dq=dq5, dk=dk5, dv=dv5,
+                                  workspace=ws5r),
         "c2": lambda: fa.fa_fwd_ex(q2, k2, v2, T2, T2, o=o2, lse=l2),
         "c2c": lambda: fa.fa_fwd_ex(q2, k2, v2, T2, T2, causal=True, o=o2c, lse=l2c),
         "fwd32": lambda: fa.fa_fwd(q10, k10, v10, causal=True, o=o10, lse=l10),
@@ -452,6 +460,8 @@ def main():
         hbm_stage("decode_fp16_s64_h32_d128_len512to8192", dec16_bytes, "dec16", "decode_fp16")
     if "bwd16" in ms:
         mfma_stage("bwd_causal_fp16_b2_h16_n4096_d128", flops5, "bwd16", "bwd_fp16")
+    if "bwdr" in ms:
+        mfma_stage("bwd_causal_recompute_dq_b2_h16_n4096_d128", flops5, "bwdr", None)
     # The small forward is cache-resident and launch-bound: reported as is,
     # not a roofline target.
     if "c2" in ms:

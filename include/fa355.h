@@ -370,9 +370,25 @@ fa_status fa_decode_check(const int32_t* seqlens, const int32_t* block_table, in
                           int max_pages, int num_pages, int window, int32_t* flags, void* stream);
 
 /*
- * fa_bwd_workspace_size -- bytes of workspace fa_bwd needs (0 if invalid).
+ * fa_bwd_workspace_size -- bytes of workspace fa_bwd needs (0 if invalid):
+ * D and L log2(e) of every query row (8 bytes per row).  With this much the
+ * 16-bit backward forms dQ by recomputing S and dP.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
+
+/*
+ * fa_bwd_workspace_size_ds -- bytes of workspace with which a 16-bit fa_bwd
+ * call (d in {64, 128}) forms dQ from a stored dS instead (0 if invalid):
+ * the above, 256-byte aligned, plus one 32 x 32 block of dS in the input type
+ * (2 KB) per (query block, key block) pair holding a visible (query, key)
+ * pair, per (batch, head) slice -- the lower triangle of blocks for causal
+ * attention, a band of ceil(W / 32) + 1 blocks per query block with a causal
+ * window of W keys, every block otherwise.  About B * H * N^2 bytes for
+ * causal attention (0.54 GB at B = 2, H = 16, N = 4096), so it is the
+ * caller's choice: fa_bwd takes this path whenever workspace_bytes is at
+ * least this size, unless fa_bwd_tune measured a recompute kernel faster.
+ */
+size_t fa_bwd_workspace_size_ds(int B, int H, int N, int d, int causal, int window);
 
 /*
  * fa_bwd -- backward pass that recomputes P from the stored L.
@@ -388,7 +404,9 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d);
  *   q, k, v, o, dO : [B, H, N, d] dtype (o and lse from fa_fwd)
  *   lse            : [B, H, N] float32
  *   dq, dk, dv     : [B, H, N, d] float32 outputs
- *   workspace      : >= fa_bwd_workspace_size(B, H, N, d) bytes
+ *   workspace      : >= fa_bwd_workspace_size(B, H, N, d) bytes; with
+ *                    >= fa_bwd_workspace_size_ds(...) bytes the 16-bit
+ *                    backward takes the stored-dS path (below)
  *
  * Supported: FA_BF16 and FA_FP16 with d in {64, 128}, and FA_FP32 with any
  * 1 <= d <= 256.  No atomics: dq, dk and dv are each written once, so
@@ -397,6 +415,19 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d);
  * accumulation): with FA_FP16 a |dP - D| above 65504 overflows, as for any
  * fp16 operand.  FA_FP32 keeps every step in float32 (float32 MFMA at
  * d = 64 and 128, vector-ALU FMAs at other d).
+ *
+ * How the 16-bit backward forms dQ (both ways give the same dv bits; dk and
+ * dq agree to rounding order, D being summed by another kernel and dq formed
+ * from the same terms in another order):
+ *  - recompute: a dQ kernel in the forward's loop order (a workgroup owns
+ *    query rows and walks the key tiles) recomputes S, P, dP and dS, and
+ *    also stores D and L log2(e) for the dK / dV kernel that follows; seven
+ *    matrix products per visible tile pair where the page's step has five;
+ *  - stored dS: a small kernel forms D and L log2(e), the dK / dV kernel
+ *    also writes each dS block it forms (rounded to the input type, as the
+ *    products use it) into the workspace, and a product kernel forms
+ *    dQ = scale * dS K from those blocks: five matrix products, plus one
+ *    write and one read of the visible dS blocks.
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
                  const float* lse, float* dq, float* dk, float* dv,
@@ -404,28 +435,30 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  void* workspace, size_t workspace_bytes, fa_dtype dtype, void* stream);
 
 /*
- * fa_bwd_tune -- measure the backward's two dQ kernels on this problem and
- * let later fa_bwd calls use the faster.
+ * fa_bwd_tune -- measure the backward's ways of forming dQ on this problem
+ * and let later fa_bwd calls use the fastest.
  *
- * dQ is formed by its own kernel, in the forward's loop order (a workgroup
- * owns query rows and walks the key tiles); it comes with 256 query rows per
- * workgroup (8 waves, two groups one phase apart, one workgroup per CU) or
- * 128 (4 waves, two workgroups per CU).  Which
- * is faster depends on how well each grid fills the chip, so the choice is
- * measured: the "profiling-driven auto-tuning" upgrade of "Build a
- * FlashAttention-2 Inference Kernel from Scratch in Pure Python", Extending
- * It.  The whole backward runs once to warm up and `reps` more times per
- * candidate between two HIP events on `stream`; times_ms[0] / [1] (if
- * non-NULL) get the mean ms per call with 128 / 256 rows and *best_dq_rows
- * (if non-NULL) the faster, remembered under (dtype, d, causal, window,
- * B * H, N).  On return dq, dk and dv hold the chosen kernel's result
- * (both give identical dk and dv, and form dq from the same terms in
- * the same order).
+ * Candidates (FA_BWD_TUNE_CANDIDATES, in this order): the recompute dQ kernel
+ * with 128 query rows per workgroup (4 waves, two workgroups per CU), with
+ * 256 (8 waves in two groups one phase apart, one workgroup per CU), and
+ * FA_BWD_DQ_STORED, dQ from the stored dS (tried only when workspace_bytes
+ * is at least fa_bwd_workspace_size_ds; its time is -1 otherwise).  Which is
+ * fastest depends on how well each grid fills the chip and on the mask, so
+ * the choice is measured: the "profiling-driven auto-tuning" upgrade of
+ * "Build a FlashAttention-2 Inference Kernel from Scratch in Pure Python",
+ * Extending It.  The whole backward runs once to warm up and `reps` more
+ * times per candidate between two HIP events on `stream`; times_ms[i] (if
+ * non-NULL, FA_BWD_TUNE_CANDIDATES floats) gets the mean ms per call and
+ * *best_dq_rows (if non-NULL) the fastest (128, 256 or FA_BWD_DQ_STORED),
+ * remembered under (dtype, d, causal, window, B * H, N).  On return dq, dk
+ * and dv hold the chosen way's result.
  *
  * Arguments as fa_bwd (16-bit types only: the float32 backward has one
  * kernel and returns FA_ERR_UNSUPPORTED), plus reps in [1, 1000].  Like
  * fa_fwd_tune it SYNCHRONISES `stream` and creates two HIP events.
  */
+#define FA_BWD_TUNE_CANDIDATES 3
+#define FA_BWD_DQ_STORED 1
 fa_status fa_bwd_tune(const void* q, const void* k, const void* v, const void* o, const void* dO,
                       const float* lse, float* dq, float* dk, float* dv,
                       int B, int H, int N, int d, float scale, int causal, int window,
@@ -433,13 +466,17 @@ fa_status fa_bwd_tune(const void* q, const void* k, const void* v, const void* o
                       int reps, int* best_dq_rows, float* times_ms);
 
 /*
- * The dQ kernel (query rows per workgroup, 128 or 256) an fa_bwd call uses
- * for this problem: the one fa_bwd_tune remembered (*tuned = 1), else the
- * built-in choice (*tuned = 0).  Returns 0 for invalid arguments and for
- * FA_FP32, whose backward has a single kernel.
+ * How an fa_bwd call with workspace_bytes of workspace forms dQ for this
+ * problem: 128 or 256 (the recompute kernel with that many query rows per
+ * workgroup) or FA_BWD_DQ_STORED.  The choice fa_bwd_tune remembered
+ * (*tuned = 1) when the workspace allows it; else (*tuned = 0) the stored dS
+ * when workspace_bytes >= fa_bwd_workspace_size_ds, else the recompute
+ * kernel whose grid fills the chip (256 rows once B * H * ceil(N / 256)
+ * reaches 256 workgroups, else 128).  Returns 0 for invalid arguments and for
+ * FA_FP32, whose backward has a single way.
  */
 int fa_bwd_auto_dq_rows(int B, int H, int N, int d, int causal, int window, fa_dtype dtype,
-                        int* tuned);
+                        size_t workspace_bytes, int* tuned);
 
 #ifdef __cplusplus
 }

@@ -196,7 +196,8 @@ def test_tune_table_export_import_round_trip(tmp_path, lib):
     assert fa355.fa_decode_auto_chunk(64, 32, 8192, 128) == (2048, True)
     assert fa355.fa_decode_auto_chunk(64, 32, 8192, 128, window=1024) == (512, False)
     assert fa355.fa_bwd_auto_dq_rows(2, 16, 4096, 128, causal=True) == (128, True)
-    assert fa355.fa_bwd_auto_dq_rows(2, 16, 4096, 128, causal=False) == (256, False)
+    assert fa355.fa_bwd_auto_dq_rows(2, 16, 4096, 128, causal=False) == (1, False)
+    assert fa355.fa_bwd_auto_dq_rows(2, 16, 4096, 128, causal=False, workspace_bytes=8) == (256, False)
     path = str(tmp_path / "tune.json")
     fa355.save_tuning(path)
     lib.fa_tune_reset()
@@ -254,9 +255,23 @@ def test_decode_and_bwd_tune_reject_bad_arguments(lib):
     assert fa355.fa_decode_auto_chunk(64, 32, 8192, 128) == (1024, False)
     assert fa355.fa_decode_auto_chunk(64, 32, 8192, 128, window=1024) == (512, False)
     assert fa355.fa_decode_auto_chunk(0, 32, 8192, 128)[0] == 0
-    assert fa355.fa_bwd_auto_dq_rows(2, 16, 4096, 128, causal=True) == (256, False)
-    assert fa355.fa_bwd_auto_dq_rows(1, 8, 1024, 64) == (128, False)
+    # the backward: dQ from the stored dS when the workspace holds it (as the binding's default
+    # does), else the recompute kernel whose grid fills the chip
+    assert fa355.fa_bwd_auto_dq_rows(2, 16, 4096, 128, causal=True) == (1, False)
+    small = fa355.fa_bwd_workspace_size(2, 16, 4096, 128)
+    big = fa355.fa_bwd_workspace_size_ds(2, 16, 4096, 128, True, -1)
+    assert fa355.fa_bwd_auto_dq_rows(2, 16, 4096, 128, causal=True, workspace_bytes=small) == (256, False)
+    assert fa355.fa_bwd_auto_dq_rows(2, 16, 4096, 128, causal=True, workspace_bytes=big - 1) == (256, False)
+    assert fa355.fa_bwd_auto_dq_rows(2, 16, 4096, 128, causal=True, workspace_bytes=big) == (1, False)
+    assert fa355.fa_bwd_auto_dq_rows(1, 8, 1024, 64, workspace_bytes=0) == (128, False)
+    assert fa355.fa_bwd_auto_dq_rows(1, 8, 1024, 64) == (1, False)
     assert fa355.fa_bwd_auto_dq_rows(1, 8, 1024, 64, dtype=torch.float32)[0] == 0
+    # a tuned stored-dS choice needs the workspace for it
+    fa355.fa_tune_import([dict(kind=fa355.TUNE_KINDS["bwd_dq_rows"], dtype=1, d=128, causal=1, window=-1,
+                               rows=32, n=4096, value=1)])
+    assert fa355.fa_bwd_auto_dq_rows(2, 16, 4096, 128, causal=True) == (1, True)
+    assert fa355.fa_bwd_auto_dq_rows(2, 16, 4096, 128, causal=True, workspace_bytes=small) == (256, False)
+    lib.fa_tune_reset()
 
 
 def test_decode_paged_rejects_bad_arguments(lib):
@@ -318,3 +333,27 @@ def test_workspace_sizes(lib):
     # backward: D and L (log2 units) per row
     assert fa355.fa_bwd_workspace_size(2, 16, 4096, 128) == 2 * 16 * 4096 * 2 * 4
     assert fa355.fa_bwd_workspace_size(0, 16, 4096, 128) == 0
+    # stored dS: that (256-byte aligned), then a 2 KB block per visible (32-query, 32-key) block pair
+    rows = 2 * 16 * 4096
+    nb = 4096 // 32
+    tri = nb * (nb + 1) // 2
+    assert fa355.fa_bwd_workspace_size_ds(2, 16, 4096, 128, True, -1) == rows * 8 + 32 * tri * 2048
+    assert fa355.fa_bwd_workspace_size_ds(2, 16, 4096, 64, False, -1) == rows * 8 + 32 * nb * nb * 2048
+    assert fa355.fa_bwd_workspace_size_ds(2, 16, 4096, 128, False, 100) == rows * 8 + 32 * nb * nb * 2048
+    # a causal window of W keys: ceil(W / 32) + 1 blocks per query block (33 for W = 1024)
+    assert fa355.fa_bwd_workspace_size_ds(2, 16, 4096, 128, True, 1024) == rows * 8 + 32 * nb * 33 * 2048
+    assert fa355.fa_bwd_workspace_size_ds(2, 16, 4096, 128, True, 1000) == rows * 8 + 32 * nb * 33 * 2048
+    assert fa355.fa_bwd_workspace_size_ds(2, 16, 4096, 128, True, 0) == rows * 8 + 32 * nb * 1 * 2048
+    # a window over the whole slice: the triangle
+    assert fa355.fa_bwd_workspace_size_ds(2, 16, 4096, 128, True, 5000) == rows * 8 + 32 * tri * 2048
+    # ragged: D and L of 3 * 100 rows take 2400 bytes, padded to 2560
+    assert fa355.fa_bwd_workspace_size_ds(1, 3, 100, 64, True, -1) == 2560 + 3 * 10 * 2048
+    assert fa355.fa_bwd_workspace_size_ds(2, 16, 4096, 96, True, -1) == 0
+    assert fa355.fa_bwd_workspace_size_ds(0, 16, 4096, 128, True, -1) == 0
+    assert fa355.fa_bwd_workspace_size_ds(2, 16, 4096, 128, 2, -1) == 0
+    assert fa355.fa_bwd_workspace_size_ds(2, 16, 4096, 128, True, -2) == 0
+    # the binding allocates the stored-dS workspace up to its cap, else the minimum
+    assert fa355.fa_bwd_default_workspace_size(2, 16, 4096, 128, True) == rows * 8 + 32 * tri * 2048
+    assert fa355.fa_bwd_default_workspace_size(2, 16, 4096, 128, True, stored_ds=False) == rows * 8
+    assert fa355.fa_bwd_default_workspace_size(2, 16, 4096, 128, True, dtype=torch.float32) == rows * 8
+    assert fa355.fa_bwd_default_workspace_size(1, 32, 65536, 128, True) == 32 * 65536 * 8

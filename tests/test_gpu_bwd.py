@@ -19,20 +19,28 @@ def _gpu():
     need_gpu()
 
 
-def run(q, k, v, dO, causal, window=-1, scale=None):
+def run(q, k, v, dO, causal, window=-1, scale=None, stored_ds=None):
+    """fa_fwd then fa_bwd; stored_ds: dQ from the stored dS (True), by the
+    recompute kernels (False), or the binding's default workspace (None,
+    which stores dS at these sizes)."""
     qd, kd, vd, gd = (t.cuda() for t in (q, k, v, dO))
     o, lse = fa.fa_fwd(qd, kd, vd, causal=causal, window=window, scale=scale)
-    dq, dk, dv = fa.fa_bwd(qd, kd, vd, o, gd, lse, causal=causal, window=window, scale=scale)
+    dq, dk, dv = fa.fa_bwd(qd, kd, vd, o, gd, lse, causal=causal, window=window, scale=scale,
+                           stored_ds=stored_ds)
     torch.cuda.synchronize()
     return dq.cpu(), dk.cpu(), dv.cpu()
 
 
+STORED = pytest.mark.parametrize("stored_ds", [True, False], ids=["stored_ds", "recompute"])
+
+
+@STORED
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", [1, 64, 200, 257])
 @pytest.mark.parametrize("causal,window", [(False, -1), (True, -1), (True, 45), (False, 30)])
-def test_small_shapes(d, N, causal, window):
+def test_small_shapes(d, N, causal, window, stored_ds):
     q, k, v, dO = attention_inputs(1, 2, N, d, "bf16", seed=N + d, with_grad=True)
-    dq, dk, dv = run(q, k, v, dO, causal, window)
+    dq, dk, dv = run(q, k, v, dO, causal, window, stored_ds=stored_ds)
     s = 1 / math.sqrt(d)
     rq, rk, rv = oracle.attention_bwd_ref(q, k, v, dO, s, causal, window)
     check_bf16(dq, rq, "dQ")
@@ -64,11 +72,12 @@ def test_gradient_identities_on_gpu():
 
 
 @pytest.mark.slow
-def test_full_size_sampled_heads():
+@STORED
+def test_full_size_sampled_heads(stored_ds):
     """B=2, H=16, N=4096, d=128, causal: two whole heads against the oracle."""
     w = WORKLOADS["bwd_b2_h16_n4096_d128_bf16"]
     q, k, v, dO = attention_inputs(w["B"], w["H"], w["N"], w["d"], "bf16", seed=0, with_grad=True)
-    dq, dk, dv = run(q, k, v, dO, True)
+    dq, dk, dv = run(q, k, v, dO, True, stored_ds=stored_ds)
     s = 1 / math.sqrt(128)
     for b, h in ((0, 0), (1, 9)):
         rq, rk, rv = oracle.attention_bwd_ref(q[b, h][None], k[b, h][None], v[b, h][None],
@@ -79,12 +88,13 @@ def test_full_size_sampled_heads():
 
 
 @pytest.mark.slow
-def test_full_size_window_sampled_heads():
+@STORED
+def test_full_size_window_sampled_heads(stored_ds):
     """The windowed backward stage the bench times: B=2, H=16, N=4096, d=128,
     causal with a 1024-token window; two whole heads against the oracle."""
     w = WORKLOADS["bwd_b2_h16_n4096_d128_bf16"]
     q, k, v, dO = attention_inputs(w["B"], w["H"], w["N"], w["d"], "bf16", seed=0, with_grad=True)
-    dq, dk, dv = run(q, k, v, dO, True, 1024)
+    dq, dk, dv = run(q, k, v, dO, True, 1024, stored_ds=stored_ds)
     s = 1 / math.sqrt(128)
     for b, h in ((0, 3), (1, 15)):
         rq, rk, rv = oracle.attention_bwd_ref(q[b, h][None], k[b, h][None], v[b, h][None],
@@ -94,34 +104,55 @@ def test_full_size_window_sampled_heads():
         check_bf16(dv[b, h], rv[0], f"dV[{b},{h}]")
 
 
+@STORED
 @pytest.mark.parametrize("B,H,N,d", [(1, 3, 700, 128), (1, 2, 1100, 64)])
-@pytest.mark.parametrize("causal,window", [(False, -1), (True, -1), (True, 100), (False, 50)])
-def test_several_tiles_ragged(B, H, N, d, causal, window):
-    """Several 128-key and 128-query tiles of both kernels, a ragged tail."""
+@pytest.mark.parametrize("causal,window", [(False, -1), (True, -1), (True, 100), (False, 50), (True, 0),
+                                           (True, 31), (True, 32), (True, 5000)])
+def test_several_tiles_ragged(B, H, N, d, causal, window, stored_ds):
+    """Several 128-key and 128-query tiles of every kernel, a ragged tail;
+    windows at and around the 32-key block edges of the stored dS band, and
+    one longer than the sequence."""
     q, k, v, dO = attention_inputs(B, H, N, d, "bf16", seed=N + 7 * d, with_grad=True)
-    dq, dk, dv = run(q, k, v, dO, causal, window)
+    dq, dk, dv = run(q, k, v, dO, causal, window, stored_ds=stored_ds)
     rq, rk, rv = oracle.attention_bwd_ref(q, k, v, dO, 1 / math.sqrt(d), causal, window)
     check_bf16(dq, rq, "dQ")
     check_bf16(dk, rk, "dK")
     check_bf16(dv, rv, "dV")
 
 
-def test_backward_is_deterministic():
+@STORED
+def test_backward_is_deterministic(stored_ds):
     """No atomics: two calls on the same inputs give identical bits."""
     q, k, v, dO = attention_inputs(2, 4, 515, 128, "bf16", seed=3, with_grad=True)
-    a = run(q, k, v, dO, True)
-    b = run(q, k, v, dO, True)
+    a = run(q, k, v, dO, True, stored_ds=stored_ds)
+    b = run(q, k, v, dO, True, stored_ds=stored_ds)
     for x, y, name in zip(a, b, ("dQ", "dK", "dV")):
         assert torch.equal(x, y), name
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal,window", [(False, -1), (True, -1), (True, 70), (False, 90)])
+def test_stored_and_recomputed_dq_agree(d, causal, window):
+    """The two ways of forming dQ share the dK / dV kernel: dV has the same
+    bits (it depends on L only), dK and dQ agree to rounding order (D is
+    summed by another kernel, dQ from the same rounded dS terms)."""
+    q, k, v, dO = attention_inputs(1, 3, 333, d, "bf16", seed=5 + d, with_grad=True)
+    a = run(q, k, v, dO, causal, window, stored_ds=True)
+    b = run(q, k, v, dO, causal, window, stored_ds=False)
+    assert torch.equal(a[2], b[2])
+    for x, y, name in zip(a[:2], b[:2], ("dQ", "dK")):
+        assert torch.allclose(x, y, rtol=1e-3, atol=1e-3), name
+
+
+@STORED
 @pytest.mark.parametrize("B,H,N,d", [(1, 64, 1100, 128), (1, 128, 600, 64)])
 @pytest.mark.parametrize("causal,window", [(False, -1), (True, -1), (True, 300), (False, 200)])
-def test_many_heads_256_row_dq_tiles(B, H, N, d, causal, window):
+def test_many_heads_256_row_dq_tiles(B, H, N, d, causal, window, stored_ds):
     """Enough (head, 256-row tile) pairs to fill the chip, which selects the
-    256-row dQ kernel; ragged tails; sampled heads against the oracle."""
+    256-row recompute dQ kernel (or, with the stored dS, many product
+    workgroups); ragged tails; sampled heads against the oracle."""
     q, k, v, dO = attention_inputs(B, H, N, d, "bf16", seed=N + d + H, with_grad=True)
-    dq, dk, dv = run(q, k, v, dO, causal, window)
+    dq, dk, dv = run(q, k, v, dO, causal, window, stored_ds=stored_ds)
     s = 1 / math.sqrt(d)
     for h in (0, H // 2 + 5, H - 1):
         rq, rk, rv = oracle.attention_bwd_ref(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1],
@@ -131,15 +162,16 @@ def test_many_heads_256_row_dq_tiles(B, H, N, d, causal, window):
         check_bf16(dv[:, h:h + 1], rv, f"dV[h={h}]")
 
 
+@STORED
 @pytest.mark.parametrize("N,d", [(65, 128), (300, 64)])
-def test_outputs_written_only_in_bounds(N, d):
+def test_outputs_written_only_in_bounds(N, d, stored_ds):
     """Guard bands after dq, dk, dv and the workspace stay untouched."""
     B, H = 1, 2
     q, k, v, dO = (t.cuda() for t in attention_inputs(B, H, N, d, "bf16", seed=N, with_grad=True))
     o, lse = fa.fa_fwd(q, k, v, causal=True)
     n = B * H * N * d
     bufs = [torch.full((n + 4096,), 7.0, dtype=torch.float32, device="cuda") for _ in range(3)]
-    need = fa.fa_bwd_workspace_size(B, H, N, d)
+    need = (fa.fa_bwd_workspace_size_ds(B, H, N, d, True, -1) if stored_ds else fa.fa_bwd_workspace_size(B, H, N, d))
     wbuf = torch.full((need // 4 + 4096,), 7.0, dtype=torch.float32, device="cuda")
     dq, dk, dv = (b[:n].view(B, H, N, d) for b in bufs)
     fa.fa_bwd(q, k, v, o, dO, lse, causal=True, dq=dq, dk=dk, dv=dv, workspace=wbuf[:need // 4])

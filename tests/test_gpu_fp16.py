@@ -73,14 +73,15 @@ def test_fp16_masked_positions_contribute_exactly_zero():
     assert torch.equal(o1[:, :, :r], o2[:, :, :r]) and torch.equal(l1[:, :, :r], l2[:, :, :r])
 
 
+@pytest.mark.parametrize("stored_ds", [True, False], ids=["stored_ds", "recompute"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", [64, 257])
 @pytest.mark.parametrize("causal,window", [(False, -1), (True, -1), (True, 45)])
-def test_fp16_backward(d, N, causal, window):
+def test_fp16_backward(d, N, causal, window, stored_ds):
     q, k, v, dO = attention_inputs(1, 2, N, d, "fp16", seed=N + d, with_grad=True)
     qd, kd, vd, gd = (t.cuda() for t in (q, k, v, dO))
     o, lse = fa.fa_fwd(qd, kd, vd, causal=causal, window=window)
-    dq, dk, dv = fa.fa_bwd(qd, kd, vd, o, gd, lse, causal=causal, window=window)
+    dq, dk, dv = fa.fa_bwd(qd, kd, vd, o, gd, lse, causal=causal, window=window, stored_ds=stored_ds)
     torch.cuda.synchronize()
     rq, rk, rv = oracle.attention_bwd_ref(q, k, v, dO, 1 / math.sqrt(d), causal, window)
     check_bf16(dq.cpu(), rq, "dQ")
@@ -88,12 +89,14 @@ def test_fp16_backward(d, N, causal, window):
     check_bf16(dv.cpu(), rv, "dV")
 
 
-def test_fp16_backward_many_tiles():
-    """Enough heads that the 256-row dQ kernel is chosen (grid fills the chip)."""
+@pytest.mark.parametrize("stored_ds", [True, False], ids=["stored_ds", "recompute"])
+def test_fp16_backward_many_tiles(stored_ds):
+    """Enough heads that the 256-row recompute dQ kernel is chosen (grid fills
+    the chip) when dS is not stored."""
     q, k, v, dO = attention_inputs(2, 64, 600, 128, "fp16", seed=2, with_grad=True)
     qd, kd, vd, gd = (t.cuda() for t in (q, k, v, dO))
     o, lse = fa.fa_fwd(qd, kd, vd, causal=True)
-    dq, dk, dv = fa.fa_bwd(qd, kd, vd, o, gd, lse, causal=True)
+    dq, dk, dv = fa.fa_bwd(qd, kd, vd, o, gd, lse, causal=True, stored_ds=stored_ds)
     torch.cuda.synchronize()
     for b, h in [(0, 0), (1, 63)]:
         rq, rk, rv = oracle.attention_bwd_ref(q[b, h][None], k[b, h][None], v[b, h][None],

@@ -41,7 +41,8 @@ def test_captured_step_replays_match_eager_calls():
 
     o, lse = torch.empty_like(q), torch.empty((B, H, N), dtype=torch.float32, device=dev)
     dq, dk, dv = (torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3))
-    ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device=dev)
+    # the stored-dS backward, as the eager call below (the binding's default at this size)
+    ws = torch.empty(fa.fa_bwd_workspace_size_ds(B, H, N, d, True, -1), dtype=torch.uint8, device=dev)
     o32, lse32 = torch.empty_like(q32), torch.empty((1, 2, 300), dtype=torch.float32, device=dev)
     dq32, dk32, dv32 = (torch.empty_like(q32) for _ in range(3))
     ws32 = torch.empty(fa.fa_bwd_workspace_size(1, 2, 300, 64), dtype=torch.uint8, device=dev)

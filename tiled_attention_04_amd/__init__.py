@@ -22,6 +22,10 @@ from .fa355 import (  # noqa: F401
     fa_bwd_auto_dq_rows,
     fa_bwd_tune,
     fa_bwd_workspace_size,
+    fa_bwd_workspace_size_ds,
+    fa_bwd_default_workspace_size,
+    BWD_DS_WORKSPACE_CAP,
+    FA_BWD_DQ_STORED,
     fa_decode,
     fa_decode_auto_chunk,
     fa_decode_check,

@@ -122,9 +122,15 @@ int auto_decode_chunk(fa_dtype dtype, int d, int window, int S, int H, int Lmax)
   return t != 0 ? t : fa::decode_auto_chunk(S, H, Lmax, window);
 }
 
-int auto_dq_rows(fa_dtype dtype, int d, int causal, int window, int B, int H, int N) {
+// How an fa_bwd call forms dQ: the tuned choice, else from the stored dS
+// whenever the workspace holds it, else the recompute kernel the heuristic
+// picks (also when the tuned choice is the stored dS but the workspace is
+// too small for it).
+int auto_dq_rows(fa_dtype dtype, int d, int causal, int window, int B, int H, int N, size_t workspace_bytes) {
+  const bool room = workspace_bytes >= fa::bwd_workspace_bytes_ds(B, H, N, d, fa::Mask{causal, window});
   const int t = tuned_value(tune_key(kTuneBwd, dtype, d, causal, window, (long long)B * H, N));
-  return t != 0 ? t : fa::bwd_auto_dq_rows(B, H, N);
+  if (t == 128 || t == 256 || (t == fa::kDqStored && room)) return t;
+  return room ? fa::kDqStored : fa::bwd_auto_dq_rows(B, H, N);
 }
 
 // One timing loop of a tuning call: a warm-up launch, then reps launches
@@ -229,6 +235,8 @@ fa_status check_bwd(const void* q, const void* k, const void* v, const void* o, 
 }  // namespace
 
 extern "C" {
+
+static_assert(fa::kDqStored == FA_BWD_DQ_STORED, "stored-dS choice code");
 
 int fa_version(void) { return 100; }
 
@@ -466,7 +474,7 @@ fa_status fa_tune_import(const int64_t* rows, int n_rows) {
       for (int c : kDecodeTuneChunks) ok_value |= r[7] == c;
       ok_value &= r[3] == 0;
     } else if (r[0] == FA_TUNE_BWD_DQ_ROWS) {
-      ok_value = r[7] == 128 || r[7] == 256;
+      ok_value = r[7] == 128 || r[7] == 256 || r[7] == FA_BWD_DQ_STORED;
     }
     if (!ok_value || (r[1] != FA_BF16 && r[1] != FA_FP16) || (r[2] != 64 && r[2] != 128) ||
         (r[3] != 0 && r[3] != 1) || r[4] < -1 || r[4] > INT_MAX || r[5] <= 0 || r[5] > INT_MAX ||
@@ -586,6 +594,11 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
   return fa::bwd_workspace_bytes(B, H, N, d);
 }
 
+size_t fa_bwd_workspace_size_ds(int B, int H, int N, int d, int causal, int window) {
+  if (check_dense(B, H, N, d, 0.f, causal, window, FA_BF16) != FA_OK || (d != 64 && d != 128)) return 0;
+  return fa::bwd_workspace_bytes_ds(B, H, N, d, fa::Mask{causal, window});
+}
+
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
                  const float* lse, float* dq, float* dk, float* dv, int B, int H, int N, int d,
                  float scale, int causal, int window, void* workspace, size_t workspace_bytes,
@@ -601,7 +614,8 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   }
   return done(fa::launch_bwd_mfma(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale,
                                   fa::Mask{causal, window}, workspace, dtype == FA_FP16,
-                                  auto_dq_rows(dtype, d, causal, window, B, H, N), (hipStream_t)stream),
+                                  auto_dq_rows(dtype, d, causal, window, B, H, N, workspace_bytes),
+                                  (hipStream_t)stream),
               "fa_bwd");
 }
 
@@ -619,10 +633,15 @@ fa_status fa_bwd_tune(const void* q, const void* k, const void* v, const void* o
   EventPair evs;
   if (evs.err != hipSuccess) return done(evs.err, "fa_bwd_tune (event)");
   hipError_t err = hipSuccess;
-  const int cand[2] = {128, 256};
+  const int cand[FA_BWD_TUNE_CANDIDATES] = {128, 256, fa::kDqStored};
+  const bool room = workspace_bytes >= fa::bwd_workspace_bytes_ds(B, H, N, d, mask);
   float best_ms = 0.f;
   int best = 0;
-  for (int i = 0; i < 2 && err == hipSuccess; ++i) {
+  for (int i = 0; i < FA_BWD_TUNE_CANDIDATES && err == hipSuccess; ++i) {
+    if (cand[i] == fa::kDqStored && !room) {
+      if (times_ms) times_ms[i] = -1.f;
+      continue;
+    }
     const float ms = time_launches(evs.ev[0], evs.ev[1], s, reps, err, [&] {
       return fa::launch_bwd_mfma(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, mask, workspace,
                                  dtype == FA_FP16, cand[i], s);
@@ -641,17 +660,16 @@ fa_status fa_bwd_tune(const void* q, const void* k, const void* v, const void* o
               "fa_bwd_tune");
 }
 
-int fa_bwd_auto_dq_rows(int B, int H, int N, int d, int causal, int window, fa_dtype dtype, int* tuned) {
+int fa_bwd_auto_dq_rows(int B, int H, int N, int d, int causal, int window, fa_dtype dtype,
+                        size_t workspace_bytes, int* tuned) {
   if (tuned) *tuned = 0;
   if (check_dense(B, H, N, d, 0.f, causal, window, dtype) != FA_OK || dtype == FA_FP32 ||
       (d != 64 && d != 128))
     return 0;
+  const int choice = auto_dq_rows(dtype, d, causal, window, B, H, N, workspace_bytes);
   const int t = tuned_value(tune_key(kTuneBwd, dtype, d, causal, window, (long long)B * H, N));
-  if (t != 0) {
-    if (tuned) *tuned = 1;
-    return t;
-  }
-  return fa::bwd_auto_dq_rows(B, H, N);
+  if (tuned) *tuned = t != 0 && t == choice;
+  return choice;
 }
 
 }  // extern "C"

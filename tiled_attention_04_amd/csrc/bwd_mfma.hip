@@ -28,6 +28,50 @@ namespace {
 
 constexpr int kBKV = 128;  // keys per dK / dV workgroup
 
+// Where the dK / dV kernel leaves dS for the dQ product: one 32 x 32 block
+// (2 KB) per (query block qb, key block kb) that holds a visible pair, at
+// block index ds_block(qb, kb) of its (batch, head) slice:
+//  * mode 1, causal without a window: the lower triangle, qb (qb + 1) / 2 + kb;
+//  * mode 2, causal with a window of W keys: a band of A + 1 blocks per
+//    query block, A = ceil(W / 32), slot kb - qb + A (kb >= qb - A for every
+//    visible block);
+//  * mode 0, otherwise: every block, qb nb + kb.
+struct DsLayout {
+  int mode;
+  int nb;              // 32-row blocks per slice
+  int A;               // band: ceil(window / 32)
+  int width;           // band: blocks per query block
+  long long per_head;  // blocks per slice
+};
+
+__host__ __device__ __forceinline__ long long ds_block(const DsLayout& L, int qb, int kb) {
+  return L.mode == 1   ? (long long)qb * (qb + 1) / 2 + kb
+         : L.mode == 2 ? (long long)qb * L.width + kb - qb + L.A
+                       : (long long)qb * L.nb + kb;
+}
+
+// Byte offset of the dS blocks in the workspace: after D and L2 (two floats
+// per query row), 256-byte aligned.
+size_t ds_offset(long long rows) { return ((size_t)rows * 8u + 255u) / 256u * 256u; }
+
+DsLayout ds_layout(int N, int causal, int window) {
+  DsLayout L{};
+  L.nb = (N + 31) / 32;
+  if (causal && (window < 0 || (window + 31) / 32 >= L.nb)) {  // a window over the whole slice: triangle
+    L.mode = 1;
+    L.per_head = (long long)L.nb * (L.nb + 1) / 2;
+  } else if (causal) {
+    L.mode = 2;
+    L.A = (window + 31) / 32;
+    L.width = L.A + 1;
+    L.per_head = (long long)L.nb * L.width;
+  } else {
+    L.mode = 0;
+    L.per_head = (long long)L.nb * L.nb;
+  }
+  return L;
+}
+
 
 // dK / dV kernel with four waves and two workgroups per CU.  A workgroup owns
 // 128 keys, 32 per wave, and walks the query tiles that see them 32 queries
@@ -70,12 +114,12 @@ __device__ __forceinline__ uint32_t block_src_rows(int blk, int lane, int pitch,
   return row < rows && col < D * 2 ? (uint32_t)(row * D * 2 + col) : 0x80000000u;
 }
 
-template <typename T, int D>
+template <typename T, int D, bool DS>
 __global__ __launch_bounds__(kKv4Threads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_kv4_kernel(const T* __restrict__ q, const T* __restrict__ k,
                     const T* __restrict__ v, const T* __restrict__ dO,
                     const float* __restrict__ Dv, const float* __restrict__ L2,
-                    float* __restrict__ dk, float* __restrict__ dv,
+                    float* __restrict__ dk, float* __restrict__ dv, T* __restrict__ dsw, DsLayout lay,
                     int BH, int N, int nkt, float scale, float scale_log2, int causal, int window) {
   using TL = Kv4Tile<D>;
   constexpr int NW = kKv4Threads / 64;  // 4
@@ -179,6 +223,19 @@ void bwd_kv4_kernel(const T* __restrict__ q, const T* __restrict__ k,
   const int k_rd = (32 * w + l32) * KP + 16 * h;   // B operands of S (K rows)
   const int tr_q = tr_addr<QP>(lane);              // B operands of dV / dK
 
+  // With DS each step's dS block is stored at the start of the next step,
+  // so that the stores complete during a whole step of work instead of
+  // holding up the step's closing wait.
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  uint32_t dpend[8];
+  char* pend = nullptr;
+  auto store_pending = [&] __device__ () {
+    if (pend) {
+      __builtin_nontemporal_store(u32x4{dpend[0], dpend[1], dpend[2], dpend[3]}, (u32x4*)(pend + l32 * 64 + h * 32));
+      __builtin_nontemporal_store(u32x4{dpend[4], dpend[5], dpend[6], dpend[7]},
+                                  (u32x4*)(pend + l32 * 64 + h * 32 + 16));
+    }
+  };
   auto tile = [&] __device__ (auto stage, int qt) {
     constexpr int ST = decltype(stage)::value;
     const char* Qs = stage_q(stage);
@@ -186,6 +243,10 @@ void bwd_kv4_kernel(const T* __restrict__ q, const T* __restrict__ k,
     const float* LD = stage_ld(stage);
     const int q0 = qt * kKv4BQ;
     if (qt + 1 < qt1) load_qtile(qt + 1, integral_constant<int, ST ^ 1>{});
+    if constexpr (DS) {
+      store_pending();
+      pend = nullptr;
+    }
     const bool act = wk0 <= wk1 && !(causal && wk0 > q0 + kKv4BQ - 1) && !(window >= 0 && wk1 < q0 - window);
     if (act) {
       const bool need_mask = (causal && wk0 + 31 > q0) || (window >= 0 && q0 + kKv4BQ - 1 - wk0 > window) ||
@@ -225,6 +286,16 @@ void bwd_kv4_kernel(const T* __restrict__ q, const T* __restrict__ k,
       uint32_t ppk[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) ppk[j] = pack2<T>(pv[2 * j], pv[2 * j + 1]);
+      uint32_t dspk[8];
+      auto form_ds = [&] __device__ () {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 D4 = *(const float4*)(LD + 64 + 8 * g + 4 * h);
+          dspk[2 * g] = pack2<T>(pv[4 * g] * (dpacc[4 * g] - D4.x), pv[4 * g + 1] * (dpacc[4 * g + 1] - D4.y));
+          dspk[2 * g + 1] = pack2<T>(pv[4 * g + 2] * (dpacc[4 * g + 2] - D4.z),
+                                      pv[4 * g + 3] * (dpacc[4 * g + 3] - D4.w));
+        }
+      };
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const vec8<T> pa = as_vec8<T>(uint4{ppk[4 * s], ppk[4 * s + 1], ppk[4 * s + 2], ppk[4 * s + 3]});
@@ -232,13 +303,16 @@ void bwd_kv4_kernel(const T* __restrict__ q, const T* __restrict__ k,
         for (int c = 0; c < CB; ++c)
           dv_acc[c] = mfma32(pa, read_tr8<QP, T>(Os + tr_q + 16 * s * QP + 64 * c), dv_acc[c]);
       }
-      uint32_t dspk[8];
+      form_ds();
+      if constexpr (DS) {
+        // The block is stored at the start of the next step.  The 32 x 32 dS
+        // block of (query block qt, this wave's key block) is row-major by
+        // key: the lane's 16 values are slots 16 h .. 16 h + 15 of its key's
+        // row (slot 16 h + r holds query c_row(r, h)).  Written once and read
+        // once by the next kernel: non-temporal stores.
+        pend = (char*)(dsw + ((size_t)bh * (size_t)lay.per_head + (size_t)ds_block(lay, qt, wk0 >> 5)) * 1024);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 D4 = *(const float4*)(LD + 64 + 8 * g + 4 * h);
-        dspk[2 * g] = pack2<T>(pv[4 * g] * (dpacc[4 * g] - D4.x), pv[4 * g + 1] * (dpacc[4 * g + 1] - D4.y));
-        dspk[2 * g + 1] = pack2<T>(pv[4 * g + 2] * (dpacc[4 * g + 2] - D4.z),
-                                    pv[4 * g + 3] * (dpacc[4 * g + 3] - D4.w));
+        for (int j = 0; j < 8; ++j) dpend[j] = dspk[j];
       }
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -248,8 +322,8 @@ void bwd_kv4_kernel(const T* __restrict__ q, const T* __restrict__ k,
           dk_acc[c] = mfma32(da, read_tr8<QP, T>(Qs + tr_q + 16 * s * QP + 64 * c), dk_acc[c]);
       }
     }
-    // The next tile's direct loads have landed; after the barrier no wave
-    // reads this stage any more.
+    // The next tile's direct loads have landed (and, with DS, this step's
+    // dS stores); after the barrier no wave reads this stage any more.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
@@ -260,6 +334,7 @@ void bwd_kv4_kernel(const T* __restrict__ q, const T* __restrict__ k,
     tile(integral_constant<int, 1>{}, qt + 1);
   }
 
+  if constexpr (DS) store_pending();
   // dK = scale * dS^T Q, dV = P^T dO for this wave's keys; rows past N fall
   // outside the buffers and are dropped.
   const rsrc_t dk_dst = make_rsrc(dk + base, (uint32_t)N * D * 4u);
@@ -814,6 +889,261 @@ void bwd_dq_pp_kernel(const T* __restrict__ q, const T* __restrict__ k,
   row_constants_store(Dv, L2, (size_t)bh * N + qi, row_ok, h, Di, Li);
 }
 
+
+// D = rowsum(dO * O) and L2 = L log2(e) (+inf for a row without visible keys)
+// of every query row, for the stored-dS backward (whose dK / dV kernel runs
+// first): 8 lanes of 16 bytes per 64 columns, D / 8 lanes per row.
+constexpr int kPreThreads = 256;
+
+template <typename T, int D>
+__global__ __launch_bounds__(kPreThreads)
+void bwd_pre_kernel(const T* __restrict__ o, const T* __restrict__ dO, const float* __restrict__ lse,
+                    float* __restrict__ Dv, float* __restrict__ L2, long long rows) {
+  constexpr int LPR = D / 8;                   // lanes per row
+  constexpr int RPB = kPreThreads / LPR;       // rows per workgroup
+  const int t = threadIdx.x;
+  const long long row = (long long)blockIdx.x * RPB + t / LPR;
+  const int part = t % LPR;
+  float p = 0.f;
+  if (row < rows) {  // each element is read once: non-temporal loads
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const uint4 a = __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4*)(o + (size_t)row * D + 8 * part)));
+    const uint4 b = __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4*)(dO + (size_t)row * D + 8 * part)));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p = __builtin_fmaf(lo16<T>(word(a, i)), lo16<T>(word(b, i)), p);
+      p = __builtin_fmaf(hi16<T>(word(a, i)), hi16<T>(word(b, i)), p);
+    }
+  }
+  p = group_sum<LPR>(p);
+  if (row < rows && part == 0) {
+    const float L = lse[row];
+    Dv[row] = p;
+    L2[row] = L == kNegInf ? __builtin_inff() : L * kLog2e;
+  }
+}
+
+// dQ = scale * dS K from the dS blocks the dK / dV kernel stored: the
+// product of "Building Flash Attention from Scratch in Pure NumPy", Step 4,
+// with nothing recomputed.  Four waves own 128 query rows (32 each) and walk
+// the key blocks their rows see 32 keys at a time.  The kernel streams the
+// dS blocks once from HBM, so what sets its pace is how many bytes are in
+// flight: each wave keeps its next eight 2 KB dS blocks in flight in
+// registers (64 per lane), and the workgroup's K rows (read by every query
+// tile of the slice, mostly from L2) come through a ring of eight LDS stages
+// by direct loads.  (Loads retire in issue order, so the dS loads run no
+// further ahead than the K stages: a wait for step i's K rows also waits for
+// every dS load issued before them.)  Per step a wave copies its dS block into its own 2 KB of
+// LDS and forms
+//   dQ^T += K^T dS^T
+// with K^T and dS^T both from transpose reads (the dS block is row-major by
+// key, so its transpose reads give the queries as the accumulator's
+// columns).  A wave skips the blocks that hold no pair visible to its rows
+// (the dK / dV kernel never wrote them).
+constexpr int kDsThreads = 256;
+constexpr int kDsStages = 8;  // K stages, and dS blocks in flight per wave
+
+// The K rows of one 32-key step, unpadded (2 D bytes per row, 32 rows = 2 D
+// direct-load blocks of 1 KB), with the 16-byte chunks of each row permuted
+// by an XOR with a function of the row, so that the transpose reads of four
+// consecutive rows hit distinct LDS banks (unpadded rows 256 or 128 bytes
+// apart would all start on the same bank).  8 KB per stage at d = 128, so
+// that eight stages fit two workgroups per CU.
+template <int D>
+struct DsTile {
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kKBytes = 32 * kRowBytes;
+  static constexpr int kKBlocks = kKBytes / 1024;
+  static constexpr int kKPer = kKBlocks / 4;  // direct loads per wave and step
+  static_assert(kKBlocks % 4 == 0, "K blocks per wave");
+  // XOR applied to the 16-byte chunk index of row r: rows r .. r + 3 of a
+  // transpose read then start 64 bytes apart modulo the 256-byte bank cycle.
+  static __device__ __forceinline__ int chunk_xor(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(kDsThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_ds_kernel(const T* __restrict__ k, const T* __restrict__ dsw, DsLayout lay,
+                      float* __restrict__ dq, int BH, int N, int nqt, float scale, int causal, int window) {
+  using TL = DsTile<D>;
+  constexpr int NW = kDsThreads / 64;  // 4
+  constexpr int BQ = 32 * NW;          // 128 query rows
+  constexpr int CB = D / 32;
+  constexpr int RB = TL::kRowBytes;
+  constexpr int KPER = TL::kKPer;
+  constexpr int S = kDsStages;
+  // One LDS object per K stage, so that the compiler can tell the stages'
+  // direct loads apart and wait only for the stage it reads.
+  __shared__ __attribute__((aligned(1024))) char T0[TL::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char T1[TL::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char T2[TL::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char T3[TL::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char T4[TL::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char T5[TL::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char T6[TL::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char T7[TL::kKBytes];
+  __shared__ __attribute__((aligned(1024))) char Sd[NW * 2048];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  __builtin_assume(w >= 0 && w < NW);
+
+  int bh, qr;
+  tile_order(blockIdx.x, BH, nqt, causal && window < 0, bh, qr);
+  const int qt = causal ? nqt - 1 - qr : qr;  // causal: the longest rows first
+  const int q0 = qt * BQ;
+  const int wq0 = q0 + 32 * w;  // this wave's rows: wq0 .. wq0 + 31
+  const int qb = wq0 >> 5;
+  const size_t base = (size_t)bh * (size_t)N * D;
+  const T* ds_slice = dsw + (size_t)bh * (size_t)lay.per_head * 1024;
+  char* Sw = Sd + w * 2048;
+
+  // Key blocks holding a key visible to any row of the workgroup.
+  const int kmin = window >= 0 ? max(0, q0 - window) : 0;
+  const int kmax = causal ? min(N - 1, q0 + BQ - 1) : N - 1;
+  const int kb0 = kmin >> 5, nsteps = (kmax >> 5) + 1 - kb0;
+  // Whether key block kb holds a pair visible to this wave's rows -- the
+  // test under which the dK / dV kernel stored the block.
+  auto visible = [&] __device__ (int kb) {
+    const int kk0 = kb * 32, kk1 = min(kk0 + 31, N - 1);
+    return kk0 < N && wq0 < N && !(causal && kk0 > wq0 + 31) && !(window >= 0 && kk1 < wq0 - window);
+  };
+
+  // Source offset of this lane's 16 bytes in each of its K blocks: LDS
+  // chunk c of row r holds K chunk c ^ chunk_xor(r).
+  uint32_t kpre[KPER];
+#pragma unroll
+  for (int j = 0; j < KPER; ++j) {
+    const int pos = (w + j * NW) * 1024 + lane * 16;
+    const int r = pos / RB, c = (pos % RB) / 16;
+    kpre[j] = (uint32_t)(r * RB + ((c ^ TL::chunk_xor(r)) * 16));
+  }
+  // Every wave issues the same loads per step -- KPER direct loads of K rows
+  // and two 16-byte loads of a dS block (steps past the end and blocks the
+  // wave skips load through an empty buffer: zeros, no memory traffic) -- so
+  // one wait count serves every step and wave, and the compiler's own count
+  // of the loads in flight stays exact enough not to add waits of its own.
+  constexpr int per_step = KPER + 2;
+  auto load_k = [&] __device__ (int i, char* kd) {
+    const int kb = kb0 + i;
+    const rsrc_t ks = make_rsrc(k + base + (size_t)kb * 32 * D, i < nsteps ? (uint32_t)max(0, N - kb * 32) * D * 2u : 0u);
+#pragma unroll
+    for (int j = 0; j < KPER; ++j) load_lds16(ks, kd + (w + j * NW) * 1024, kpre[j]);
+  };
+  auto load_ds = [&] __device__ (int i, uint4 (&r)[2]) {
+    const int kb = kb0 + i;
+    const bool mine = i < nsteps && visible(kb);
+    const rsrc_t ss = make_rsrc(ds_slice + (mine ? (size_t)ds_block(lay, qb, kb) * 1024 : 0), mine ? 2048u : 0u);
+    // Each block is read once: non-temporal, as the decode reads its cache.
+    r[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ss, (uint32_t)lane * 16u, 0, 2));
+    r[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ss, 1024u + (uint32_t)lane * 16u, 0, 2));
+  };
+
+  f32x16 acc[CB];
+#pragma unroll
+  for (int c = 0; c < CB; ++c) acc[c] = f32x16{};
+  // Transpose-read addresses: row 4 (g / 2) + gi / 4 (plus 16 s, plus 8 in
+  // the read's second half) and bytes 64 c + 32 (g & 1) + 8 (gi & 3) of
+  // the logical tile, as tr_addr gives for a padded one; in the swizzled
+  // tile the 64-byte block c of that row sits at block c ^ x, x the row's
+  // chunk XOR / 4 (the same for all rows a lane reads).
+  const int g = lane >> 4, gi = lane & 15;
+  const int trow = 4 * (g >> 1) + (gi >> 2);
+  const int tx = TL::chunk_xor(trow) / 4;
+  int trk[CB];
+#pragma unroll
+  for (int c = 0; c < CB; ++c) trk[c] = trow * RB + 64 * (c ^ tx) + 32 * (g & 1) + 8 * (gi & 3);
+  const int trs = tr_addr<64>(lane);
+  uint4 dsr[S][2];
+
+  auto stage_k = [&] __device__ (auto st) -> char* {
+    constexpr int X = decltype(st)::value;
+    return X == 0 ? T0 : X == 1 ? T1 : X == 2 ? T2 : X == 3 ? T3 : X == 4 ? T4 : X == 5 ? T5 : X == 6 ? T6 : T7;
+  };
+  using std::integral_constant;
+  // Issue order as if steps -8 .. -1 had run: dS of step 0, then (K of step
+  // j, dS of step j + 1) for j = 0 .. 6.
+  load_ds(0, dsr[0]);
+  auto prologue = [&] __device__ (auto jj) {
+    constexpr int J = decltype(jj)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    load_k(J, stage_k(integral_constant<int, J>{}));
+    __builtin_amdgcn_sched_barrier(0);
+    load_ds(J + 1, dsr[J + 1]);
+  };
+  prologue(integral_constant<int, 0>{});
+  prologue(integral_constant<int, 1>{});
+  prologue(integral_constant<int, 2>{});
+  prologue(integral_constant<int, 3>{});
+  prologue(integral_constant<int, 4>{});
+  prologue(integral_constant<int, 5>{});
+  prologue(integral_constant<int, 6>{});
+
+  // Step i: after the K rows of step i were issued came the dS of step
+  // i + 1 and the loads of steps i + 1 .. i + 6, so waiting down to that
+  // many leaves K of step i (and the older dS of step i) landed; the barrier
+  // makes every wave's K loads visible and retires every read of step
+  // i - 1's stage, into which the K rows of step i + 7 go next.  Then this
+  // wave's dS block moves from registers to its LDS block, the registers
+  // take the dS of step i + 8, and the products.
+  auto step = [&] __device__ (auto sl, int i) {
+    constexpr int X = decltype(sl)::value;  // K stage and register slot of step i
+    wait_vm_n<2 + (S - 2) * per_step>();
+    barrier_keep_loads();
+    load_k(i + S - 1, stage_k(integral_constant<int, (X + S - 1) % S>{}));
+    __builtin_amdgcn_sched_barrier(0);  // the wait count assumes K's loads go first
+    const bool vis = i < nsteps && visible(kb0 + i);
+    if (vis) {
+      *(uint4*)(Sw + lane * 16) = dsr[X][0];
+      *(uint4*)(Sw + 1024 + lane * 16) = dsr[X][1];
+    }
+    load_ds(i + S, dsr[X]);
+    if (vis) {
+      const char* Kt = stage_k(integral_constant<int, X>{});
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const vec8<T> b = read_tr8<64, T>(Sw + trs + 16 * s * 64);
+#pragma unroll
+        for (int c = 0; c < CB; ++c) acc[c] = mfma32(read_tr8<RB, T>(Kt + trk[c] + 16 * s * RB), b, acc[c]);
+      }
+    }
+  };
+  // Whole rounds of eight steps (those past the end do no work): with no
+  // exit inside the round each register slot stays in its registers from
+  // round to round, where exits between the steps made the compiler copy
+  // slots at the loop's back edge and wait for their loads there.
+  for (int i = 0; i < nsteps; i += S) {
+    step(integral_constant<int, 0>{}, i);
+    step(integral_constant<int, 1>{}, i + 1);
+    step(integral_constant<int, 2>{}, i + 2);
+    step(integral_constant<int, 3>{}, i + 3);
+    step(integral_constant<int, 4>{}, i + 4);
+    step(integral_constant<int, 5>{}, i + 5);
+    step(integral_constant<int, 6>{}, i + 6);
+    step(integral_constant<int, 7>{}, i + 7);
+  }
+  // dQ straight from the accumulators: the lane holds 16 columns of the row
+  // of its slot, four runs of four, each one 16-byte store (the two halves
+  // of the wave fill 32 contiguous bytes of a row; the rows' four runs of a
+  // 32-column block complete whole 128-byte lines in L2).  This is a small
+  // part of the kernel's traffic (dQ once against every visible dS block).
+  // The empty loads past the end must land before the wave ends.
+  const int slot = lane & 31, hh = lane >> 5;
+  const int row = wq0 + c_row(slot & 15, slot >> 4);
+  if (row < N) {
+    float* dst = dq + base + (size_t)row * D;
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *(float4*)(dst + 32 * c + 8 * g4 + 4 * hh) =
+            float4{scale * acc[c][4 * g4], scale * acc[c][4 * g4 + 1], scale * acc[c][4 * g4 + 2],
+                   scale * acc[c][4 * g4 + 3]};
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
 template <typename T, int D>
 hipError_t launch_t(const void* q, const void* k, const void* v, const void* o, const void* dO,
                     const float* lse, float* dq, float* dk, float* dv, int B, int H, int N,
@@ -821,6 +1151,26 @@ hipError_t launch_t(const void* q, const void* k, const void* v, const void* o, 
   const long long rows = (long long)B * H * N;
   float* Dv = (float*)ws;
   float* L2 = Dv + rows;
+  if (dq_rows == kDqStored) {
+    // D and L2, then dK / dV (storing dS), then dQ as the product dS K.
+    constexpr int RPB = kPreThreads / (D / 8);
+    hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(kPreThreads), 0,
+                       stream, (const T*)o, (const T*)dO, lse, Dv, L2, rows);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const DsLayout lay = ds_layout(N, mask.causal, mask.window);
+    T* dsw = (T*)((char*)ws + ds_offset(rows));
+    const int nkt = (N + kBKV - 1) / kBKV;
+    hipLaunchKernelGGL((bwd_kv4_kernel<T, D, true>), dim3((unsigned)((long long)nkt * B * H)), dim3(kKv4Threads),
+                       0, stream, (const T*)q, (const T*)k, (const T*)v, (const T*)dO, Dv, L2, dk, dv, dsw, lay,
+                       B * H, N, nkt, scale, scale * kLog2e, mask.causal, mask.window);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int nqt = (N + 127) / 128;
+    hipLaunchKernelGGL((bwd_dq_ds_kernel<T, D>), dim3((unsigned)((long long)nqt * B * H)), dim3(kDsThreads), 0,
+                       stream, (const T*)k, (const T*)dsw, lay, dq, B * H, N, nqt, scale, mask.causal, mask.window);
+    return hipGetLastError();
+  }
   // dQ first: it also stores D and L2 of every query row, which the dK / dV
   // kernel reads.  dQ: the ping-pong kernel (256 query rows per workgroup) or
   // the 4-wave kernel (128 rows).
@@ -841,8 +1191,8 @@ hipError_t launch_t(const void* q, const void* k, const void* v, const void* o, 
   if (err != hipSuccess) return err;
   const int nkt = (N + kBKV - 1) / kBKV;
   const long long grid = (long long)nkt * B * H;
-  hipLaunchKernelGGL((bwd_kv4_kernel<T, D>), dim3((unsigned)grid), dim3(kKv4Threads), 0, stream,
-                     (const T*)q, (const T*)k, (const T*)v, (const T*)dO, Dv, L2, dk, dv,
+  hipLaunchKernelGGL((bwd_kv4_kernel<T, D, false>), dim3((unsigned)grid), dim3(kKv4Threads), 0, stream,
+                     (const T*)q, (const T*)k, (const T*)v, (const T*)dO, Dv, L2, dk, dv, (T*)nullptr, DsLayout{},
                      B * H, N, nkt, scale, scale * kLog2e, mask.causal, mask.window);
   return hipGetLastError();
 }
@@ -860,11 +1210,18 @@ size_t bwd_workspace_bytes(int B, int H, int N, int d) {
   return (size_t)B * H * N * 2 * sizeof(float);
 }
 
+size_t bwd_workspace_bytes_ds(int B, int H, int N, int d, Mask mask) {
+  (void)d;
+  const long long rows = (long long)B * H * N;
+  const DsLayout lay = ds_layout(N, mask.causal, mask.window);
+  return ds_offset(rows) + (size_t)B * H * (size_t)lay.per_head * 2048u;
+}
+
 hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const void* o,
                            const void* dO, const float* lse, float* dq, float* dk, float* dv,
                            int B, int H, int N, int d, float scale, Mask mask, void* ws, bool f16,
                            int dq_rows, hipStream_t stream) {
-  if (dq_rows != 128 && dq_rows != 256) dq_rows = bwd_auto_dq_rows(B, H, N);
+  if (dq_rows != 128 && dq_rows != 256 && dq_rows != kDqStored) dq_rows = bwd_auto_dq_rows(B, H, N);
   if (f16) {
     if (d == 128)
       return launch_t<fa::f16, 128>(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, scale, mask, ws, dq_rows, stream);

@@ -62,10 +62,16 @@ hipError_t launch_decode_noalloc(const void* q, const void* kc, const void* vc, 
                                  void* o, float* lse, int S, int H, int Lmax, int d, float scale,
                                  int window, int chunk, Elem elem, hipStream_t stream);
 
-// 16-bit backward (bf16, or fp16 when f16): preprocess, dK/dV and dQ
-// kernels, d in {64, 128}.  dq_rows picks the dQ kernel: 256 (8-wave
-// ping-pong) or 128 (4 waves); bwd_auto_dq_rows is the built-in choice.
+// 16-bit backward (bf16, or fp16 when f16), d in {64, 128}.  dq_rows picks
+// how dQ is formed: by a kernel that recomputes S and dP, with 256 (8-wave
+// ping-pong) or 128 (4 waves) query rows per workgroup, before the dK / dV
+// kernel (bwd_auto_dq_rows is the built-in choice between them; workspace
+// bwd_workspace_bytes); or kDqStored: the dK / dV kernel also stores dS and
+// a product kernel forms dQ = scale dS K from it (workspace
+// bwd_workspace_bytes_ds, which grows with the visible blocks of N x N).
+constexpr int kDqStored = 1;
 size_t bwd_workspace_bytes(int B, int H, int N, int d);
+size_t bwd_workspace_bytes_ds(int B, int H, int N, int d, Mask mask);
 
 // Float32 backward, any 1 <= d <= 256: the dQ kernel (which also leaves D of
 // every query row in ws) then the dK / dV kernel, both over square tiles of

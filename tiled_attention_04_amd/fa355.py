@@ -43,12 +43,13 @@ SIGNATURES = {
     "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _Z,
                              _I, _P]),
     "fa_bwd_workspace_size": (_Z, [_I, _I, _I, _I]),
+    "fa_bwd_workspace_size_ds": (_Z, [_I, _I, _I, _I, _I, _I]),
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _I, _P]),
     "fa_decode_tune": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _Z, _I, _P, _I, _P, _P]),
     "fa_decode_auto_chunk": (_I, [_I, _I, _I, _I, _I, _I, _P]),
     "fa_bwd_tune": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _I, _P,
                          _I, _P, _P]),
-    "fa_bwd_auto_dq_rows": (_I, [_I, _I, _I, _I, _I, _I, _I, _P]),
+    "fa_bwd_auto_dq_rows": (_I, [_I, _I, _I, _I, _I, _I, _I, _Z, _P]),
     "fa_decode_check": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
 }
 
@@ -395,9 +396,38 @@ def fa_bwd_workspace_size(B: int, H: int, N: int, d: int) -> int:
     return int(lib().fa_bwd_workspace_size(B, H, N, d))
 
 
+def fa_bwd_workspace_size_ds(B: int, H: int, N: int, d: int, causal: bool = False, window: int = -1) -> int:
+    return int(lib().fa_bwd_workspace_size_ds(B, H, N, d, int(causal), int(window)))
+
+
+# The binding gives fa_bwd the stored-dS workspace by default while it stays
+# within this many bytes (the dS blocks grow as N^2), else the minimum.
+BWD_DS_WORKSPACE_CAP = 8 << 30
+FA_BWD_DQ_STORED = 1
+
+
+def fa_bwd_default_workspace_size(B: int, H: int, N: int, d: int, causal: bool = False, window: int = -1,
+                                  dtype=torch.bfloat16, stored_ds=None) -> int:
+    """Workspace bytes the binding allocates for an fa_bwd call: with the
+    stored dS (16-bit types, d in {64, 128}) when stored_ds is True, or when
+    it is None and that size is at most BWD_DS_WORKSPACE_CAP; else the
+    minimum (dQ by recomputation)."""
+    small = fa_bwd_workspace_size(B, H, N, d)
+    if stored_ds is False or dtype == torch.float32:
+        return small
+    big = fa_bwd_workspace_size_ds(B, H, N, d, causal, window)
+    if stored_ds and big == 0:
+        raise ValueError("the stored-dS backward takes 16-bit inputs with d in {64, 128}")
+    return big if big and (stored_ds or big <= BWD_DS_WORKSPACE_CAP) else small
+
+
 def fa_bwd(q, k, v, o, dO, lse, *, causal: bool = False, window: int = -1, scale=None,
-           dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """Backward pass from the forward's o and lse.  Returns float32 (dq, dk, dv)."""
+           dq=None, dk=None, dv=None, workspace=None, stream=None, stored_ds=None):
+    """Backward pass from the forward's o and lse.  Returns float32 (dq, dk, dv).
+
+    Without a workspace the binding allocates fa_bwd_default_workspace_size
+    bytes (stored_ds: None = dS stored while its workspace stays within
+    BWD_DS_WORKSPACE_CAP, True = stored, False = recomputed)."""
     B, H, N, d = q.shape
     dt = q.dtype
     if dt not in _DTYPE:
@@ -409,8 +439,8 @@ def fa_bwd(q, k, v, o, dO, lse, *, causal: bool = False, window: int = -1, scale
         outs.append(torch.empty(q.shape, dtype=torch.float32, device=q.device) if t is None else t)
     gp = [_dev(t, n, torch.float32, q.shape) for t, n in zip(outs, ("dq", "dk", "dv"))]
     if workspace is None:
-        workspace = torch.empty(max(fa_bwd_workspace_size(B, H, N, d), 1), dtype=torch.uint8,
-                                device=q.device)
+        need = fa_bwd_default_workspace_size(B, H, N, d, causal, window, dt, stored_ds)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     wp = _dev(workspace, "workspace")
     _check(lib().fa_bwd(*ptrs, lp, *gp, B, H, N, d, _default_scale(scale, d), int(causal),
                         int(window), wp, workspace.numel() * workspace.element_size(), _DTYPE[dt],
@@ -418,14 +448,16 @@ def fa_bwd(q, k, v, o, dO, lse, *, causal: bool = False, window: int = -1, scale
     return tuple(outs)
 
 
-BWD_TUNE_CANDIDATES = (128, 256)
+BWD_TUNE_CANDIDATES = (128, 256, FA_BWD_DQ_STORED)
 
 
 def fa_bwd_tune(q, k, v, o, dO, lse, *, causal: bool = False, window: int = -1, scale=None, reps: int = 10,
-                dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """Time the backward with each dQ kernel (128 or 256 query rows per
-    workgroup) and remember the faster for later fa_bwd calls (synchronises
-    the stream).  Returns (best rows, {rows: mean ms per call}, (dq, dk, dv))."""
+                dq=None, dk=None, dv=None, workspace=None, stream=None, stored_ds=None):
+    """Time the backward with each way of forming dQ (the recompute kernel with
+    128 or 256 query rows per workgroup, and FA_BWD_DQ_STORED when the
+    workspace holds the stored dS) and remember the fastest for later fa_bwd
+    calls (synchronises the stream).  Returns (best, {candidate: mean ms per
+    call, -1 if not tried}, (dq, dk, dv))."""
     B, H, N, d = q.shape
     dt = q.dtype
     if dt not in _DTYPE:
@@ -437,11 +469,11 @@ def fa_bwd_tune(q, k, v, o, dO, lse, *, causal: bool = False, window: int = -1, 
         outs.append(torch.empty(q.shape, dtype=torch.float32, device=q.device) if t is None else t)
     gp = [_dev(t, n, torch.float32, q.shape) for t, n in zip(outs, ("dq", "dk", "dv"))]
     if workspace is None:
-        workspace = torch.empty(max(fa_bwd_workspace_size(B, H, N, d), 1), dtype=torch.uint8,
-                                device=q.device)
+        need = fa_bwd_default_workspace_size(B, H, N, d, causal, window, dt, stored_ds)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     wp = _dev(workspace, "workspace")
     best = ctypes.c_int(0)
-    times = (ctypes.c_float * 2)()
+    times = (ctypes.c_float * len(BWD_TUNE_CANDIDATES))()
     _check(lib().fa_bwd_tune(*ptrs, lp, *gp, B, H, N, d, _default_scale(scale, d), int(causal),
                              int(window), wp, workspace.numel() * workspace.element_size(), _DTYPE[dt],
                              _stream(stream), int(reps), ctypes.byref(best), times))
@@ -449,8 +481,14 @@ def fa_bwd_tune(q, k, v, o, dO, lse, *, causal: bool = False, window: int = -1, 
 
 
 def fa_bwd_auto_dq_rows(B: int, H: int, N: int, d: int, *, causal: bool = False, window: int = -1,
-                        dtype=torch.bfloat16):
-    """(dQ kernel rows an fa_bwd call uses, whether it was tuned)."""
+                        dtype=torch.bfloat16, workspace_bytes=None):
+    """(How an fa_bwd call with workspace_bytes of workspace forms dQ -- 128 or
+    256 recompute rows, or FA_BWD_DQ_STORED --, whether that was tuned).
+    workspace_bytes defaults to what the binding's fa_bwd allocates."""
+    if workspace_bytes is None:
+        workspace_bytes = (fa_bwd_default_workspace_size(B, H, N, d, causal, window, dtype)
+                           if B > 0 and H > 0 and N > 0 and d > 0 else 0)
     tuned = ctypes.c_int(0)
-    r = lib().fa_bwd_auto_dq_rows(B, H, N, d, int(causal), int(window), _DTYPE[dtype], ctypes.byref(tuned))
+    r = lib().fa_bwd_auto_dq_rows(B, H, N, d, int(causal), int(window), _DTYPE[dtype], int(workspace_bytes),
+                                  ctypes.byref(tuned))
     return int(r), bool(tuned.value)

@@ -140,7 +140,10 @@ def main():
         del kc, vc, q
 
     print()
-    print("| backward workload | " + " | ".join(f"dQ {r} rows ms" for r in fa355.BWD_TUNE_CANDIDATES)
+    def dq_name(r):
+        return "stored dS" if r == fa355.FA_BWD_DQ_STORED else f"dQ {r} rows"
+
+    print("| backward workload | " + " | ".join(f"{dq_name(r)} ms" for r in fa355.BWD_TUNE_CANDIDATES)
           + " | fastest | TFLOP/s | heuristic |")
     print("|---|" + "---|" * (len(fa355.BWD_TUNE_CANDIDATES) + 3))
     for name, (B, H, N, d), dtype, causal, window in BWD_WORKLOADS:
@@ -151,8 +154,8 @@ def main():
         best, times, _ = fa355.fa_bwd_tune(q, k, v, o, g, lse, causal=causal, window=window, reps=args.reps)
         flops = 10.0 * d * B * H * visible_pairs(N, causal, window)
         tf = flops / (times[best] * 1e-3) / 1e12
-        cells = " | ".join(f"{times[r]:.4f}" for r in fa355.BWD_TUNE_CANDIDATES)
-        print(f"| {name} | {cells} | {best} | {tf:.1f} | {heur} |", flush=True)
+        cells = " | ".join(f"{times[r]:.4f}" if times[r] >= 0 else "-" for r in fa355.BWD_TUNE_CANDIDATES)
+        print(f"| {name} | {cells} | {dq_name(best)} | {tf:.1f} | {dq_name(heur)} |", flush=True)
         tuned += fa355.fa_tune_export()
         del q, k, v, g, o, lse
 
