@@ -943,6 +943,15 @@ void bwd_pre_kernel(const T* __restrict__ o, const T* __restrict__ dO, const flo
 constexpr int kDsThreads = 256;
 constexpr int kDsStages = 8;  // K stages, and dS blocks in flight per wave
 
+// s_waitcnt on the vector-memory counter only, for any count up to 63 (the
+// counter's width on gfx950: four low bits and two high bits of the
+// immediate).
+template <int N>
+__device__ __forceinline__ void wait_vm_n() {
+  static_assert(N >= 0 && N <= 63, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
 // The K rows of one 32-key step, unpadded (2 D bytes per row, 32 rows = 2 D
 // direct-load blocks of 1 KB), with the 16-byte chunks of each row permuted
 // by an XOR with a function of the row, so that the transpose reads of four

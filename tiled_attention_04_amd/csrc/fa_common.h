@@ -268,14 +268,6 @@ __device__ __forceinline__ void wait_vm(int n) {
   }
 }
 
-// The same for any count up to 63 (the counter's width on gfx950: four low
-// bits and two high bits of the immediate).
-template <int N>
-__device__ __forceinline__ void wait_vm_n() {
-  static_assert(N >= 0 && N <= 63, "vmcnt is six bits");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
-
 // Workgroup barrier that does not drain outstanding vector loads (unlike
 // __syncthreads, whose release fence waits for every memory operation).  The
 // "memory" clobber keeps LDS accesses on their side of it and the scheduling
