@@ -231,9 +231,8 @@ void bwd_kv4_kernel(const T* __restrict__ q, const T* __restrict__ k,
   char* pend = nullptr;
   auto store_pending = [&] __device__ () {
     if (pend) {
-      __builtin_nontemporal_store(u32x4{dpend[0], dpend[1], dpend[2], dpend[3]}, (u32x4*)(pend + l32 * 64 + h * 32));
-      __builtin_nontemporal_store(u32x4{dpend[4], dpend[5], dpend[6], dpend[7]},
-                                  (u32x4*)(pend + l32 * 64 + h * 32 + 16));
+      __builtin_nontemporal_store(u32x4{dpend[0], dpend[1], dpend[2], dpend[3]}, (u32x4*)(pend + lane * 16));
+      __builtin_nontemporal_store(u32x4{dpend[4], dpend[5], dpend[6], dpend[7]}, (u32x4*)(pend + 1024 + lane * 16));
     }
   };
   auto tile = [&] __device__ (auto stage, int qt) {
@@ -306,10 +305,12 @@ void bwd_kv4_kernel(const T* __restrict__ q, const T* __restrict__ k,
       form_ds();
       if constexpr (DS) {
         // The block is stored at the start of the next step.  The 32 x 32 dS
-        // block of (query block qt, this wave's key block) is row-major by
-        // key: the lane's 16 values are slots 16 h .. 16 h + 15 of its key's
-        // row (slot 16 h + r holds query c_row(r, h)).  Written once and read
-        // once by the next kernel: non-temporal stores.
+        // block of (query block qt, this wave's key block) holds in lane
+        // order the lane's 16 values -- slots 16 h .. 16 h + 15 of its key's
+        // row, slot 16 h + r for query c_row(r, h) --, the first eight at
+        // 16 lane, the last eight at 1024 + 16 lane, so that each store
+        // instruction writes 1 KB contiguous.  Written once and read once by
+        // the next kernel: non-temporal stores.
         pend = (char*)(dsw + ((size_t)bh * (size_t)lay.per_head + (size_t)ds_block(lay, qt, wk0 >> 5)) * 1024);
 #pragma unroll
         for (int j = 0; j < 8; ++j) dpend[j] = dspk[j];
@@ -926,22 +927,22 @@ void bwd_pre_kernel(const T* __restrict__ o, const T* __restrict__ dO, const flo
 // dQ = scale * dS K from the dS blocks the dK / dV kernel stored: the
 // product of "Building Flash Attention from Scratch in Pure NumPy", Step 4,
 // with nothing recomputed.  Four waves own 128 query rows (32 each) and walk
-// the key blocks their rows see 32 keys at a time.  The kernel streams the
-// dS blocks once from HBM, so what sets its pace is how many bytes are in
-// flight: each wave keeps its next eight 2 KB dS blocks in flight in
-// registers (64 per lane), and the workgroup's K rows (read by every query
-// tile of the slice, mostly from L2) come through a ring of eight LDS stages
-// by direct loads.  (Loads retire in issue order, so the dS loads run no
-// further ahead than the K stages: a wait for step i's K rows also waits for
-// every dS load issued before them.)  Per step a wave copies its dS block into its own 2 KB of
-// LDS and forms
+// the key blocks their rows see, two 32-key blocks per step.  The kernel
+// streams the dS blocks once from HBM: each wave keeps the dS blocks of its
+// next four steps in flight in registers (non-temporal loads), and the
+// workgroup's K rows (read by every query tile of the slice, mostly from L2)
+// come through a ring of four LDS stages by direct loads.  (Loads retire in
+// issue order, so the dS loads run no further ahead than the K stages: a
+// wait for step i's K rows also waits for every dS load issued before
+// them.)  Per block a wave copies its dS block into its own 2 KB of LDS,
+// row-major by key (16-byte chunks swizzled), and forms
 //   dQ^T += K^T dS^T
-// with K^T and dS^T both from transpose reads (the dS block is row-major by
-// key, so its transpose reads give the queries as the accumulator's
-// columns).  A wave skips the blocks that hold no pair visible to its rows
-// (the dK / dV kernel never wrote them).
+// with K^T and dS^T both from transpose reads (those of the dS tile give the
+// queries as the accumulator's columns).  A wave skips the blocks that hold
+// no pair visible to its rows (the dK / dV kernel never wrote them).
 constexpr int kDsThreads = 256;
-constexpr int kDsStages = 8;  // K stages, and dS blocks in flight per wave
+constexpr int kDsKB = 2;      // 32-key blocks per step
+constexpr int kDsStages = 4;  // K stages, and steps of dS in flight per wave
 
 // s_waitcnt on the vector-memory counter only, for any count up to 63 (the
 // counter's width on gfx950: four low bits and two high bits of the
@@ -952,16 +953,16 @@ __device__ __forceinline__ void wait_vm_n() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
-// The K rows of one 32-key step, unpadded (2 D bytes per row, 32 rows = 2 D
-// direct-load blocks of 1 KB), with the 16-byte chunks of each row permuted
-// by an XOR with a function of the row, so that the transpose reads of four
-// consecutive rows hit distinct LDS banks (unpadded rows 256 or 128 bytes
-// apart would all start on the same bank).  8 KB per stage at d = 128, so
-// that eight stages fit two workgroups per CU.
+// The K rows of one step (kDsKB blocks of 32 keys), unpadded (2 D bytes per
+// row), with the 16-byte chunks of each row permuted by an XOR with a
+// function of the row, so that the transpose reads of four consecutive rows
+// hit distinct LDS banks (unpadded rows 256 or 128 bytes apart would all
+// start on the same bank).  16 KB per stage at d = 128, so that four stages
+// fit two workgroups per CU.
 template <int D>
 struct DsTile {
   static constexpr int kRowBytes = 2 * D;
-  static constexpr int kKBytes = 32 * kRowBytes;
+  static constexpr int kKBytes = 32 * kDsKB * kRowBytes;
   static constexpr int kKBlocks = kKBytes / 1024;
   static constexpr int kKPer = kKBlocks / 4;  // direct loads per wave and step
   static_assert(kKBlocks % 4 == 0, "K blocks per wave");
@@ -980,6 +981,7 @@ void bwd_dq_ds_kernel(const T* __restrict__ k, const T* __restrict__ dsw, DsLayo
   constexpr int CB = D / 32;
   constexpr int RB = TL::kRowBytes;
   constexpr int KPER = TL::kKPer;
+  constexpr int KB = kDsKB;
   constexpr int S = kDsStages;
   // One LDS object per K stage, so that the compiler can tell the stages'
   // direct loads apart and wait only for the stage it reads.
@@ -987,10 +989,6 @@ void bwd_dq_ds_kernel(const T* __restrict__ k, const T* __restrict__ dsw, DsLayo
   __shared__ __attribute__((aligned(1024))) char T1[TL::kKBytes];
   __shared__ __attribute__((aligned(1024))) char T2[TL::kKBytes];
   __shared__ __attribute__((aligned(1024))) char T3[TL::kKBytes];
-  __shared__ __attribute__((aligned(1024))) char T4[TL::kKBytes];
-  __shared__ __attribute__((aligned(1024))) char T5[TL::kKBytes];
-  __shared__ __attribute__((aligned(1024))) char T6[TL::kKBytes];
-  __shared__ __attribute__((aligned(1024))) char T7[TL::kKBytes];
   __shared__ __attribute__((aligned(1024))) char Sd[NW * 2048];
 
   const int t = threadIdx.x;
@@ -1008,10 +1006,10 @@ void bwd_dq_ds_kernel(const T* __restrict__ k, const T* __restrict__ dsw, DsLayo
   const T* ds_slice = dsw + (size_t)bh * (size_t)lay.per_head * 1024;
   char* Sw = Sd + w * 2048;
 
-  // Key blocks holding a key visible to any row of the workgroup.
+  // Key blocks holding a key visible to any row of the workgroup, KB per step.
   const int kmin = window >= 0 ? max(0, q0 - window) : 0;
   const int kmax = causal ? min(N - 1, q0 + BQ - 1) : N - 1;
-  const int kb0 = kmin >> 5, nsteps = (kmax >> 5) + 1 - kb0;
+  const int kb0 = kmin >> 5, nsteps = ((kmax >> 5) + 1 - kb0 + KB - 1) / KB;
   // Whether key block kb holds a pair visible to this wave's rows -- the
   // test under which the dK / dV kernel stored the block.
   auto visible = [&] __device__ (int kb) {
@@ -1029,50 +1027,79 @@ void bwd_dq_ds_kernel(const T* __restrict__ k, const T* __restrict__ dsw, DsLayo
     kpre[j] = (uint32_t)(r * RB + ((c ^ TL::chunk_xor(r)) * 16));
   }
   // Every wave issues the same loads per step -- KPER direct loads of K rows
-  // and two 16-byte loads of a dS block (steps past the end and blocks the
+  // and two 16-byte loads per dS block (steps past the end and blocks the
   // wave skips load through an empty buffer: zeros, no memory traffic) -- so
   // one wait count serves every step and wave, and the compiler's own count
   // of the loads in flight stays exact enough not to add waits of its own.
-  constexpr int per_step = KPER + 2;
+  constexpr int per_step = KPER + 2 * KB;
   auto load_k = [&] __device__ (int i, char* kd) {
-    const int kb = kb0 + i;
+    const int kb = kb0 + KB * i;
     const rsrc_t ks = make_rsrc(k + base + (size_t)kb * 32 * D, i < nsteps ? (uint32_t)max(0, N - kb * 32) * D * 2u : 0u);
 #pragma unroll
     for (int j = 0; j < KPER; ++j) load_lds16(ks, kd + (w + j * NW) * 1024, kpre[j]);
   };
-  auto load_ds = [&] __device__ (int i, uint4 (&r)[2]) {
-    const int kb = kb0 + i;
-    const bool mine = i < nsteps && visible(kb);
-    const rsrc_t ss = make_rsrc(ds_slice + (mine ? (size_t)ds_block(lay, qb, kb) * 1024 : 0), mine ? 2048u : 0u);
-    // Each block is read once: non-temporal, as the decode reads its cache.
-    r[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ss, (uint32_t)lane * 16u, 0, 2));
-    r[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ss, 1024u + (uint32_t)lane * 16u, 0, 2));
+  auto load_ds = [&] __device__ (int i, uint4 (&r)[KB][2]) {
+#pragma unroll
+    for (int b = 0; b < KB; ++b) {
+      const int kb = kb0 + KB * i + b;
+      const bool mine = i < nsteps && visible(kb);
+      const rsrc_t ss = make_rsrc(ds_slice + (mine ? (size_t)ds_block(lay, qb, kb) * 1024 : 0), mine ? 2048u : 0u);
+      // Each block is read once: non-temporal, as the decode reads its cache.
+      r[b][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ss, (uint32_t)lane * 16u, 0, 2));
+      r[b][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ss, 1024u + (uint32_t)lane * 16u, 0, 2));
+    }
   };
 
   f32x16 acc[CB];
 #pragma unroll
   for (int c = 0; c < CB; ++c) acc[c] = f32x16{};
   // Transpose-read addresses: row 4 (g / 2) + gi / 4 (plus 16 s, plus 8 in
-  // the read's second half) and bytes 64 c + 32 (g & 1) + 8 (gi & 3) of
-  // the logical tile, as tr_addr gives for a padded one; in the swizzled
-  // tile the 64-byte block c of that row sits at block c ^ x, x the row's
-  // chunk XOR / 4 (the same for all rows a lane reads).
+  // the read's second half, plus 32 per block) and bytes 64 c + 32 (g & 1) +
+  // 8 (gi & 3) of the logical tile, as tr_addr gives for a padded one; in
+  // the swizzled tile the 64-byte block c of that row sits at block c ^ x,
+  // x the row's chunk XOR / 4 (the same for all rows a lane reads).
   const int g = lane >> 4, gi = lane & 15;
   const int trow = 4 * (g >> 1) + (gi >> 2);
   const int tx = TL::chunk_xor(trow) / 4;
   int trk[CB];
 #pragma unroll
   for (int c = 0; c < CB; ++c) trk[c] = trow * RB + 64 * (c ^ tx) + 32 * (g & 1) + 8 * (gi & 3);
-  const int trs = tr_addr<64>(lane);
-  uint4 dsr[S][2];
+  // The dS tile in LDS: 32 rows (keys) of 64 bytes (32 slots), row-major,
+  // with the 16-byte chunk c of row r at chunk c ^ ((r / 4) & 3).  The
+  // stored block is in the dK / dV kernel's lane order: this lane's two
+  // 16-byte pieces are chunks 2 h and 2 h + 1 of the row of key lane % 32
+  // (h = lane / 32), and with the swizzle the sixteen lanes of each write
+  // pass hit distinct banks (unswizzled, keys 64 bytes apart collide four
+  // ways).  The transpose reads (row 16 s + 8 half + 4 (g / 2) + gi / 4,
+  // bytes 32 (g & 1) + 8 (gi & 3), as tr_addr gives) follow the same swizzle,
+  // which moves whole 16-byte chunks, so each lane's 8 bytes stay whole.
+  const int dkey = lane & 31, dh = lane >> 5, dsw_x = (dkey >> 2) & 3;
+  const int ds_lds0 = dkey * 64 + 16 * ((2 * dh) ^ dsw_x);
+  const int ds_lds1 = dkey * 64 + 16 * ((2 * dh + 1) ^ dsw_x);
+  int trs[2][2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int r = 16 * s + 8 * half + 4 * (g >> 1) + (gi >> 2);
+      const int c = 2 * (g & 1) + ((gi & 3) >> 1);
+      trs[s][half] = r * 64 + 16 * (c ^ ((r >> 2) & 3)) + 8 * (gi & 1);
+    }
+  auto read_ds = [&] __device__ (int s) -> vec8<T> {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Sw + trs[s][0]));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Sw + trs[s][1]));
+    const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+    return as_vec8<T>(uint4{l2.x, l2.y, h2.x, h2.y});
+  };
+  uint4 dsr[S][KB][2];
 
   auto stage_k = [&] __device__ (auto st) -> char* {
     constexpr int X = decltype(st)::value;
-    return X == 0 ? T0 : X == 1 ? T1 : X == 2 ? T2 : X == 3 ? T3 : X == 4 ? T4 : X == 5 ? T5 : X == 6 ? T6 : T7;
+    return X == 0 ? T0 : X == 1 ? T1 : X == 2 ? T2 : T3;
   };
   using std::integral_constant;
-  // Issue order as if steps -8 .. -1 had run: dS of step 0, then (K of step
-  // j, dS of step j + 1) for j = 0 .. 6.
+  // Issue order as if steps -4 .. -1 had run: dS of step 0, then (K of step
+  // j, dS of step j + 1) for j = 0 .. 2.
   load_ds(0, dsr[0]);
   auto prologue = [&] __device__ (auto jj) {
     constexpr int J = decltype(jj)::value;
@@ -1084,41 +1111,43 @@ void bwd_dq_ds_kernel(const T* __restrict__ k, const T* __restrict__ dsw, DsLayo
   prologue(integral_constant<int, 0>{});
   prologue(integral_constant<int, 1>{});
   prologue(integral_constant<int, 2>{});
-  prologue(integral_constant<int, 3>{});
-  prologue(integral_constant<int, 4>{});
-  prologue(integral_constant<int, 5>{});
-  prologue(integral_constant<int, 6>{});
 
   // Step i: after the K rows of step i were issued came the dS of step
-  // i + 1 and the loads of steps i + 1 .. i + 6, so waiting down to that
+  // i + 1 and the loads of steps i + 1 and i + 2, so waiting down to that
   // many leaves K of step i (and the older dS of step i) landed; the barrier
   // makes every wave's K loads visible and retires every read of step
-  // i - 1's stage, into which the K rows of step i + 7 go next.  Then this
-  // wave's dS block moves from registers to its LDS block, the registers
-  // take the dS of step i + 8, and the products.
+  // i - 1's stage, into which the K rows of step i + 3 go next.  Then, per
+  // block of the step, this wave's dS block moves from registers to its LDS
+  // block (LDS runs a wave's accesses in order, so the second block's write
+  // follows the first block's reads) and the products; the registers take
+  // the dS of step i + 4.
   auto step = [&] __device__ (auto sl, int i) {
     constexpr int X = decltype(sl)::value;  // K stage and register slot of step i
-    wait_vm_n<2 + (S - 2) * per_step>();
+    wait_vm_n<2 * KB + (S - 2) * per_step>();
     barrier_keep_loads();
     load_k(i + S - 1, stage_k(integral_constant<int, (X + S - 1) % S>{}));
     __builtin_amdgcn_sched_barrier(0);  // the wait count assumes K's loads go first
-    const bool vis = i < nsteps && visible(kb0 + i);
-    if (vis) {
-      *(uint4*)(Sw + lane * 16) = dsr[X][0];
-      *(uint4*)(Sw + 1024 + lane * 16) = dsr[X][1];
-    }
-    load_ds(i + S, dsr[X]);
-    if (vis) {
-      const char* Kt = stage_k(integral_constant<int, X>{});
+    bool vis[KB];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const vec8<T> b = read_tr8<64, T>(Sw + trs + 16 * s * 64);
+    for (int b = 0; b < KB; ++b) vis[b] = i < nsteps && visible(kb0 + KB * i + b);
+    const char* Kt = stage_k(integral_constant<int, X>{});
 #pragma unroll
-        for (int c = 0; c < CB; ++c) acc[c] = mfma32(read_tr8<RB, T>(Kt + trk[c] + 16 * s * RB), b, acc[c]);
+    for (int b = 0; b < KB; ++b) {
+      if (vis[b]) {
+        *(uint4*)(Sw + ds_lds0) = dsr[X][b][0];
+        *(uint4*)(Sw + ds_lds1) = dsr[X][b][1];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const vec8<T> bo = read_ds(s);
+#pragma unroll
+          for (int c = 0; c < CB; ++c)
+            acc[c] = mfma32(read_tr8<RB, T>(Kt + trk[c] + (32 * b + 16 * s) * RB), bo, acc[c]);
+        }
       }
     }
+    load_ds(i + S, dsr[X]);
   };
-  // Whole rounds of eight steps (those past the end do no work): with no
+  // Whole rounds of four steps (those past the end do no work): with no
   // exit inside the round each register slot stays in its registers from
   // round to round, where exits between the steps made the compiler copy
   // slots at the loop's back edge and wait for their loads there.
@@ -1127,10 +1156,6 @@ void bwd_dq_ds_kernel(const T* __restrict__ k, const T* __restrict__ dsw, DsLayo
     step(integral_constant<int, 1>{}, i + 1);
     step(integral_constant<int, 2>{}, i + 2);
     step(integral_constant<int, 3>{}, i + 3);
-    step(integral_constant<int, 4>{}, i + 4);
-    step(integral_constant<int, 5>{}, i + 5);
-    step(integral_constant<int, 6>{}, i + 6);
-    step(integral_constant<int, 7>{}, i + 7);
   }
   // dQ straight from the accumulators: the lane holds 16 columns of the row
   // of its slot, four runs of four, each one 16-byte store (the two halves
