@@ -387,6 +387,8 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d);
  * causal attention (0.54 GB at B = 2, H = 16, N = 4096), so it is the
  * caller's choice: fa_bwd takes this path whenever workspace_bytes is at
  * least this size, unless fa_bwd_tune measured a recompute kernel faster.
+ * (It pays once the product kernel's grid of B * H * ceil(N / 128)
+ * workgroups fills the chip; on small grids the recompute kernels lead.)
  */
 size_t fa_bwd_workspace_size_ds(int B, int H, int N, int d, int causal, int window);
 

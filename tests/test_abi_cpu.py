@@ -264,7 +264,10 @@ def test_decode_and_bwd_tune_reject_bad_arguments(lib):
     assert fa355.fa_bwd_auto_dq_rows(2, 16, 4096, 128, causal=True, workspace_bytes=big - 1) == (256, False)
     assert fa355.fa_bwd_auto_dq_rows(2, 16, 4096, 128, causal=True, workspace_bytes=big) == (1, False)
     assert fa355.fa_bwd_auto_dq_rows(1, 8, 1024, 64, workspace_bytes=0) == (128, False)
-    assert fa355.fa_bwd_auto_dq_rows(1, 8, 1024, 64) == (1, False)
+    # the binding's default workspace stores dS only once the product grid fills the chip
+    assert fa355.fa_bwd_auto_dq_rows(1, 8, 1024, 64) == (128, False)
+    big64 = fa355.fa_bwd_workspace_size_ds(1, 8, 1024, 64, False, -1)
+    assert fa355.fa_bwd_auto_dq_rows(1, 8, 1024, 64, workspace_bytes=big64) == (1, False)
     assert fa355.fa_bwd_auto_dq_rows(1, 8, 1024, 64, dtype=torch.float32)[0] == 0
     # a tuned stored-dS choice needs the workspace for it
     fa355.fa_tune_import([dict(kind=fa355.TUNE_KINDS["bwd_dq_rows"], dtype=1, d=128, causal=1, window=-1,
@@ -357,3 +360,8 @@ def test_workspace_sizes(lib):
     assert fa355.fa_bwd_default_workspace_size(2, 16, 4096, 128, True, stored_ds=False) == rows * 8
     assert fa355.fa_bwd_default_workspace_size(2, 16, 4096, 128, True, dtype=torch.float32) == rows * 8
     assert fa355.fa_bwd_default_workspace_size(1, 32, 65536, 128, True) == 32 * 65536 * 8
+    # below two product workgroups per CU (B * H * ceil(N / 128) < 512) the minimum, unless asked
+    assert fa355.fa_bwd_default_workspace_size(1, 8, 1024, 64, True) == 8 * 1024 * 8
+    assert fa355.fa_bwd_default_workspace_size(1, 8, 1024, 64, True, stored_ds=True) == \
+        fa355.fa_bwd_workspace_size_ds(1, 8, 1024, 64, True, -1)
+    assert fa355.fa_bwd_default_workspace_size(1, 16, 4096, 128, True) == 16 * 4096 * 8 + 16 * tri * 2048

@@ -41,7 +41,7 @@ def test_captured_step_replays_match_eager_calls():
 
     o, lse = torch.empty_like(q), torch.empty((B, H, N), dtype=torch.float32, device=dev)
     dq, dk, dv = (torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3))
-    # the stored-dS backward, as the eager call below (the binding's default at this size)
+    # the stored-dS backward, as the eager call below
     ws = torch.empty(fa.fa_bwd_workspace_size_ds(B, H, N, d, True, -1), dtype=torch.uint8, device=dev)
     o32, lse32 = torch.empty_like(q32), torch.empty((1, 2, 300), dtype=torch.float32, device=dev)
     dq32, dk32, dv32 = (torch.empty_like(q32) for _ in range(3))
@@ -91,7 +91,7 @@ def test_captured_step_replays_match_eager_calls():
         got = [t.clone() for t in (o, lse, dq, dk, dv, o32, lse32, dq32, dk32, dv32, od, ld, op, lp, on, ln)]
 
         eo, el = fa.fa_fwd(q, k, v, causal=True)
-        edq, edk, edv = fa.fa_bwd(q, k, v, eo, g, el, causal=True)
+        edq, edk, edv = fa.fa_bwd(q, k, v, eo, g, el, causal=True, stored_ds=True)
         eo32, el32 = fa.fa_fwd(q32, k32, v32, causal=True, window=50)
         edq32, edk32, edv32 = fa.fa_bwd(q32, k32, v32, eo32, g32, el32, causal=True, window=50)
         eod, eld = fa.fa_decode(qd, kc, vc, sl)

@@ -114,11 +114,16 @@ def test_bwd_tune_remembers_the_faster_dq_kernel(dtype, d, causal, window):
     q, k, v, dO = attention_inputs(B, H, N, d, dtype, seed=21, with_grad=True)
     qd, kd, vd, gd = (t.cuda() for t in (q, k, v, dO))
     o, lse = fa.fa_fwd(qd, kd, vd, causal=causal, window=window)
-    best, times, (dq, dk, dv) = fa.fa_bwd_tune(qd, kd, vd, o, gd, lse, causal=causal, window=window, reps=3)
+    # every candidate is tried: the workspace holds the stored dS (at this size the binding's
+    # default would not provide it)
+    ws_bytes = fa.fa_bwd_workspace_size_ds(B, H, N, d, causal, window)
+    best, times, (dq, dk, dv) = fa.fa_bwd_tune(qd, kd, vd, o, gd, lse, causal=causal, window=window, reps=3,
+                                               stored_ds=True)
     assert set(times) == set(fa.BWD_TUNE_CANDIDATES) and min(times.values()) > 0
     assert best in fa.BWD_TUNE_CANDIDATES and times[best] == min(times.values())
-    assert fa.fa_bwd_auto_dq_rows(B, H, N, d, causal=causal, window=window, dtype=qd.dtype) == (best, True)
-    dq2, dk2, dv2 = fa.fa_bwd(qd, kd, vd, o, gd, lse, causal=causal, window=window)
+    assert fa.fa_bwd_auto_dq_rows(B, H, N, d, causal=causal, window=window, dtype=qd.dtype,
+                                  workspace_bytes=ws_bytes) == (best, True)
+    dq2, dk2, dv2 = fa.fa_bwd(qd, kd, vd, o, gd, lse, causal=causal, window=window, stored_ds=True)
     torch.cuda.synchronize()
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
     rq, rk, rv = oracle.attention_bwd_ref(q[:, 2:3], k[:, 2:3], v[:, 2:3], dO[:, 2:3], 1 / math.sqrt(d), causal,
@@ -132,8 +137,9 @@ def test_bwd_tune_remembers_the_faster_dq_kernel(dtype, d, causal, window):
         fa.fa_tune_import([dict(kind=fa.TUNE_KINDS["bwd_dq_rows"],
                                 dtype=fa.FA_FP16 if dtype == "fp16" else fa.FA_BF16, d=d, causal=int(causal),
                                 window=window, rows=B * H, n=N, value=other)])
-        assert fa.fa_bwd_auto_dq_rows(B, H, N, d, causal=causal, window=window, dtype=qd.dtype) == (other, True)
-        dq3, dk3, dv3 = fa.fa_bwd(qd, kd, vd, o, gd, lse, causal=causal, window=window)
+        assert fa.fa_bwd_auto_dq_rows(B, H, N, d, causal=causal, window=window, dtype=qd.dtype,
+                                      workspace_bytes=ws_bytes) == (other, True)
+        dq3, dk3, dv3 = fa.fa_bwd(qd, kd, vd, o, gd, lse, causal=causal, window=window, stored_ds=True)
         torch.cuda.synchronize()
         assert torch.equal(dv, dv3)
         if (other == fa.FA_BWD_DQ_STORED) == (best == fa.FA_BWD_DQ_STORED):

@@ -400,9 +400,14 @@ def fa_bwd_workspace_size_ds(B: int, H: int, N: int, d: int, causal: bool = Fals
     return int(lib().fa_bwd_workspace_size_ds(B, H, N, d, int(causal), int(window)))
 
 
-# The binding gives fa_bwd the stored-dS workspace by default while it stays
-# within this many bytes (the dS blocks grow as N^2), else the minimum.
+# The binding gives fa_bwd the stored-dS workspace by default when the
+# product kernel's grid (128 query rows per workgroup) fills the chip at two
+# workgroups per CU and the workspace stays within this many bytes (the dS
+# blocks grow as N^2); else the minimum.  (Measured: the stored-dS path
+# leads at 2x16x4096x128, causal or windowed, and trails the recompute
+# kernels at 1x8x1024x64, whose 64 workgroups leave most CUs idle.)
 BWD_DS_WORKSPACE_CAP = 8 << 30
+BWD_DS_MIN_WORKGROUPS = 512
 FA_BWD_DQ_STORED = 1
 
 
@@ -410,15 +415,17 @@ def fa_bwd_default_workspace_size(B: int, H: int, N: int, d: int, causal: bool =
                                   dtype=torch.bfloat16, stored_ds=None) -> int:
     """Workspace bytes the binding allocates for an fa_bwd call: with the
     stored dS (16-bit types, d in {64, 128}) when stored_ds is True, or when
-    it is None and that size is at most BWD_DS_WORKSPACE_CAP; else the
-    minimum (dQ by recomputation)."""
+    it is None, the grid of B * H * ceil(N / 128) workgroups reaches
+    BWD_DS_MIN_WORKGROUPS and that size is at most BWD_DS_WORKSPACE_CAP;
+    else the minimum (dQ by recomputation)."""
     small = fa_bwd_workspace_size(B, H, N, d)
     if stored_ds is False or dtype == torch.float32:
         return small
     big = fa_bwd_workspace_size_ds(B, H, N, d, causal, window)
     if stored_ds and big == 0:
         raise ValueError("the stored-dS backward takes 16-bit inputs with d in {64, 128}")
-    return big if big and (stored_ds or big <= BWD_DS_WORKSPACE_CAP) else small
+    fills = B * H * ((N + 127) // 128) >= BWD_DS_MIN_WORKGROUPS
+    return big if big and (stored_ds or (fills and big <= BWD_DS_WORKSPACE_CAP)) else small
 
 
 def fa_bwd(q, k, v, o, dO, lse, *, causal: bool = False, window: int = -1, scale=None,
