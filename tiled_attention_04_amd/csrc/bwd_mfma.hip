@@ -9,8 +9,12 @@
 //   P = exp(S - L),  dV += P^T dO,  dP = dO V^T,  dS = P * (dP - D),
 //   dK += scale * dS^T Q,  dQ += scale * dS K.
 //
-// Mapping onto CDNA4 (v_mfma_f32_32x32x16_bf16 / _f16, fp32 accumulation), two
-// kernels on one stream:
+// Mapping onto CDNA4 (v_mfma_f32_32x32x16_bf16 / _f16, fp32 accumulation).
+// With a workspace that holds dS (the stored-dS path), three kernels on one
+// stream: bwd_pre (D and L in log2 units), bwd_kv4 below, which also writes
+// each dS block it forms, and bwd_dq_ds, dQ = scale dS K from those blocks
+// -- the page's five products, nothing recomputed.  Otherwise (the recompute
+// path) two kernels on one stream:
 //  * bwd_dq4 (4 waves, two workgroups per CU) or bwd_dq_pp (8 waves in two
 //    groups one phase apart, for grids that fill the chip): dQ, with the
 //    loops the other way round (a workgroup owns 128 or 256 query rows and
